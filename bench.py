@@ -1,0 +1,308 @@
+"""Benchmark of the SSD forward pass on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--config IDX] [--no-cpu-baseline]
+
+One step = one whole forward pass (all steps of the chunked path: cumsum,
+chunk states, state passing, chunk scan with the chunk output) over one batch
+of seeded synthetic inputs already resident in HBM. Prints ONE JSON line.
+
+Besides the headline tokens/s, it times every kernel on its own with HIP
+events recorded on the stream the kernels run on, and reports the dominant
+kernel against its roofline (algorithmic bytes or flops per launch divided
+by its average duration), next to the fp64 CPU oracle timed on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd tokens/s + % of bf16 MFMA / HBM roofline, B=8 L=2048 H=64 P=64 N=128"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix, published
+FP32_VECTOR_PEAK_TFS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1, help="workload index (1 = the headline workload)")
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--kernel-reps", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=2)
+    return ap.parse_args()
+
+
+def algorithmic_model(cfg, Q, io_bytes):
+    """Algorithmic bytes and flops per launch of each kernel (whole batch).
+
+    Bytes count each operand and result once per launch, at its storage
+    dtype: states in the io dtype, dA_cumsum/dt_chunked fp32. Flops count
+    2 per multiply-add of the useful (causal) work, C.B^T once per group.
+    """
+    b, L, H, P, N, G = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
+    T = b * L
+    nc = -(-L // Q)
+    s = io_bytes
+    st = b * H * nc * P * N * s          # all chunk states, one pass
+    cs = b * H * nc * Q * 4              # dA_cumsum or dt_chunked
+    out = {
+        "chunk_cumsum": dict(bytes=T * H * 4 + 2 * cs, flops=2 * T * H),
+        "chunk_state": dict(bytes=T * H * P * s + T * G * N * s + 2 * cs + st,
+                            flops=2 * T * H * P * N + 2 * T * H * P),
+        "state_passing": dict(bytes=2 * st + 4 * b * H * P * N * (2 if cfg.init_state else 1) + b * H * nc * 4,
+                              flops=2 * b * H * nc * P * N),
+        "chunk_scan": dict(bytes=2 * T * H * P * s + 2 * T * G * N * s + 2 * cs + st,
+                           flops=T * H * (Q + 1) * P + T * G * (Q + 1) * N + 2 * T * H * P * N + 3 * T * H * P),
+    }
+    return out
+
+
+def kernel_source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "mamba_ssd_scan_fwd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel, cfg_name, per_launch_algo):
+    """HBM traffic of `kernel` from the committed rocprofv3 counter summary,
+    or None when absent or taken on another version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+        ent = rec["kernels"][kernel]
+        if ent["workload"] != cfg_name:
+            return None
+        if ent["source_digest"] != kernel_source_digest(ent["source_files"]):
+            return None
+        return float(ent["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(cfg, inp, nseq):
+    """The fp64 oracle as it stands, on `nseq` whole sequences (all heads)."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    from oracle import ssd_recurrent
+
+    def f64(t):
+        return None if t is None else t.detach().cpu().float().numpy().astype(np.float64)
+
+    sl = slice(0, nseq)
+    args = [f64(inp["x"][sl]), f64(inp["dt"][sl]), f64(inp["A"]), f64(inp["B"][sl]), f64(inp["C"][sl]),
+            f64(inp["D"]), f64(inp["init_state"][sl]) if inp["init_state"] is not None else None]
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        ssd_recurrent(*args)
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    tokens = nseq * cfg.seqlen
+    return {
+        "value": tokens / dt,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{nseq} of {cfg.batch} sequences x {cfg.seqlen} tokens, all {cfg.nheads} heads "
+                  f"({tokens} tokens, {dt:.1f} s, fp64 NumPy, one thread, {platform.processor() or platform.machine()})",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(how it would shard is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mamba_ssd_scan_fwd_amd as ssd
+    from ssd_inputs import CONFIGS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ssd.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = CONFIGS[args.config]
+    inp = make_inputs(cfg, seed=args.config)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    io_bytes = 2 if cfg.io_dtype == "bf16" else 4
+    desc = ssd.make_desc(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups,
+                         cfg.io_dtype, args.chunk)
+    Q = ssd.effective_chunk_size(desc)
+    ws = torch.empty(ssd.workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(d["x"])
+    hT = torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], chunk_size=args.chunk,
+                    y=y, final_state=hT, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+    tokens_per_s = cfg.tokens * args.steps / (gpu_ms / 1e3)
+
+    # ---- every kernel on its own: HIP events on the launch stream ----------
+    reps = args.kernel_reps or max(10, min(args.steps, 50))
+    nc = -(-cfg.seqlen // Q)
+    cs = torch.empty((cfg.batch, cfg.nheads, nc, Q), dtype=torch.float32, device=dev)
+    dtc = torch.empty_like(cs)
+    st = torch.empty((cfg.batch, cfg.nheads, nc, cfg.headdim, cfg.dstate), dtype=d["x"].dtype, device=dev)
+    kw = dict(chunk_size=args.chunk)
+    common = dict(headdim=cfg.headdim, dstate=cfg.dstate, ngroups=cfg.ngroups, io_dtype=cfg.io_dtype)
+
+    def k_cumsum():
+        lib = ssd.load_library()
+        import ctypes
+        r = lib.ssd_chunk_cumsum(ctypes.byref(desc), ctypes.c_void_p(d["dt"].data_ptr()),
+                                 ctypes.c_void_p(d["A"].data_ptr()), ctypes.c_void_p(cs.data_ptr()),
+                                 ctypes.c_void_p(dtc.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        assert r == 0
+
+    def k_state():
+        lib = ssd.load_library()
+        import ctypes
+        r = lib.ssd_chunk_state(ctypes.byref(desc), ctypes.c_void_p(d["x"].data_ptr()),
+                                ctypes.c_void_p(d["B"].data_ptr()), ctypes.c_void_p(cs.data_ptr()),
+                                ctypes.c_void_p(dtc.data_ptr()), ctypes.c_void_p(st.data_ptr()),
+                                ctypes.c_void_p(stream.cuda_stream))
+        assert r == 0
+
+    def k_pass():
+        lib = ssd.load_library()
+        import ctypes
+        h0 = d["init_state"]
+        r = lib.ssd_state_passing(ctypes.byref(desc), ctypes.c_void_p(st.data_ptr()),
+                                  ctypes.c_void_p(cs.data_ptr()),
+                                  None if h0 is None else ctypes.c_void_p(h0.data_ptr()),
+                                  ctypes.c_void_p(hT.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        assert r == 0
+
+    def k_scan():
+        lib = ssd.load_library()
+        import ctypes
+        Dp = None if d["D"] is None else ctypes.c_void_p(d["D"].data_ptr())
+        r = lib.ssd_chunk_scan(ctypes.byref(desc), ctypes.c_void_p(d["x"].data_ptr()),
+                               ctypes.c_void_p(d["B"].data_ptr()), ctypes.c_void_p(d["C"].data_ptr()), Dp,
+                               ctypes.c_void_p(cs.data_ptr()), ctypes.c_void_p(dtc.data_ptr()),
+                               ctypes.c_void_p(st.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                               ctypes.c_void_p(stream.cuda_stream))
+        assert r == 0
+
+    del kw, common
+    kernels = [("chunk_cumsum", k_cumsum, None), ("chunk_state", k_state, None),
+               ("state_passing", k_pass, k_state), ("chunk_scan", k_scan, None)]
+    k_cumsum(); k_state(); k_pass()  # noqa: E702  -- entering states for chunk_scan
+    torch.cuda.synchronize()
+    durations = {}
+    for name, fn, reset in kernels:
+        evs = []
+        for _ in range(reps):
+            if reset is not None:
+                reset()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        durations[name] = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3  # us
+    model = algorithmic_model(cfg, Q, io_bytes)
+    per_kernel = {}
+    for name, us in durations.items():
+        m = model[name]
+        per_kernel[name] = {
+            "avg_us": round(us, 2),
+            "algo_bytes": m["bytes"],
+            "algo_flops": m["flops"],
+            "GB_per_s": round(m["bytes"] / (us * 1e-6) / 1e9, 1),
+            "TFLOP_per_s": round(m["flops"] / (us * 1e-6) / 1e12, 2),
+        }
+    dom = max(durations, key=durations.get)
+    m = model[dom]
+    ach_gbs = m["bytes"] / (durations[dom] * 1e-6) / 1e9
+    traffic = traffic_from_profile(dom, cfg.name, m["bytes"])
+    roofline = {
+        "kernel": dom,
+        "bound": "hbm",
+        "achieved": round(ach_gbs, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(ach_gbs / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "algo_bytes_per_launch": m["bytes"],
+        "avg_launch_us": round(durations[dom], 2),
+        "mfma_frac_useful": round(m["flops"] / (durations[dom] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, inp, min(args.cpu_sample_seqs, cfg.batch))
+
+    total_flops = sum(v["flops"] for v in model.values())
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.io_dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "nheads": cfg.nheads,
+                   "headdim": cfg.headdim, "dstate": cfg.dstate, "ngroups": cfg.ngroups,
+                   "chunk": Q, "init_state": cfg.init_state},
+        "tflops_per_s": round(total_flops * args.steps / (gpu_ms / 1e3) / 1e12, 2),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "kernels": per_kernel,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * ssd.h -- C ABI of the Mamba-2 SSD (structured state-space duality) forward
+ * pass for AMD Instinct MI355X (gfx950).
+ *
+ * The operator (one selective SSM layer core, per batch b and head h with
+ * B/C group g = h / (nheads / ngroups)):
+ *
+ *     h_t      = exp(dt_t * A_h) * h_{t-1} + dt_t * x_t B_t^T      (P x N state)
+ *     y_t      = h_t C_t + D_h * x_t
+ *     h_{-1}   = init_state (zeros when NULL);   final_state = h_{L-1}
+ *
+ * The transition is one scalar per head times the identity (Telegram post
+ * "Mamba3", opening paragraph; "Mamba-3 : SSM optimise inference", section
+ * "Du training-first a l'inference-first"), discretised with zero-order hold
+ * for A and an Euler step for B ("Mamba3", discretisation section). It is
+ * evaluated with the blocked two-pass algorithm: the sequence is cut into
+ * chunks of Q tokens processed in parallel, and the per-chunk states are then
+ * recombined ("Mamba-2 vs Transformers: SSMs, structured state space
+ * duality", section "Mamba-2 and the SSD paper: what changed in practice").
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Tensor pointers are DEVICE pointers to dense row-major arrays; the caller
+ *    owns them and keeps them alive until the enqueued work has completed.
+ *    The library keeps no pointer after a call returns and holds no mutable
+ *    global state, so calls from several host threads are safe.
+ *  - Calls are asynchronous: kernels are enqueued on `stream` (a hipStream_t;
+ *    NULL is the default stream) and nothing is synchronised.
+ *  - All arguments are validated before anything is enqueued; on any error
+ *    nothing is written. SSD_ERR_HIP reports a failed kernel launch; faults
+ *    inside kernels surface at the caller's next synchronisation.
+ *  - No C++ exception crosses this boundary.
+ *
+ * Layouts (row-major, innermost last), with L = seqlen, H = nheads,
+ * P = headdim, N = dstate, G = ngroups, Q = chunk size, nc = ceil(L / Q):
+ *     x, y            [batch, L, H, P]     io dtype
+ *     dt              [batch, L, H]        fp32, used as given (no softplus)
+ *     A, D            [H]                  fp32 (A <= 0 expected; D nullable)
+ *     B, C            [batch, L, G, N]     io dtype
+ *     init_state,
+ *     final_state     [batch, H, P, N]     fp32
+ *   Chunked intermediates (the workspace; see ssd_workspace_bytes):
+ *     dA_cumsum       [batch, H, nc, Q]    fp32, inclusive sum of dt*A within
+ *                                          the chunk (positions >= L: dt = 0)
+ *     dt_chunked      [batch, H, nc, Q]    fp32, dt regrouped per chunk, 0 past L
+ *     states          [batch, H, nc, P, N] state dtype (= io dtype): the local
+ *                                          state of each chunk, overwritten in
+ *                                          place by the state entering it.
+ *
+ * Supported: io dtype fp32 or bf16; P in {16, 32, 64, 128};
+ * N in {16, 32, 64, 128, 256}; H % G == 0; chunk_size in {0 (default), 64,
+ * 128, 256}. Base pointers of x, B, C, y, init_state, final_state must be
+ * 16-byte aligned, dt/A/D 4-byte aligned, the workspace 256-byte aligned.
+ */
+#ifndef SSD_H_
+#define SSD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SSD_API __attribute__((visibility("default")))
+#else
+#define SSD_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSD_DTYPE_F32 = 0,
+  SSD_DTYPE_BF16 = 1
+} ssd_dtype_t;
+
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_NULL_POINTER = 1, /* a required pointer is NULL                     */
+  SSD_ERR_BAD_SHAPE = 2,    /* a dimension <= 0, H % G != 0, or too large     */
+  SSD_ERR_UNSUPPORTED = 3,  /* P, N, dtype or chunk size outside the set above */
+  SSD_ERR_ALIGNMENT = 4,    /* a base pointer is misaligned                    */
+  SSD_ERR_WORKSPACE = 5,    /* workspace given but smaller than required       */
+  SSD_ERR_ALIAS = 6,        /* an output overlaps an input it must not overlap */
+  SSD_ERR_HIP = 7           /* the HIP runtime reported an error               */
+} ssd_status_t;
+
+/* Problem description. Plain data; the library reads it during the call only. */
+typedef struct {
+  int64_t batch;
+  int64_t seqlen;     /* L  */
+  int64_t nheads;     /* H  */
+  int64_t headdim;    /* P  */
+  int64_t dstate;     /* N  */
+  int64_t ngroups;    /* G  */
+  int32_t io_dtype;   /* ssd_dtype_t: dtype of x, B, C, y (and of states)     */
+  int32_t chunk_size; /* Q: 0 picks the library default for the shape         */
+} ssd_desc_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+SSD_API const char* ssd_status_string(int status);
+
+/* Chunk length Q the library will use for `desc` (resolves chunk_size == 0). */
+SSD_API ssd_status_t ssd_effective_chunk_size(const ssd_desc_t* desc, int32_t* chunk_size);
+
+/* Bytes of device workspace ssd_forward needs for `desc`: dA_cumsum,
+ * dt_chunked and states, each starting on a 256-byte boundary, in that order.
+ * Pure host computation; no HIP call. */
+SSD_API ssd_status_t ssd_workspace_bytes(const ssd_desc_t* desc, size_t* bytes);
+
+/* The whole forward pass: y and (when final_state != NULL) the final state.
+ *   x, dt, A, B, C, y        required.
+ *   D           nullable: NULL means D = 0 (no skip term).
+ *   init_state  nullable: NULL means a zero initial state.
+ *   final_state nullable: NULL means it is not written. It may be the same
+ *               pointer as init_state (in-place state update); partial
+ *               overlap is rejected.
+ *   workspace   nullable: NULL makes the library allocate and free it in
+ *               stream order (hipMallocAsync / hipFreeAsync); otherwise at
+ *               least ssd_workspace_bytes() bytes, 256-byte aligned, not
+ *               overlapping any other argument.
+ *   y must not overlap any input.
+ * Runs the five steps below on `stream`, in order. */
+SSD_API ssd_status_t ssd_forward(const ssd_desc_t* desc,
+                         const void* x, const float* dt, const float* A,
+                         const void* B, const void* C, const float* D,
+                         const float* init_state,
+                         void* y, float* final_state,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* ---- the steps of the chunked path, each callable on its own ------------ */
+
+/* Step 1, chunk cumulative sum of dt*A ("Mamba-2 vs Transformers", section
+ * "Mamba-2 and the SSD paper: what changed in practice": chunks processed in
+ * parallel). Writes dA_cumsum and dt_chunked ([batch, H, nc, Q] fp32 each). */
+SSD_API ssd_status_t ssd_chunk_cumsum(const ssd_desc_t* desc, const float* dt, const float* A,
+                              float* dA_cumsum, float* dt_chunked, void* stream);
+
+/* Step 2, local state of every chunk (same section: the per-chunk SSM
+ * states), on matrix cores for bf16:
+ *   states[b,h,c] = sum_{j in c} exp(Lam_c - l_j) dt_j x_j B_j^T,
+ * with l = dA_cumsum and Lam_c its last entry in chunk c.
+ * Writes states [batch, H, nc, P, N] in the io dtype. */
+SSD_API ssd_status_t ssd_chunk_state(const ssd_desc_t* desc, const void* x, const void* B,
+                             const float* dA_cumsum, const float* dt_chunked,
+                             void* states, void* stream);
+
+/* Step 3, inter-chunk state passing (same section: the per-chunk states are
+ * recombined). In place over `states`: on return states[b,h,c] holds the
+ * state entering chunk c,  H_{-1} = init_state (or 0),
+ * Hin_c = H_{c-1},  H_c = exp(Lam_c) H_{c-1} + S_c. Writes final_state
+ * (= H_{nc-1}) in fp32 when non-NULL; final_state may equal init_state. */
+SSD_API ssd_status_t ssd_state_passing(const ssd_desc_t* desc, void* states, const float* dA_cumsum,
+                               const float* init_state, float* final_state, void* stream);
+
+/* Steps 4 and 5 fused, intra-chunk output on matrix cores plus the chunk
+ * output from the entering state (the masked dual form inside a chunk,
+ * "Mamba-2 vs Transformers", contraction-order table):
+ *   y_i = sum_{j<=i in chunk} exp(l_i - l_j) dt_j (C_i . B_j) x_j
+ *       + exp(l_i) Hin_c C_i + D_h x_i.
+ * `states` must hold the entering states (the output of step 3). */
+SSD_API ssd_status_t ssd_chunk_scan(const ssd_desc_t* desc, const void* x, const void* B, const void* C,
+                            const float* D, const float* dA_cumsum, const float* dt_chunked,
+                            const void* states, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H_ */

@@ -1,0 +1,23 @@
+"""Mamba-2 SSD forward pass for AMD Instinct MI355X (gfx950).
+
+The computation lives in ``libssd.so`` (C ABI declared in include/ssd.h, HIP
+kernels under csrc/); this package is its thin Python binding. Build the
+library with ``python -m mamba_ssd_scan_fwd_amd.build``.
+"""
+
+from .binding import (  # noqa: F401
+    EXPORTED_SYMBOLS,
+    SSDDesc,
+    SSDError,
+    chunk_cumsum,
+    chunk_scan,
+    chunk_state,
+    effective_chunk_size,
+    forward,
+    lib_path,
+    load_library,
+    make_desc,
+    state_passing,
+    status_string,
+    workspace_bytes,
+)

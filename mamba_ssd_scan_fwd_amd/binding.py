@@ -1,0 +1,311 @@
+"""ctypes binding of libssd.so: argument marshalling only.
+
+PyTorch provides device memory and the current stream; every step of the
+computation runs in the library's HIP kernels. If the library has not been
+built, every call raises -- there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "SSDError",
+    "SSDDesc",
+    "lib_path",
+    "load_library",
+    "make_desc",
+    "status_string",
+    "effective_chunk_size",
+    "workspace_bytes",
+    "forward",
+    "chunk_cumsum",
+    "chunk_state",
+    "state_passing",
+    "chunk_scan",
+    "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+# Every symbol include/ssd.h declares.
+EXPORTED_SYMBOLS = (
+    "ssd_status_string",
+    "ssd_effective_chunk_size",
+    "ssd_workspace_bytes",
+    "ssd_forward",
+    "ssd_chunk_cumsum",
+    "ssd_chunk_state",
+    "ssd_state_passing",
+    "ssd_chunk_scan",
+)
+
+SSD_DTYPE_F32 = 0
+SSD_DTYPE_BF16 = 1
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class SSDDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("seqlen", ctypes.c_int64),
+        ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64),
+        ("ngroups", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32),
+    ]
+
+
+def lib_path() -> str:
+    return os.environ.get("SSD_LIB", os.path.join(_HERE, "libssd.so"))
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library():
+    """Load libssd.so once. Raises if it is missing: build it first with
+    ``python -m mamba_ssd_scan_fwd_amd.build``."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"libssd.so not found at {path}; build it with `python -m mamba_ssd_scan_fwd_amd.build`"
+            )
+        lib = ctypes.CDLL(path)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        dp = ctypes.POINTER(SSDDesc)
+        lib.ssd_status_string.argtypes = [ctypes.c_int]
+        lib.ssd_status_string.restype = ctypes.c_char_p
+        lib.ssd_effective_chunk_size.argtypes = [dp, ctypes.POINTER(i32)]
+        lib.ssd_effective_chunk_size.restype = ctypes.c_int
+        lib.ssd_workspace_bytes.argtypes = [dp, ctypes.POINTER(sz)]
+        lib.ssd_workspace_bytes.restype = ctypes.c_int
+        lib.ssd_forward.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.ssd_forward.restype = ctypes.c_int
+        lib.ssd_chunk_cumsum.argtypes = [dp, vp, vp, vp, vp, vp]
+        lib.ssd_chunk_cumsum.restype = ctypes.c_int
+        lib.ssd_chunk_state.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+        lib.ssd_chunk_state.restype = ctypes.c_int
+        lib.ssd_state_passing.argtypes = [dp, vp, vp, vp, vp, vp]
+        lib.ssd_state_passing.restype = ctypes.c_int
+        lib.ssd_chunk_scan.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.ssd_chunk_scan.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ssd_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SSDError(status, where)
+
+
+def make_desc(batch, seqlen, nheads, headdim, dstate, ngroups, io_dtype, chunk_size=0) -> SSDDesc:
+    if isinstance(io_dtype, torch.dtype):
+        io = {torch.float32: SSD_DTYPE_F32, torch.bfloat16: SSD_DTYPE_BF16}.get(io_dtype)
+        if io is None:
+            raise TypeError(f"unsupported io dtype {io_dtype}")
+    elif io_dtype in ("fp32", "f32", "float32"):
+        io = SSD_DTYPE_F32
+    elif io_dtype in ("bf16", "bfloat16"):
+        io = SSD_DTYPE_BF16
+    else:
+        io = int(io_dtype)
+    return SSDDesc(int(batch), int(seqlen), int(nheads), int(headdim), int(dstate), int(ngroups), io,
+                   int(chunk_size))
+
+
+def effective_chunk_size(desc: SSDDesc) -> int:
+    q = ctypes.c_int32(0)
+    _check(load_library().ssd_effective_chunk_size(ctypes.byref(desc), ctypes.byref(q)),
+           "ssd_effective_chunk_size")
+    return int(q.value)
+
+
+def workspace_bytes(desc: SSDDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().ssd_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "ssd_workspace_bytes")
+    return int(n.value)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype=None, device=None, shape=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _desc_from(x, B, chunk_size):
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return make_desc(bsz, L, H, P, N, G, x.dtype, chunk_size)
+
+
+def forward(x, dt, A, B, C, D=None, init_state=None, *, chunk_size: int = 0,
+            return_final_state: bool = True, y=None, final_state=None, workspace=None,
+            library_workspace: bool = False, stream=None):
+    """SSD forward pass on the GPU. Returns (y, final_state or None).
+
+    x [b, L, H, P] and B, C [b, L, G, N] in fp32 or bf16 (all the same);
+    dt [b, L, H], A [H], D [H] (optional) and init_state [b, H, P, N]
+    (optional) in fp32. ``final_state`` may be passed as ``init_state`` for an
+    in-place state update. With ``library_workspace=True`` the library
+    allocates its workspace itself, in stream order.
+    """
+    dev = x.device
+    _need(x, "x", device=dev)
+    io = x.dtype
+    bsz, L, H, P = x.shape
+    _need(B, "B", io, dev)
+    G, N = B.shape[2], B.shape[3]
+    _need(C, "C", io, dev, B.shape)
+    _need(dt, "dt", torch.float32, dev, (bsz, L, H))
+    _need(A, "A", torch.float32, dev, (H,))
+    if D is not None:
+        _need(D, "D", torch.float32, dev, (H,))
+    if init_state is not None:
+        _need(init_state, "init_state", torch.float32, dev, (bsz, H, P, N))
+    desc = _desc_from(x, B, chunk_size)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", io, dev, x.shape)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _need(final_state, "final_state", torch.float32, dev, (bsz, H, P, N))
+    nws = workspace_bytes(desc)
+    if library_workspace:
+        workspace, wsize = None, 0
+    elif workspace is None:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+        wsize = nws
+    else:
+        wsize = workspace.numel() * workspace.element_size()
+        if wsize < nws:
+            raise ValueError(f"workspace needs {nws} bytes")
+    st = load_library().ssd_forward(
+        ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state),
+        _ptr(y), _ptr(final_state), _ptr(workspace), ctypes.c_size_t(wsize), _stream(stream, dev))
+    _check(st, "ssd_forward")
+    return y, final_state
+
+
+def _chunk_shape(desc):
+    q = effective_chunk_size(desc)
+    nc = -(-desc.seqlen // q)
+    return q, nc
+
+
+def chunk_cumsum(dt, A, *, headdim, dstate, ngroups=1, io_dtype=torch.bfloat16, chunk_size=0, stream=None):
+    """Step 1 alone. Returns (dA_cumsum, dt_chunked), each [b, H, nc, Q] fp32."""
+    dev = dt.device
+    _need(dt, "dt", torch.float32, dev)
+    bsz, L, H = dt.shape
+    _need(A, "A", torch.float32, dev, (H,))
+    desc = make_desc(bsz, L, H, headdim, dstate, ngroups, io_dtype, chunk_size)
+    q, nc = _chunk_shape(desc)
+    cs = torch.empty((bsz, H, nc, q), dtype=torch.float32, device=dev)
+    dtc = torch.empty_like(cs)
+    _check(load_library().ssd_chunk_cumsum(ctypes.byref(desc), _ptr(dt), _ptr(A), _ptr(cs), _ptr(dtc),
+                                           _stream(stream, dev)), "ssd_chunk_cumsum")
+    return cs, dtc
+
+
+def chunk_state(x, B, dA_cumsum, dt_chunked, *, chunk_size=0, stream=None):
+    """Step 2 alone. Returns states [b, H, nc, P, N] in the io dtype."""
+    dev = x.device
+    _need(x, "x", device=dev)
+    _need(B, "B", x.dtype, dev)
+    desc = _desc_from(x, B, chunk_size)
+    q, nc = _chunk_shape(desc)
+    bsz, L, H, P = x.shape
+    _need(dA_cumsum, "dA_cumsum", torch.float32, dev, (bsz, H, nc, q))
+    _need(dt_chunked, "dt_chunked", torch.float32, dev, (bsz, H, nc, q))
+    states = torch.empty((bsz, H, nc, P, B.shape[3]), dtype=x.dtype, device=dev)
+    _check(load_library().ssd_chunk_state(ctypes.byref(desc), _ptr(x), _ptr(B), _ptr(dA_cumsum),
+                                          _ptr(dt_chunked), _ptr(states), _stream(stream, dev)),
+           "ssd_chunk_state")
+    return states
+
+
+def state_passing(states, dA_cumsum, init_state=None, *, seqlen, ngroups=1, chunk_size=0,
+                  return_final_state=True, final_state=None, stream=None):
+    """Step 3 alone, in place over ``states``. Returns (states, final_state)."""
+    dev = states.device
+    _need(states, "states", device=dev)
+    bsz, H, nc, P, N = states.shape
+    desc = make_desc(bsz, seqlen, H, P, N, ngroups, states.dtype, chunk_size)
+    q, nc2 = _chunk_shape(desc)
+    if nc2 != nc:
+        raise ValueError("states does not match seqlen / chunk size")
+    _need(dA_cumsum, "dA_cumsum", torch.float32, dev, (bsz, H, nc, q))
+    if init_state is not None:
+        _need(init_state, "init_state", torch.float32, dev, (bsz, H, P, N))
+    if final_state is None and return_final_state:
+        final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=dev)
+    _check(load_library().ssd_state_passing(ctypes.byref(desc), _ptr(states), _ptr(dA_cumsum),
+                                            _ptr(init_state), _ptr(final_state), _stream(stream, dev)),
+           "ssd_state_passing")
+    return states, final_state
+
+
+def chunk_scan(x, B, C, D, dA_cumsum, dt_chunked, states, *, chunk_size=0, y=None, stream=None):
+    """Steps 4+5 alone. ``states`` holds the entering states. Returns y."""
+    dev = x.device
+    _need(x, "x", device=dev)
+    _need(B, "B", x.dtype, dev)
+    _need(C, "C", x.dtype, dev, B.shape)
+    desc = _desc_from(x, B, chunk_size)
+    q, nc = _chunk_shape(desc)
+    bsz, L, H, P = x.shape
+    _need(dA_cumsum, "dA_cumsum", torch.float32, dev, (bsz, H, nc, q))
+    _need(dt_chunked, "dt_chunked", torch.float32, dev, (bsz, H, nc, q))
+    _need(states, "states", x.dtype, dev, (bsz, H, nc, P, B.shape[3]))
+    if D is not None:
+        _need(D, "D", torch.float32, dev, (H,))
+    if y is None:
+        y = torch.empty_like(x)
+    _check(load_library().ssd_chunk_scan(ctypes.byref(desc), _ptr(x), _ptr(B), _ptr(C), _ptr(D),
+                                         _ptr(dA_cumsum), _ptr(dt_chunked), _ptr(states), _ptr(y),
+                                         _stream(stream, dev)), "ssd_chunk_scan")
+    return y

@@ -1,0 +1,302 @@
+// C ABI of the SSD forward pass: argument validation, planning (chunk length,
+// workspace carve-up) and the enqueue of the step kernels. Everything up to
+// the first launch is plain host code with no HIP call, so the validation is
+// testable without a GPU.
+#include "../../include/ssd.h"
+
+#include <cstdint>
+#include <cstring>
+#include <cstdlib>
+#include <cstdio>
+
+#include "ssd_internal.h"
+
+namespace ssd {
+hipError_t launch_chunk_state_simt(const Plan& p, const void* x, const void* B,
+                                   const float* dA_cs, const float* dtc, void* states,
+                                   hipStream_t s);
+hipError_t launch_chunk_scan_simt(const Plan& p, const void* x, const void* B, const void* C,
+                                  const float* D, const float* dA_cs, const float* dtc,
+                                  const void* states, void* y, hipStream_t s);
+bool mfma_chunk_state_supported(const Plan& p);
+bool mfma_chunk_scan_supported(const Plan& p);
+hipError_t launch_chunk_state_mfma(const Plan& p, const void* x, const void* B,
+                                   const float* dA_cs, const float* dtc, void* states,
+                                   hipStream_t s);
+hipError_t launch_chunk_scan_mfma(const Plan& p, const void* x, const void* B, const void* C,
+                                  const float* D, const float* dA_cs, const float* dtc,
+                                  const void* states, void* y, hipStream_t s);
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool is_pow2_in(int64_t v, int64_t lo, int64_t hi) {
+  return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+// Limits keep every grid dimension and every 32-bit in-kernel index in range.
+constexpr int64_t kMaxBatch = 65535;
+constexpr int64_t kMaxHeads = 65535;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+int default_chunk(const ssd_desc_t& d) {
+  // 256 halves the chunk-state traffic of 128 and keeps the intra-chunk
+  // tiles within the register budget up to N = 256.
+  (void)d;
+  return 256;
+}
+
+ssd_status_t make_plan(const ssd_desc_t* d, Plan* p) {
+  if (d == nullptr || p == nullptr) return SSD_ERR_NULL_POINTER;
+  if (d->batch <= 0 || d->seqlen <= 0 || d->nheads <= 0 || d->headdim <= 0 ||
+      d->dstate <= 0 || d->ngroups <= 0)
+    return SSD_ERR_BAD_SHAPE;
+  if (d->nheads % d->ngroups != 0) return SSD_ERR_BAD_SHAPE;
+  if (d->batch > kMaxBatch || d->nheads > kMaxHeads || d->batch * d->nheads > (int64_t(1) << 31))
+    return SSD_ERR_BAD_SHAPE;
+  if (d->io_dtype != SSD_DTYPE_F32 && d->io_dtype != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+  if (!is_pow2_in(d->headdim, 16, 128)) return SSD_ERR_UNSUPPORTED;
+  if (!is_pow2_in(d->dstate, 16, 256)) return SSD_ERR_UNSUPPORTED;
+  int Q = d->chunk_size;
+  if (Q == 0) Q = default_chunk(*d);
+  if (Q != 64 && Q != 128 && Q != 256) return SSD_ERR_UNSUPPORTED;
+  const int64_t nc = (d->seqlen + Q - 1) / Q;
+  // element counts of the largest arrays must stay well inside 64-bit byte math
+  if (d->batch * d->seqlen > kMaxElems / (d->nheads * d->headdim)) return SSD_ERR_BAD_SHAPE;
+  if (d->batch * d->nheads * nc > kMaxElems / (d->headdim * d->dstate)) return SSD_ERR_BAD_SHAPE;
+  // flattened 1-D grids: (batch * heads * chunks * row blocks) must fit grid.x
+  if (d->batch * d->nheads * nc * (Q / 16) >= (int64_t(1) << 31)) return SSD_ERR_BAD_SHAPE;
+  p->batch = d->batch;
+  p->L = d->seqlen;
+  p->H = d->nheads;
+  p->P = d->headdim;
+  p->N = d->dstate;
+  p->G = d->ngroups;
+  p->io = d->io_dtype == SSD_DTYPE_BF16 ? kBF16 : kF32;
+  p->Q = Q;
+  p->nc = nc;
+  return SSD_OK;
+}
+
+struct WsLayout {
+  size_t cs_off, dt_off, st_off, total;
+};
+
+WsLayout ws_layout(const Plan& p) {
+  WsLayout w;
+  const size_t cs_bytes = size_t(p.batch * p.H * p.nc * p.Q) * sizeof(float);
+  const size_t st_bytes = size_t(p.batch * p.H * p.nc * p.P * p.N) * p.io_bytes();
+  w.cs_off = 0;
+  w.dt_off = align_up(w.cs_off + cs_bytes, kWsAlign);
+  w.st_off = align_up(w.dt_off + cs_bytes, kWsAlign);
+  w.total = align_up(w.st_off + st_bytes, kWsAlign);
+  return w;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* ptr, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+  return Range{lo, lo + bytes};
+}
+bool overlap(const Range& a, const Range& b) {
+  if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+ssd_status_t from_hip(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+bool debug_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("SSD_DEBUG");
+    return v != nullptr && v[0] != '\0' && v[0] != '0';
+  }();
+  return on;
+}
+
+// Kernel choice per step. The bf16 io dtype runs the matrix-core kernels; the
+// fp32 io dtype keeps fp32 operands and runs the FMA kernels.
+hipError_t run_chunk_state(const Plan& p, const void* x, const void* B, const float* cs,
+                           const float* dtc, void* st, hipStream_t s) {
+  if (mfma_chunk_state_supported(p)) return launch_chunk_state_mfma(p, x, B, cs, dtc, st, s);
+  return launch_chunk_state_simt(p, x, B, cs, dtc, st, s);
+}
+hipError_t run_chunk_scan(const Plan& p, const void* x, const void* B, const void* C,
+                          const float* D, const float* cs, const float* dtc, const void* st,
+                          void* y, hipStream_t s) {
+  if (mfma_chunk_scan_supported(p)) return launch_chunk_scan_mfma(p, x, B, C, D, cs, dtc, st, y, s);
+  return launch_chunk_scan_simt(p, x, B, C, D, cs, dtc, st, y, s);
+}
+
+}  // namespace
+}  // namespace ssd
+
+using ssd::Plan;
+
+extern "C" {
+
+const char* ssd_status_string(int status) {
+  switch (status) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_NULL_POINTER: return "SSD_ERR_NULL_POINTER: a required pointer is NULL";
+    case SSD_ERR_BAD_SHAPE: return "SSD_ERR_BAD_SHAPE: a dimension is <= 0 or too large, or nheads % ngroups != 0";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: headdim, dstate, dtype or chunk size not supported";
+    case SSD_ERR_ALIGNMENT: return "SSD_ERR_ALIGNMENT: a base pointer is misaligned";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace smaller than ssd_workspace_bytes()";
+    case SSD_ERR_ALIAS: return "SSD_ERR_ALIAS: an output overlaps an input";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown ssd_status_t";
+  }
+}
+
+ssd_status_t ssd_effective_chunk_size(const ssd_desc_t* desc, int32_t* chunk_size) {
+  if (chunk_size == nullptr) return SSD_ERR_NULL_POINTER;
+  Plan p;
+  const ssd_status_t st = ssd::make_plan(desc, &p);
+  if (st != SSD_OK) return st;
+  *chunk_size = p.Q;
+  return SSD_OK;
+}
+
+ssd_status_t ssd_workspace_bytes(const ssd_desc_t* desc, size_t* bytes) {
+  if (bytes == nullptr) return SSD_ERR_NULL_POINTER;
+  Plan p;
+  const ssd_status_t st = ssd::make_plan(desc, &p);
+  if (st != SSD_OK) return st;
+  *bytes = ssd::ws_layout(p).total;
+  return SSD_OK;
+}
+
+ssd_status_t ssd_forward(const ssd_desc_t* desc, const void* x, const float* dt, const float* A,
+                         const void* B, const void* C, const float* D, const float* init_state,
+                         void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  Plan p;
+  ssd_status_t st = ssd::make_plan(desc, &p);
+  if (st != SSD_OK) return st;
+  if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL_POINTER;
+  if (!ssd::aligned(x, 16) || !ssd::aligned(B, 16) || !ssd::aligned(C, 16) || !ssd::aligned(y, 16) ||
+      !ssd::aligned(init_state, 16) || !ssd::aligned(final_state, 16) || !ssd::aligned(dt, 4) ||
+      !ssd::aligned(A, 4) || !ssd::aligned(D, 4) || !ssd::aligned(workspace, ssd::kWsAlign))
+    return SSD_ERR_ALIGNMENT;
+  const ssd::WsLayout ws = ssd::ws_layout(p);
+  if (workspace != nullptr && workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
+
+  const size_t io = p.io_bytes();
+  const size_t xy_bytes = size_t(p.batch * p.L * p.H * p.P) * io;
+  const size_t bc_bytes = size_t(p.batch * p.L * p.G * p.N) * io;
+  const size_t dt_bytes = size_t(p.batch * p.L * p.H) * sizeof(float);
+  const size_t hd_bytes = size_t(p.H) * sizeof(float);
+  const size_t st_bytes = size_t(p.batch * p.H * p.P * p.N) * sizeof(float);
+  const ssd::Range in[] = {ssd::range_of(x, xy_bytes),   ssd::range_of(dt, dt_bytes),
+                           ssd::range_of(A, hd_bytes),   ssd::range_of(B, bc_bytes),
+                           ssd::range_of(C, bc_bytes),   ssd::range_of(D, hd_bytes),
+                           ssd::range_of(init_state, st_bytes)};
+  const ssd::Range ry = ssd::range_of(y, xy_bytes);
+  const ssd::Range rf = ssd::range_of(final_state, st_bytes);
+  const ssd::Range rw = ssd::range_of(workspace, ws.total);
+  for (const ssd::Range& r : in) {
+    if (ssd::overlap(ry, r)) return SSD_ERR_ALIAS;
+    if (ssd::overlap(rw, r)) return SSD_ERR_ALIAS;
+    // final_state may be exactly init_state (in-place); any other overlap is an error
+    if (ssd::overlap(rf, r) && !(r.lo == reinterpret_cast<uintptr_t>(init_state) && rf.lo == r.lo))
+      return SSD_ERR_ALIAS;
+  }
+  if (ssd::overlap(ry, rf) || ssd::overlap(ry, rw) || ssd::overlap(rf, rw)) return SSD_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* wbase = workspace;
+  bool owned = false;
+  if (wbase == nullptr) {
+    if (hipMallocAsync(&wbase, ws.total, s) != hipSuccess) return SSD_ERR_HIP;
+    owned = true;
+  }
+  char* w = static_cast<char*>(wbase);
+  float* cs = reinterpret_cast<float*>(w + ws.cs_off);
+  float* dtc = reinterpret_cast<float*>(w + ws.dt_off);
+  void* states = w + ws.st_off;
+  if (ssd::debug_enabled())
+    std::fprintf(stderr, "[ssd] B=%lld L=%lld H=%lld P=%lld N=%lld G=%lld io=%s Q=%d nc=%lld ws=%zu state=%s scan=%s\n",
+                 (long long)p.batch, (long long)p.L, (long long)p.H, (long long)p.P, (long long)p.N,
+                 (long long)p.G, p.io == ssd::kBF16 ? "bf16" : "fp32", p.Q, (long long)p.nc, ws.total,
+                 ssd::mfma_chunk_state_supported(p) ? "mfma" : "simt",
+                 ssd::mfma_chunk_scan_supported(p) ? "mfma" : "simt");
+
+  hipError_t e = ssd::launch_chunk_cumsum(p, dt, A, cs, dtc, s);
+  if (e == hipSuccess) e = ssd::run_chunk_state(p, x, B, cs, dtc, states, s);
+  if (e == hipSuccess) e = ssd::launch_state_passing(p, states, cs, init_state, final_state, s);
+  if (e == hipSuccess) e = ssd::run_chunk_scan(p, x, B, C, D, cs, dtc, states, y, s);
+  if (owned) {
+    const hipError_t fe = hipFreeAsync(wbase, s);
+    if (e == hipSuccess) e = fe;
+  }
+  return ssd::from_hip(e);
+}
+
+ssd_status_t ssd_chunk_cumsum(const ssd_desc_t* desc, const float* dt, const float* A,
+                              float* dA_cumsum, float* dt_chunked, void* stream) {
+  Plan p;
+  ssd_status_t st = ssd::make_plan(desc, &p);
+  if (st != SSD_OK) return st;
+  if (!dt || !A || !dA_cumsum || !dt_chunked) return SSD_ERR_NULL_POINTER;
+  if (!ssd::aligned(dt, 4) || !ssd::aligned(A, 4) || !ssd::aligned(dA_cumsum, 16) ||
+      !ssd::aligned(dt_chunked, 16))
+    return SSD_ERR_ALIGNMENT;
+  return ssd::from_hip(
+      ssd::launch_chunk_cumsum(p, dt, A, dA_cumsum, dt_chunked, static_cast<hipStream_t>(stream)));
+}
+
+ssd_status_t ssd_chunk_state(const ssd_desc_t* desc, const void* x, const void* B,
+                             const float* dA_cumsum, const float* dt_chunked, void* states,
+                             void* stream) {
+  Plan p;
+  ssd_status_t st = ssd::make_plan(desc, &p);
+  if (st != SSD_OK) return st;
+  if (!x || !B || !dA_cumsum || !dt_chunked || !states) return SSD_ERR_NULL_POINTER;
+  if (!ssd::aligned(x, 16) || !ssd::aligned(B, 16) || !ssd::aligned(dA_cumsum, 16) ||
+      !ssd::aligned(dt_chunked, 16) || !ssd::aligned(states, 16))
+    return SSD_ERR_ALIGNMENT;
+  return ssd::from_hip(ssd::run_chunk_state(p, x, B, dA_cumsum, dt_chunked, states,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+ssd_status_t ssd_state_passing(const ssd_desc_t* desc, void* states, const float* dA_cumsum,
+                               const float* init_state, float* final_state, void* stream) {
+  Plan p;
+  ssd_status_t st = ssd::make_plan(desc, &p);
+  if (st != SSD_OK) return st;
+  if (!states || !dA_cumsum) return SSD_ERR_NULL_POINTER;
+  if (!ssd::aligned(states, 16) || !ssd::aligned(dA_cumsum, 4) || !ssd::aligned(init_state, 16) ||
+      !ssd::aligned(final_state, 16))
+    return SSD_ERR_ALIGNMENT;
+  const size_t sb = size_t(p.batch * p.H * p.P * p.N) * sizeof(float);
+  const ssd::Range rf = ssd::range_of(final_state, sb), ri = ssd::range_of(init_state, sb);
+  if (ssd::overlap(rf, ri) && rf.lo != ri.lo) return SSD_ERR_ALIAS;
+  return ssd::from_hip(ssd::launch_state_passing(p, states, dA_cumsum, init_state, final_state,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+ssd_status_t ssd_chunk_scan(const ssd_desc_t* desc, const void* x, const void* B, const void* C,
+                            const float* D, const float* dA_cumsum, const float* dt_chunked,
+                            const void* states, void* y, void* stream) {
+  Plan p;
+  ssd_status_t st = ssd::make_plan(desc, &p);
+  if (st != SSD_OK) return st;
+  if (!x || !B || !C || !dA_cumsum || !dt_chunked || !states || !y) return SSD_ERR_NULL_POINTER;
+  if (!ssd::aligned(x, 16) || !ssd::aligned(B, 16) || !ssd::aligned(C, 16) || !ssd::aligned(y, 16) ||
+      !ssd::aligned(D, 4) || !ssd::aligned(dA_cumsum, 16) || !ssd::aligned(dt_chunked, 16) ||
+      !ssd::aligned(states, 16))
+    return SSD_ERR_ALIGNMENT;
+  const size_t xy_bytes = size_t(p.batch * p.L * p.H * p.P) * p.io_bytes();
+  if (ssd::overlap(ssd::range_of(y, xy_bytes), ssd::range_of(x, xy_bytes))) return SSD_ERR_ALIAS;
+  return ssd::from_hip(ssd::run_chunk_scan(p, x, B, C, D, dA_cumsum, dt_chunked, states, y,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

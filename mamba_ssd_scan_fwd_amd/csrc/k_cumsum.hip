@@ -1,0 +1,98 @@
+// Step 1: per-chunk inclusive cumulative sum of dt * A.
+//
+// The blocked algorithm processes the sequence in chunks ("Mamba-2 vs
+// Transformers: SSMs, structured state space duality", section "Mamba-2 and
+// the SSD paper: what changed in practice"); inside chunk c the decay between
+// positions j <= i is exp(l_i - l_j) with l the inclusive sum of dt*A from the
+// chunk start. This kernel produces l (dA_cumsum) and dt regrouped per chunk
+// (dt_chunked), both [batch, H, nc, Q] fp32 with the positions of a chunk
+// contiguous, so the contraction kernels read one contiguous run per
+// (b, h, c). Positions past the sequence end get dt = 0, so l stays flat.
+//
+// Mapping: one workgroup per (chunk, batch, block of HB heads). The dt tile
+// [Q][HB] is read with the head index fastest (coalesced along dt's innermost
+// axis) into LDS; then one wavefront per head scans the Q positions: each lane
+// owns Q/64 consecutive positions, scans them serially, and the lane totals
+// are combined with a log-step wavefront scan (__shfl_up).
+#include "ssd_internal.h"
+
+namespace ssd {
+namespace {
+
+constexpr int kHB = 16;       // heads per workgroup
+constexpr int kThreads = 256; // 4 wavefronts
+
+template <int Q>
+__global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(
+    const float* __restrict__ dt, const float* __restrict__ A,
+    float* __restrict__ dA_cs, float* __restrict__ dtc,
+    int64_t L, int H, int64_t nc) {
+  constexpr int QPL = Q / 64;  // positions per lane
+  __shared__ float tile[Q][kHB + 1];
+  const int64_t c = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  const int h0 = blockIdx.z * kHB;
+  const int hb = min(kHB, H - h0);
+  const int tid = threadIdx.x;
+
+  for (int idx = tid; idx < Q * kHB; idx += kThreads) {
+    const int i = idx / kHB, hh = idx % kHB;
+    const int64_t t = c * Q + i;
+    float v = 0.f;
+    if (hh < hb && t < L) v = dt[(b * L + t) * H + h0 + hh];
+    tile[i][hh] = v;
+  }
+  __syncthreads();
+
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int hh = wave; hh < hb; hh += kThreads / 64) {
+    const int h = h0 + hh;
+    const float a = A[h];
+    float d[QPL], s[QPL];
+    float run = 0.f;
+#pragma unroll
+    for (int k = 0; k < QPL; ++k) {
+      d[k] = tile[lane * QPL + k][hh];
+      run += d[k] * a;
+      s[k] = run;
+    }
+    // inclusive wavefront scan of the lane totals
+    float incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    const float excl = incl - run;
+    const int64_t base = (((b * H + h) * nc) + c) * Q + lane * QPL;
+#pragma unroll
+    for (int k = 0; k < QPL; ++k) {
+      dA_cs[base + k] = s[k] + excl;
+      dtc[base + k] = d[k];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_cumsum(const Plan& p, const float* dt, const float* A,
+                               float* dA_cs, float* dtc, hipStream_t s) {
+  dim3 grid((unsigned)p.nc, (unsigned)p.batch, (unsigned)((p.H + kHB - 1) / kHB));
+  switch (p.Q) {
+    case 64:
+      chunk_cumsum_kernel<64><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc);
+      break;
+    case 128:
+      chunk_cumsum_kernel<128><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc);
+      break;
+    case 256:
+      chunk_cumsum_kernel<256><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -1,0 +1,44 @@
+// Internal declarations shared by the host planner (api.cpp) and the kernel
+// translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <cstdint>
+
+namespace ssd {
+
+enum IoType : int { kF32 = 0, kBF16 = 1 };
+
+// A validated problem plus the chosen chunk length.
+struct Plan {
+  int64_t batch, L, H, P, N, G;
+  int io;       // IoType of x, B, C, y and of the chunk states
+  int Q;        // chunk length
+  int64_t nc;   // number of chunks = ceil(L / Q)
+  int64_t heads_per_group() const { return H / G; }
+  size_t io_bytes() const { return io == kBF16 ? 2 : 4; }
+};
+
+// Step launchers. Each returns the hipGetLastError() after its launches.
+hipError_t launch_chunk_cumsum(const Plan& p, const float* dt, const float* A,
+                               float* dA_cs, float* dtc, hipStream_t s);
+hipError_t launch_chunk_state(const Plan& p, const void* x, const void* B,
+                              const float* dA_cs, const float* dtc, void* states,
+                              hipStream_t s);
+hipError_t launch_state_passing(const Plan& p, void* states, const float* dA_cs,
+                                const float* h0, float* hT, hipStream_t s);
+hipError_t launch_chunk_scan(const Plan& p, const void* x, const void* B, const void* C,
+                             const float* D, const float* dA_cs, const float* dtc,
+                             const void* states, void* y, hipStream_t s);
+
+// Element conversion helpers used by every kernel file.
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(__hip_bfloat16 v) { return __bfloat162float(v); }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ __hip_bfloat16 from_f32<__hip_bfloat16>(float v) {
+  return __float2bfloat16(v);  // round to nearest even
+}
+
+}  // namespace ssd

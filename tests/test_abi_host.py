@@ -1,0 +1,210 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and validates arguments before touching the GPU.
+
+No call here reaches a kernel: every ssd_forward / step call is given an
+argument the host validation rejects (fake, never dereferenced device
+addresses), so these tests run without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_ssd_scan_fwd_amd as ssd
+from mamba_ssd_scan_fwd_amd.binding import SSDDesc, make_desc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+OK, NULLP, SHAPE, UNSUP, ALIGN, WS, ALIAS, HIP = range(8)
+
+
+def lib():
+    if not os.path.exists(ssd.lib_path()):
+        pytest.skip("libssd.so not built (python -m mamba_ssd_scan_fwd_amd.build)")
+    return ssd.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SSD_API\s+[\w\s\*]+?\b(ssd_\w+)\s*\(", text)))
+
+
+def test_header_declares_what_the_binding_binds():
+    assert declared_symbols() == sorted(ssd.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    # and nothing of the internal C++ namespace leaks out
+    out = os.popen(f"nm -D --defined-only {ssd.lib_path()}").read()
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert {s for s in exported if s.startswith("ssd")} == set(declared_symbols())
+    assert not any("ssd" in s and s.startswith("_Z") for s in exported)
+
+
+def test_status_strings():
+    lib()
+    for code in range(8):
+        assert ssd.status_string(code).startswith(["SSD_OK", "SSD_ERR"][code > 0])
+    assert "unknown" in ssd.status_string(99)
+
+
+def desc(**kw):
+    d = dict(batch=8, seqlen=2048, nheads=64, headdim=64, dstate=128, ngroups=1, io_dtype="bf16",
+             chunk_size=0)
+    d.update(kw)
+    return make_desc(**d)
+
+
+def status_of(fn, *args):
+    try:
+        fn(*args)
+    except ssd.SSDError as e:
+        return e.status
+    return OK
+
+
+@pytest.mark.parametrize("Q", [0, 64, 128, 256])
+def test_effective_chunk_and_workspace_layout(Q):
+    lib()
+    d = desc(chunk_size=Q)
+    q = ssd.effective_chunk_size(d)
+    assert q == (256 if Q == 0 else Q)
+    nc = -(-2048 // q)
+
+    def up(v):
+        return -(-v // 256) * 256
+
+    cs = 8 * 64 * nc * q * 4
+    st = 8 * 64 * nc * 64 * 128 * 2
+    assert ssd.workspace_bytes(d) == up(up(up(cs) + cs) + st)
+    # fp32 states for the fp32 io dtype
+    d32 = desc(chunk_size=Q, io_dtype="fp32", seqlen=1000)
+    nc = -(-1000 // q)
+    cs = 8 * 64 * nc * q * 4
+    assert ssd.workspace_bytes(d32) == up(up(up(cs) + cs) + 8 * 64 * nc * 64 * 128 * 4)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(batch=0), SHAPE),
+        (dict(seqlen=-1), SHAPE),
+        (dict(nheads=6, ngroups=4), SHAPE),
+        (dict(ngroups=0), SHAPE),
+        (dict(batch=70000), SHAPE),
+        (dict(headdim=48), UNSUP),
+        (dict(headdim=256), UNSUP),
+        (dict(headdim=8), UNSUP),
+        (dict(dstate=512), UNSUP),
+        (dict(dstate=96), UNSUP),
+        (dict(chunk_size=100), UNSUP),
+        (dict(chunk_size=512), UNSUP),
+        (dict(io_dtype=7), UNSUP),
+    ],
+)
+def test_bad_descriptors_are_rejected(kw, code):
+    lib()
+    assert status_of(ssd.workspace_bytes, desc(**kw)) == code
+    assert status_of(ssd.effective_chunk_size, desc(**kw)) == code
+
+
+def test_null_descriptor():
+    L = lib()
+    n = ctypes.c_size_t(0)
+    assert L.ssd_workspace_bytes(None, ctypes.byref(n)) == NULLP
+    assert L.ssd_forward(None, *([None] * 10), 0, None) == NULLP
+
+
+BASE = 0x7F0000000000  # fake device addresses: never dereferenced
+
+
+def fwd_args(d, **over):
+    """Non-overlapping, aligned fake pointers for every ssd_forward argument."""
+    io = 2 if d.io_dtype == 1 else 4
+    xy = d.batch * d.seqlen * d.nheads * d.headdim * io
+    bc = d.batch * d.seqlen * d.ngroups * d.dstate * io
+    dt = d.batch * d.seqlen * d.nheads * 4
+    st = d.batch * d.nheads * d.headdim * d.dstate * 4
+    sizes = dict(x=xy, dt=dt, A=4 * d.nheads, B=bc, C=bc, D=4 * d.nheads, h0=st, y=xy, hT=st,
+                 ws=ssd.workspace_bytes(d))
+    ptrs, cur = {}, BASE
+    for k, s in sizes.items():
+        ptrs[k] = cur
+        cur += (s + 4095) // 4096 * 4096 + 4096
+    ptrs.update(over)
+    return ptrs, sizes
+
+
+def call_fwd(d, p, ws_bytes=None):
+    L = lib()
+    v = lambda k: None if p[k] is None else ctypes.c_void_p(p[k])  # noqa: E731
+    wsb = ssd.workspace_bytes(d) if ws_bytes is None else ws_bytes
+    return L.ssd_forward(ctypes.byref(d), v("x"), v("dt"), v("A"), v("B"), v("C"), v("D"), v("h0"),
+                         v("y"), v("hT"), v("ws"), ctypes.c_size_t(wsb), None)
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "y"])
+def test_required_pointers(name):
+    d = desc()
+    p, _ = fwd_args(d, **{name: None})
+    assert call_fwd(d, p) == NULLP
+
+
+@pytest.mark.parametrize("name,off", [("x", 2), ("B", 8), ("C", 4), ("y", 2), ("h0", 4), ("hT", 8),
+                                      ("dt", 2), ("A", 1), ("D", 2), ("ws", 16)])
+def test_misaligned_pointers(name, off):
+    d = desc()
+    p, _ = fwd_args(d)
+    p[name] += off
+    assert call_fwd(d, p) == ALIGN
+
+
+def test_workspace_too_small():
+    d = desc()
+    p, _ = fwd_args(d)
+    assert call_fwd(d, p, ws_bytes=ssd.workspace_bytes(d) - 256) == WS
+
+
+@pytest.mark.parametrize("case", ["y_is_x", "y_overlaps_B", "ws_overlaps_C", "hT_partial_h0", "hT_is_x",
+                                  "y_overlaps_hT"])
+def test_aliasing_is_rejected(case):
+    d = desc()
+    p, s = fwd_args(d)
+    if case == "y_is_x":
+        p["y"] = p["x"]
+    elif case == "y_overlaps_B":
+        p["y"] = p["B"] + s["B"] - 1024
+    elif case == "ws_overlaps_C":
+        p["ws"] = p["C"] + 256
+    elif case == "hT_partial_h0":
+        p["hT"] = p["h0"] + 1024
+    elif case == "hT_is_x":
+        p["hT"] = p["x"]
+    elif case == "y_overlaps_hT":
+        p["hT"] = p["y"] + 4096
+    assert call_fwd(d, p) == ALIAS
+
+
+def test_step_entry_points_validate_too():
+    L = lib()
+    d = desc(headdim=48)
+    assert L.ssd_chunk_cumsum(ctypes.byref(d), *([ctypes.c_void_p(BASE)] * 4), None) == UNSUP
+    d = desc()
+    assert L.ssd_chunk_cumsum(ctypes.byref(d), None, *([ctypes.c_void_p(BASE)] * 3), None) == NULLP
+    assert L.ssd_chunk_state(ctypes.byref(d), *([ctypes.c_void_p(BASE + 2)] * 5), None) == ALIGN
+    assert L.ssd_state_passing(ctypes.byref(d), None, ctypes.c_void_p(BASE), None, None, None) == NULLP
+    p0 = ctypes.c_void_p(BASE)
+    assert L.ssd_state_passing(ctypes.byref(d), p0, p0, ctypes.c_void_p(BASE + 4096),
+                               ctypes.c_void_p(BASE + 8192), None) == ALIAS
+    assert L.ssd_chunk_scan(ctypes.byref(d), p0, p0, p0, None, p0, p0, p0, p0, None) == ALIAS
+
+
+def test_desc_struct_layout():
+    # int64 x 6 followed by two int32: 56 bytes, no padding surprises
+    assert ctypes.sizeof(SSDDesc) == 56

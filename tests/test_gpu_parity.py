@@ -1,0 +1,345 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Every case draws seeded synthetic inputs (ssd_inputs), runs the library on
+the GPU, and compares element by element with the oracle on the same inputs:
+  * the small fp32 workload in full;
+  * each bf16 workload at reduced batch/length (several chunks and a ragged
+    tail) and at its full size in the launch configuration the benchmark
+    times, both on sampled (batch, head) pairs over the whole sequence;
+  * edge shapes (L = 1, L < Q, L = Q +- 1, every P, N, group layout, chunk
+    length, both io dtypes) in full;
+  * API options (no D, no/zero initial state, no final state, in-place state,
+    library-allocated workspace, a non-default stream);
+  * hygiene: every output element written, guard bands intact, bitwise
+    run-to-run determinism;
+  * each step of the chunked path on its own against the oracle's definition
+    of that step's output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import chunk_cumsum as o_cumsum
+from oracle import chunk_entry_states as o_entry
+from oracle import chunk_local_states as o_local
+from oracle import ssd_recurrent
+from ssd_inputs import CONFIGS, make_inputs
+from ssd_testutil import TOL, check_rel, note, np64, oracle_sampled
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def ssd():
+    import mamba_ssd_scan_fwd_amd as m
+    m.load_library()  # raises if the HIP library is missing: no fallback
+    return m
+
+
+def to_dev(inp):
+    return {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+
+
+def run(inp, **kw):
+    d = to_dev(inp)
+    y, hT = ssd().forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], **kw)
+    torch.cuda.synchronize()
+    return y.cpu(), (hT.cpu() if hT is not None else None)
+
+
+def full_check(inp, tol, tag, **kw):
+    note(f"[gpu] {tag}: x{tuple(inp['x'].shape)} B{tuple(inp['B'].shape)} {inp['x'].dtype} {kw}")
+    y, hT = run(inp, **kw)
+    yr, hr = ssd_recurrent(*(np64(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "init_state")))
+    check_rel(np64(y), yr, tol, f"{tag} y")
+    if hT is not None:
+        check_rel(np64(hT), hr, tol, f"{tag} final_state")
+    return y, hT
+
+
+def sampled_check(inp, pairs, tol, tag, **kw):
+    note(f"[gpu] {tag}: x{tuple(inp['x'].shape)} B{tuple(inp['B'].shape)} {inp['x'].dtype} pairs={pairs}")
+    y, hT = run(inp, **kw)
+    ref = oracle_sampled(inp, pairs)
+    ey = check_rel(np.stack([np64(y[b, :, h]) for b, h in pairs]),
+                   np.stack([ref[p][0] for p in pairs]), tol, f"{tag} y (sampled)")
+    eh = check_rel(np.stack([np64(hT[b, h]) for b, h in pairs]),
+                   np.stack([ref[p][1] for p in pairs]), tol, f"{tag} final_state (sampled)")
+    assert torch.isfinite(y.float()).all() and torch.isfinite(hT).all()
+    return ey, eh
+
+
+def pairs_for(cfg, n=3):
+    b, H = cfg.batch, cfg.nheads
+    cand = [(0, 0), (b - 1, H - 1), (b // 2, H // 2 + 1 if H > 2 else 0), (0, H // 3)]
+    out = []
+    for p in cand:
+        if p not in out:
+            out.append(p)
+    return out[:n]
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+# --------------------------------------------------------------------------
+
+def test_tiny_fp32_workload_in_full():
+    cfg = CONFIGS[0]
+    full_check(make_inputs(cfg, seed=0), TOL["fp32"], cfg.name)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_workloads_reduced_length(idx):
+    cfg = CONFIGS[idx]
+    small = cfg.with_(batch=min(cfg.batch, 2), seqlen=2 * 256 + 77)
+    inp = make_inputs(small, seed=100 + idx)
+    sampled_check(inp, pairs_for(small, 4), TOL[cfg.io_dtype], f"{cfg.name} reduced")
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_workloads_full_size(idx):
+    cfg = CONFIGS[idx]
+    inp = make_inputs(cfg, seed=idx)
+    sampled_check(inp, pairs_for(cfg, 3), TOL[cfg.io_dtype], f"{cfg.name} full size")
+
+
+# --------------------------------------------------------------------------
+# edge shapes, every P / N / group layout / chunk length, both dtypes
+# --------------------------------------------------------------------------
+
+BASE = CONFIGS[1].with_(batch=2, seqlen=256, nheads=4, headdim=64, dstate=128, ngroups=1)
+
+EDGE = [
+    # (L, P, N, H, G, io, Q, init)
+    (1, 64, 128, 4, 1, "bf16", 0, True),
+    (15, 64, 128, 4, 1, "bf16", 0, False),
+    (255, 64, 128, 4, 1, "bf16", 256, True),
+    (256, 64, 128, 4, 1, "bf16", 256, False),
+    (257, 64, 128, 4, 1, "bf16", 256, True),
+    (773, 64, 128, 4, 2, "bf16", 256, True),
+    (200, 64, 128, 4, 1, "bf16", 64, True),
+    (333, 64, 128, 4, 4, "bf16", 128, False),
+    (300, 16, 128, 4, 1, "bf16", 0, True),
+    (300, 32, 64, 4, 2, "bf16", 0, True),
+    (300, 128, 128, 2, 1, "bf16", 0, True),
+    (300, 64, 16, 4, 1, "bf16", 0, True),
+    (300, 64, 32, 4, 1, "bf16", 0, True),
+    (300, 64, 256, 4, 2, "bf16", 0, True),
+    (300, 128, 256, 2, 1, "bf16", 128, True),
+    (1, 16, 16, 4, 1, "fp32", 0, True),
+    (300, 16, 16, 4, 1, "fp32", 0, True),
+    (300, 64, 128, 4, 2, "fp32", 0, True),
+    (257, 128, 256, 2, 1, "fp32", 64, True),
+    (130, 32, 64, 4, 4, "fp32", 128, False),
+]
+
+
+@pytest.mark.parametrize("L,P,N,H,G,io,Q,init", EDGE)
+def test_edge_shapes(L, P, N, H, G, io, Q, init):
+    cfg = BASE.with_(seqlen=L, headdim=P, dstate=N, nheads=H, ngroups=G, io_dtype=io, init_state=init)
+    inp = make_inputs(cfg, seed=L + P + N + H + G + Q)
+    full_check(inp, TOL[io], f"edge L={L} P={P} N={N} H={H} G={G} {io} Q={Q}", chunk_size=Q)
+
+
+@pytest.mark.parametrize("Q", [64, 128, 256])
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+def test_every_chunk_length_gives_the_same_result(Q, io):
+    cfg = BASE.with_(seqlen=700, io_dtype=io, init_state=True)
+    inp = make_inputs(cfg, seed=7)
+    full_check(inp, TOL[io], f"Q={Q} {io}", chunk_size=Q)
+
+
+def test_memoryless_limit_on_gpu():
+    # A -> -inf: every chunk boundary and decay factor underflows to 0; the
+    # result must be the memoryless closed form (checked by the oracle pins).
+    cfg = BASE.with_(seqlen=300, init_state=True)
+    inp = make_inputs(cfg, seed=11)
+    inp["A"] = torch.full_like(inp["A"], -1e5)
+    full_check(inp, TOL["bf16"], "A=-1e5")
+
+
+def test_zero_dt_carries_state_on_gpu():
+    cfg = BASE.with_(seqlen=300, init_state=True)
+    inp = make_inputs(cfg, seed=12)
+    inp["dt"] = torch.zeros_like(inp["dt"])
+    y, hT = full_check(inp, TOL["bf16"], "dt=0")
+    assert torch.equal(hT, inp["init_state"])  # exp(0) = 1 and nothing added
+
+
+# --------------------------------------------------------------------------
+# API options
+# --------------------------------------------------------------------------
+
+def test_no_D_and_no_final_state():
+    cfg = BASE.with_(seqlen=300, init_state=True)
+    inp = make_inputs(cfg, seed=13)
+    inp["D"] = None
+    y, hT = full_check(inp, TOL["bf16"], "D=None, final=None", return_final_state=False)
+    assert hT is None
+
+
+def test_null_initial_state_equals_zero_initial_state_bitwise():
+    cfg = BASE.with_(seqlen=300, init_state=False)
+    inp = make_inputs(cfg, seed=14)
+    y0, h0 = run(inp)
+    inp2 = dict(inp)
+    inp2["init_state"] = torch.zeros((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate))
+    y1, h1 = run(inp2)
+    assert torch.equal(y0, y1) and torch.equal(h0, h1)
+
+
+def test_in_place_state_update():
+    cfg = BASE.with_(seqlen=300, init_state=True)
+    inp = make_inputs(cfg, seed=15)
+    d = to_dev(inp)
+    ref_y, ref_h = run(inp)
+    state = d["init_state"].clone()
+    y, hT = ssd().forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], state, final_state=state)
+    torch.cuda.synchronize()
+    assert hT.data_ptr() == state.data_ptr()
+    assert torch.equal(y.cpu(), ref_y) and torch.equal(state.cpu(), ref_h)
+
+
+def test_library_allocated_workspace_and_side_stream():
+    cfg = BASE.with_(seqlen=400, init_state=True)
+    inp = make_inputs(cfg, seed=16)
+    ref_y, ref_h = run(inp)
+    d = to_dev(inp)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        y, hT = ssd().forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"],
+                              library_workspace=True)
+    s.synchronize()
+    assert torch.equal(y.cpu(), ref_y) and torch.equal(hT.cpu(), ref_h)
+
+
+def test_state_chaining_across_calls():
+    cfg = BASE.with_(seqlen=700, init_state=True)
+    inp = make_inputs(cfg, seed=17)
+    y, hT = run(inp)
+    cut = 300
+
+    def part(sl, h0):
+        p = dict(inp)
+        for k in ("x", "dt", "B", "C"):
+            p[k] = inp[k][:, sl].contiguous()
+        p["init_state"] = h0
+        return run(p)
+
+    y1, h1 = part(slice(0, cut), inp["init_state"])
+    y2, h2 = part(slice(cut, None), h1)
+    yr, hr = ssd_recurrent(*(np64(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "init_state")))
+    check_rel(np64(torch.cat([y1, y2], 1)), yr, TOL["bf16"], "chained y")
+    check_rel(np64(h2), hr, TOL["bf16"], "chained final_state")
+
+
+# --------------------------------------------------------------------------
+# hygiene
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+def test_every_output_written_and_guard_bands_intact(io):
+    cfg = BASE.with_(seqlen=517, io_dtype=io, init_state=True, ngroups=2)
+    inp = make_inputs(cfg, seed=18)
+    d = to_dev(inp)
+    ny, nh, pad = d["x"].numel(), cfg.batch * cfg.nheads * cfg.headdim * cfg.dstate, 4096
+    ybuf = torch.full((ny + 2 * pad,), float("nan"), dtype=d["x"].dtype, device=DEV)
+    hbuf = torch.full((nh + 2 * pad,), float("nan"), dtype=torch.float32, device=DEV)
+    y = ybuf[pad:pad + ny].view_as(d["x"])
+    hT = hbuf[pad:pad + nh].view(cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate)
+    ws_n = ssd().workspace_bytes(ssd().make_desc(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim,
+                                                 cfg.dstate, cfg.ngroups, io))
+    ws = torch.full((ws_n // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    ssd().forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], y=y, final_state=hT,
+                  workspace=ws.view(torch.uint8))
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all() and torch.isfinite(hT).all()
+    assert torch.isnan(ybuf[:pad].float()).all() and torch.isnan(ybuf[pad + ny:].float()).all()
+    assert torch.isnan(hbuf[:pad]).all() and torch.isnan(hbuf[pad + nh:]).all()
+
+
+def test_bitwise_deterministic():
+    cfg = CONFIGS[1].with_(batch=2, seqlen=1100)
+    inp = make_inputs(cfg, seed=19)
+    y0, h0 = run(inp)
+    y1, h1 = run(inp)
+    assert torch.equal(y0, y1) and torch.equal(h0, h1)
+
+
+# --------------------------------------------------------------------------
+# each step on its own against the oracle's definition of its output
+# --------------------------------------------------------------------------
+
+STEP_CASES = [("bf16", 256, 600), ("bf16", 64, 300), ("fp32", 128, 333)]
+
+
+@pytest.mark.parametrize("io,Q,L", STEP_CASES)
+def test_step_chunk_cumsum(io, Q, L):
+    cfg = BASE.with_(seqlen=L, io_dtype=io, ngroups=2)
+    inp = make_inputs(cfg, seed=20)
+    d = to_dev(inp)
+    note(f"[gpu] step1 cumsum {io} Q={Q} L={L}")
+    cs, dtc = ssd().chunk_cumsum(d["dt"], d["A"], headdim=cfg.headdim, dstate=cfg.dstate, ngroups=2,
+                                 io_dtype=io, chunk_size=Q)
+    torch.cuda.synchronize()
+    ref = o_cumsum(np64(inp["dt"]), np64(inp["A"]), Q)
+    # fp32 running sum of at most Q terms of magnitude <= 1.6
+    assert np.max(np.abs(np64(cs) - ref)) <= 1e-5 * max(1.0, np.max(np.abs(ref)))
+    dref = np.zeros(ref.shape)
+    dtn = np64(inp["dt"])
+    for c in range(ref.shape[2]):
+        n = min(Q, L - c * Q)
+        dref[:, :, c, :n] = dtn[:, c * Q:c * Q + n, :].transpose(0, 2, 1)
+    assert np.array_equal(np64(dtc), dref)
+
+
+@pytest.mark.parametrize("io,Q,L", STEP_CASES)
+def test_step_chunk_state(io, Q, L):
+    cfg = BASE.with_(seqlen=L, io_dtype=io, ngroups=2)
+    inp = make_inputs(cfg, seed=21)
+    d = to_dev(inp)
+    note(f"[gpu] step2 chunk_state {io} Q={Q} L={L}")
+    cs, dtc = ssd().chunk_cumsum(d["dt"], d["A"], headdim=cfg.headdim, dstate=cfg.dstate, ngroups=2,
+                                 io_dtype=io, chunk_size=Q)
+    st = ssd().chunk_state(d["x"], d["B"], cs, dtc, chunk_size=Q)
+    torch.cuda.synchronize()
+    ref = o_local(np64(inp["x"]), np64(inp["dt"]), np64(inp["A"]), np64(inp["B"]), Q)
+    check_rel(np64(st), ref, TOL[io], f"chunk states {io} Q={Q}")
+
+
+@pytest.mark.parametrize("io,Q,L", STEP_CASES)
+def test_step_state_passing(io, Q, L):
+    cfg = BASE.with_(seqlen=L, io_dtype=io, ngroups=2, init_state=True)
+    inp = make_inputs(cfg, seed=22)
+    d = to_dev(inp)
+    args = [np64(inp[k]) for k in ("x", "dt", "A", "B")]
+    local = o_local(*args, Q)
+    entry, final = o_entry(*args, Q, np64(inp["init_state"]))
+    cs = torch.tensor(o_cumsum(args[1], args[2], Q), dtype=torch.float32, device=DEV)
+    st = torch.tensor(local, dtype=torch.float32).to(inp["x"].dtype).to(DEV)
+    note(f"[gpu] step3 state_passing {io} Q={Q} L={L}")
+    st, hT = ssd().state_passing(st, cs, d["init_state"], seqlen=L, ngroups=2, chunk_size=Q)
+    torch.cuda.synchronize()
+    check_rel(np64(st), entry, TOL[io], f"entry states {io} Q={Q}")
+    check_rel(np64(hT), final, TOL[io], f"final state {io} Q={Q}")
+
+
+@pytest.mark.parametrize("io,Q,L", STEP_CASES)
+def test_step_chunk_scan(io, Q, L):
+    cfg = BASE.with_(seqlen=L, io_dtype=io, ngroups=2, init_state=True)
+    inp = make_inputs(cfg, seed=23)
+    d = to_dev(inp)
+    args = [np64(inp[k]) for k in ("x", "dt", "A", "B")]
+    entry, _ = o_entry(*args, Q, np64(inp["init_state"]))
+    cs = torch.tensor(o_cumsum(args[1], args[2], Q), dtype=torch.float32, device=DEV)
+    _, dtc = ssd().chunk_cumsum(d["dt"], d["A"], headdim=cfg.headdim, dstate=cfg.dstate, ngroups=2,
+                                io_dtype=io, chunk_size=Q)
+    st = torch.tensor(entry, dtype=torch.float32).to(inp["x"].dtype).to(DEV)
+    note(f"[gpu] step4+5 chunk_scan {io} Q={Q} L={L}")
+    y = ssd().chunk_scan(d["x"], d["B"], d["C"], d["D"], cs, dtc, st, chunk_size=Q)
+    torch.cuda.synchronize()
+    yr, _ = ssd_recurrent(*(np64(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "init_state")))
+    check_rel(np64(y), yr, TOL[io], f"chunk scan y {io} Q={Q}")
