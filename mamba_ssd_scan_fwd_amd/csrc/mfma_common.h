@@ -1,0 +1,67 @@
+// gfx950 matrix-core helpers shared by the bf16 contraction kernels.
+//
+// Operand layout of v_mfma_f32_16x16x32_bf16 (D[16x16] += A[16x32] B[32x16]),
+// with lane l = 16*g + r (g = l / 16 in 0..3, r = l % 16):
+//   A: lane holds A[r][8g .. 8g+7]      (row r, eight consecutive k)
+//   B: lane holds B[8g .. 8g+7][r]      (column r, eight consecutive k)
+//   D: lane holds D[4g + i][r], i = 0..3 (four consecutive rows of column r)
+// Only the pairing of k between A and B matters for the product, so any
+// permutation of the 32 k indices may be used as long as A and B agree.
+#pragma once
+
+#include "ssd_internal.h"
+
+namespace ssd {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair, round to nearest even (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const bf16x8_t& a, const bf16x8_t& b,
+                                                 const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Transpose an 8x8 block of bf16 held as eight rows of 16 bytes: out[s] holds
+// column s (rows 0..7, row 0 in the low half of word 0).
+__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const uint32_t sel = (s & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4& r0 = in[2 * q];
+      const uint4& r1 = in[2 * q + 1];
+      const int m = s >> 1;
+      const uint32_t a = m == 0 ? r0.x : m == 1 ? r0.y : m == 2 ? r0.z : r0.w;
+      const uint32_t b = m == 0 ? r1.x : m == 1 ? r1.y : m == 2 ? r1.z : r1.w;
+      w[q] = __builtin_amdgcn_perm(b, a, sel);
+    }
+    out[s] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Element e (0..7) of a row of eight bf16 held in a uint4, as fp32.
+__device__ __forceinline__ float bf16_at(const uint4& v, int e) {
+  const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+  return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+}  // namespace ssd
