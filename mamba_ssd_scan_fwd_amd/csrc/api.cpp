@@ -43,10 +43,9 @@ constexpr int64_t kMaxHeads = 65535;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 int default_chunk(const ssd_desc_t& d) {
-  // 256 halves the chunk-state traffic of 128 and keeps the intra-chunk
-  // tiles within the register budget up to N = 256.
-  (void)d;
-  return 256;
+  // 256 halves the chunk-state traffic of 128; with headdim 128 or state
+  // 256 the intra-chunk kernel's register tiles only fit at 128.
+  return (d.headdim <= 64 && d.dstate <= 128) ? 256 : 128;
 }
 
 ssd_status_t make_plan(const ssd_desc_t* d, Plan* p) {

@@ -9,29 +9,35 @@
 //         + exp(l_i) Hin_c C_i                                   (chunk output)
 //         + D_h x_i
 //
-// Mapping (per workgroup: one (b, c) and HB heads of one B/C group):
-//  * Products are computed transposed, Y^T[p][i], so the score tile can stay
-//    in registers: G^T[j][i] = B_j . C_i is produced by the matrix cores with
-//    each lane holding one column i and four consecutive rows j, which is
-//    exactly the layout of the B operand of the next product Y^T += X^T W^T
-//    (two 16-row tiles of G^T make one 32-deep operand; the x fragments are
-//    read from LDS in the same j order).
-//  * G^T (the C B^T of the pages' dual form) depends only on the group, so it
-//    is computed once per workgroup and reused by its HB heads; only the
-//    decay mask is per head.
-//  * The chunk's rows are cut into R = Q/16 row groups of 16. Wavefront w
-//    owns row groups r1 = 2w+1 and r2 = R-2-2w: an odd/even pair whose causal
-//    tile counts add up to R+1, so every wavefront does the same work, and
-//    both counts stay even-aligned so tiles pair into 32-deep operands.
+// Mapping (one workgroup of four wavefronts, one per SIMD, per (b, c) and HB
+// heads of one B/C group):
+//  * Products are computed transposed, Y^T[p][i], so the score tile never
+//    leaves registers: G^T[j][i] = B_j . C_i comes out of the matrix cores
+//    with each lane holding one column i and four consecutive rows j, which
+//    is the layout of the B operand of the next product Y^T += X^T W^T (two
+//    16-row tiles of G^T form one 32-deep operand; x fragments are read from
+//    LDS in the same j order).
+//  * G^T (the C B^T of the pages' dual form) depends only on the group: it is
+//    computed once per workgroup, from B staged through LDS, and reused by
+//    the HB heads; only the decay mask is per head. It is held as packed bf16
+//    (rounded once more after the decay is applied).
+//  * The R = Q/16 row groups of 16 rows are dealt out zigzag: with Q = 256,
+//    wavefront w owns row groups w, 7-w, 8+w, 15-w, whose causal tile counts
+//    add up to the same 34 for every wavefront. One x fragment read from LDS
+//    feeds all of a wavefront's row groups.
 //  * The decay exp(l_i - l_j) is never formed from exp(l_i) * exp(-l_j)
 //    (that overflows); off-diagonal tiles use a factorisation through the
 //    tile boundaries, exp(l_i - l_r0) * exp(l_r0 - l_te) * exp(l_te - l_j),
 //    with r0 the first row of the row group and te the last row of the
 //    column tile, every factor <= 1; diagonal tiles are masked (j > i -> 0)
 //    before the exponential of l_i - l_j is taken.
-//  * x of each head is staged in LDS transposed ([p][j]); Hin ([p][n]) in
-//    its natural layout; both are prefetched into registers for the next
-//    head while the current head's products run.
+//  * Per head, x (transposed) and Hin are staged in LDS in fragment-major
+//    order: each lane's 16-byte operand fragment is contiguous, so a matrix
+//    core operand is one conflict-free 16-byte LDS read; a swizzle of the
+//    lane slot inside each 1 KB fragment block spreads the staging writes
+//    over the banks. x, Hin, l and dt of the next head are loaded into
+//    registers while the current head's products run.
+//  * The skip term D_h x_i is added in fp32 in the epilogue.
 #include "mfma_common.h"
 
 namespace ssd {
@@ -39,40 +45,75 @@ namespace {
 
 template <int P, int N, int Q>
 struct ScanCfg {
-  static constexpr int R = Q / 16;          // row groups of 16
-  static constexpr int WAVES = R / 2;       // two row groups per wavefront
+  static constexpr int R = Q / 16;            // row groups of 16
+  static constexpr int NM = Q / 32;           // 32-deep steps over the chunk positions
+  static constexpr int WAVES = 4;
   static constexpr int THREADS = WAVES * 64;
-  static constexpr int NTP = P / 16;        // p tiles
-  static constexpr int NK = (N + 31) / 32;  // 32-deep steps over n
-  static constexpr int QP = Q + 8;          // LDS pitch of x^T rows (bf16)
-  static constexpr int NP = NK * 32 + 8;    // LDS pitch of Hin rows (bf16)
+  static constexpr int RG = R / WAVES;        // row groups per wavefront: 1, 2 or 4
+  static constexpr int NTP = P / 16;          // p tiles
+  static constexpr int NK = (N + 31) / 32;    // 32-deep steps over n
+  static constexpr int NPAIR = RG / 2;        // zigzag pairs of row groups
+  // off-diagonal G^T slots: pair m holds 16m + 7 tiles
+  static constexpr int NGT = RG == 1 ? R - 1 : 16 * (NPAIR * (NPAIR - 1) / 2) + 7 * NPAIR;
   static constexpr int XBLK = (Q / 4) * (P / 8);  // 4x8 blocks of the x tile
   static constexpr int XPT = (XBLK + THREADS - 1) / THREADS;
   static constexpr int HCH = P * N / 8;           // 16-byte chunks of Hin
   static constexpr int HPT = (HCH + THREADS - 1) / THREADS;
+  static constexpr int FPT = (Q + THREADS - 1) / THREADS;
+  static constexpr int NSL = (N + 127) / 128;     // n slices when staging B
+  static constexpr int NSW = N < 128 ? N : 128;   // width of one slice
+  static constexpr int BPITCH = NSW + 8;          // staged B row pitch (bf16)
+  // LDS carve-up (bytes)
+  static constexpr int X_BYTES = NTP * NM * 64 * 16;
+  static constexpr int H_BYTES = NTP * NK * 64 * 16;
+  static constexpr int XN_PITCH = P + 8;          // natural-layout x row pitch (bf16)
+  static constexpr int XN_BYTES = Q * XN_PITCH * 2;
+  static constexpr int C_BYTES = WAVES * RG * NK * 64 * 16;
+  static constexpr int F_BYTES = 3 * Q * 4;
+  static constexpr int BST_BYTES = Q * BPITCH * 2;
+  static constexpr int LIMIT = 160 * 1024;
+  static constexpr bool USE_XN = X_BYTES + H_BYTES + F_BYTES + XN_BYTES <= LIMIT;
+  static constexpr int BASE = X_BYTES + H_BYTES + F_BYTES + (USE_XN ? XN_BYTES : 0);
+  static constexpr int REST = BASE > BST_BYTES ? BASE : BST_BYTES;
+  static constexpr bool PARK_C = C_BYTES + REST <= LIMIT;
+  static constexpr int C_SZ = PARK_C ? C_BYTES : 0;
+  static constexpr int TOTAL = C_SZ + REST;
+  // offsets: [C frags][x frags][Hin frags][l, dt, col][x natural]; the B
+  // staging area aliases everything after the C fragments (it is used
+  // before any of those buffers)
+  static constexpr int OFF_C = 0;
+  static constexpr int OFF_X = C_SZ, OFF_H = OFF_X + X_BYTES, OFF_F = OFF_H + H_BYTES;
+  static constexpr int OFF_XN = OFF_F + F_BYTES;
+  static constexpr int OFF_B = C_SZ;
 };
 
-// workgroup size: two 16-row groups per wavefront
 template <int Q>
-constexpr int kScanThreads = Q / 32 * 64;
+constexpr int kScanThreads = 256;
+
+// Slot of lane (r16, g4) inside a 1 KB fragment block. Readers cover all 64
+// slots of a block, so any per-block permutation keeps their reads
+// conflict-free; these two spread the staging writes across the banks.
+__device__ __forceinline__ int xslot(int r16, int g4, int pt) { return 16 * g4 + ((r16 + g4 + 4 * pt) & 15); }
+__device__ __forceinline__ int hslot(int r16, int g4) { return 16 * g4 + ((r16 + 4 * g4) & 15); }
 
 template <int P, int N, int Q>
-__global__ __launch_bounds__(kScanThreads<Q>) void chunk_scan_mfma_kernel(
+__global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const uint16_t* __restrict__ Cm, const float* __restrict__ D,
     const float* __restrict__ dA_cs, const float* __restrict__ dtc,
     const uint16_t* __restrict__ states, uint16_t* __restrict__ y,
     int64_t L, int H, int G, int64_t nc, int HB) {
   using C = ScanCfg<P, N, Q>;
-  constexpr int R = C::R;
-  __shared__ __align__(16) uint16_t sX[P * C::QP];
-  __shared__ __align__(16) uint16_t sH[P * C::NP];
-  __shared__ __align__(16) float sL[Q];     // l_i
-  __shared__ __align__(16) float sDt[Q];    // dt_j
-  __shared__ __align__(16) float sEl[Q];    // exp(l_i)
-  __shared__ __align__(16) float sRow[Q];   // exp(l_i - l_{16*floor(i/16)})
-  __shared__ __align__(16) float sCol[Q];   // exp(l_{16*floor(j/16)+15} - l_j) * dt_j
-  __shared__ float sT[R * R];               // exp(l_{16r} - l_{16t+15}), t < r
+  constexpr int R = C::R, NM = C::NM, RG = C::RG, NTP = C::NTP, NK = C::NK;
+  __shared__ __align__(16) unsigned char lds[C::TOTAL];
+  uint4* sXf = reinterpret_cast<uint4*>(lds + C::OFF_X);   // x^T fragments [pt][m][slot]
+  uint4* sHf = reinterpret_cast<uint4*>(lds + C::OFF_H);   // Hin fragments [pt][ks][slot]
+  float* sL = reinterpret_cast<float*>(lds + C::OFF_F);    // l_j
+  float* sDt = sL + Q;                                     // dt_j
+  float* sCol = sL + 2 * Q;                                // exp(l_{16*floor(j/16)+15} - l_j) * dt_j
+  uint16_t* sXn = reinterpret_cast<uint16_t*>(lds + C::OFF_XN);  // x [j][p] (when it fits)
+  uint4* sCf = reinterpret_cast<uint4*>(lds + C::OFF_C);   // C fragments per wavefront (when parked)
+  uint16_t* sB = reinterpret_cast<uint16_t*>(lds + C::OFF_B);  // staged B slice [j][n] (setup only)
 
   const int nhg = H / HB;
   int64_t bid = blockIdx.x;
@@ -89,41 +130,127 @@ __global__ __launch_bounds__(kScanThreads<Q>) void chunk_scan_mfma_kernel(
   const int64_t t0 = c * Q;
   const int rows = (int)(L - t0 < Q ? L - t0 : Q);
 
-  const int r1 = 2 * wave + 1;
-  const int r2 = R - 2 - 2 * wave;
-  const int i1 = 16 * r1 + r16, i2 = 16 * r2 + r16;
-
-  // ---- C fragments of both row groups (B operand: column i, 8 consecutive n) ----
-  bf16x8_t C1[C::NK], C2[C::NK];
+  // row groups of this wavefront: pair m holds 8m + w and 8m + 7 - w
+  int rk[RG], ik[RG];
 #pragma unroll
-  for (int ks = 0; ks < C::NK; ++ks) {
-    const int n = 32 * ks + 8 * g4;
-    const bool nok = n < N;
-    C1[ks] = as_bf16x8(nok && i1 < rows ? ld16(Cm + ((b * L + t0 + i1) * G + g) * N + n) : make_uint4(0, 0, 0, 0));
-    C2[ks] = as_bf16x8(nok && i2 < rows ? ld16(Cm + ((b * L + t0 + i2) * G + g) * N + n) : make_uint4(0, 0, 0, 0));
+  for (int k = 0; k < RG; ++k) {
+    rk[k] = RG == 1 ? wave : 8 * (k >> 1) + ((k & 1) ? 7 - wave : wave);
+    ik[k] = 16 * rk[k] + r16;
   }
+  // G^T slot of off-diagonal tile t of row group k (static for static k, t)
+  auto gslot = [&](int k, int t) {
+    if (RG == 1) return t < R - 1 ? t : R - 2;
+    const int m = k >> 1;
+    const int base = 16 * (m * (m - 1) / 2) + 7 * m;
+    int sidx = (k & 1) ? base + 16 * m + 6 - t : base + t;
+    return sidx < 0 ? 0 : (sidx > C::NGT - 1 ? C::NGT - 1 : sidx);
+  };
 
-  // ---- G^T tiles: k = 0..r1 -> (row group r1, column tile k); k = r1+1..R -> (r2, k-r1-1) ----
-  f32x4_t Gt[R + 1];
+  // ---- C fragments of the row groups (B operand: column i, 8 consecutive n) ----
+  bf16x8_t Cr[RG][NK];
 #pragma unroll
-  for (int k = 0; k <= R; ++k) {
-    const bool in2 = k > r1;
-    const int t = in2 ? k - r1 - 1 : k;
-    const int j = 16 * t + r16;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < RG; ++k)
 #pragma unroll
-    for (int ks = 0; ks < C::NK; ++ks) {
+    for (int ks = 0; ks < NK; ++ks) {
       const int n = 32 * ks + 8 * g4;
-      const bf16x8_t bfrag = as_bf16x8(n < N && j < rows ? ld16(Bm + ((b * L + t0 + j) * G + g) * N + n)
-                                                          : make_uint4(0, 0, 0, 0));
-      acc = mfma_16x16x32(bfrag, in2 ? C2[ks] : C1[ks], acc);
+      const bool ok = n < N && ik[k] < rows;
+      Cr[k][ks] = as_bf16x8(ld16_keep(Cm + ((b * L + t0 + min(ik[k], rows - 1)) * G + g) * N + (n < N ? n : 0), ok));
     }
-    Gt[k] = acc;
+
+  // C fragments parked in this wavefront's LDS region (when they fit): the
+  // G^T set-up below and every head's chunk-output product read them there.
+  uint4* cpark = sCf + wave * (RG * NK * 64);
+  if constexpr (C::PARK_C) {
+#pragma unroll
+    for (int k = 0; k < RG; ++k)
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) cpark[(k * NK + ks) * 64 + lane] = __builtin_bit_cast(uint4, Cr[k][ks]);
   }
 
-  // ---- per-head staging: global -> registers (prefetch) -> LDS ----
+  // ---- G^T = B C^T for every tile a row group needs, B staged through LDS.
+  // Slot e < NGT holds an off-diagonal tile; slot NGT + k the diagonal tile of
+  // row group k. Which (row group, tile) a slot holds depends on the
+  // wavefront only, so the loop over slots is static and branch-free. ----
+  auto slot_rg_tile = [&](int e, int& k, int& t) {
+    if (e >= C::NGT) {
+      k = e - C::NGT;
+      t = rk[k];
+      return;
+    }
+    if (RG == 1) {
+      k = 0;
+      t = e;
+      return;
+    }
+    int m = 0;
+#pragma unroll
+    for (int mm = 1; mm < C::NPAIR; ++mm)
+      if (e >= 16 * (mm * (mm - 1) / 2) + 7 * mm) m = mm;
+    const int base = 16 * (m * (m - 1) / 2) + 7 * m;
+    const int sp = e - base;
+    if (sp < rk[2 * m]) {
+      k = 2 * m;
+      t = sp;
+    } else {
+      k = 2 * m + 1;
+      t = 16 * m + 6 - sp;
+    }
+  };
+  f32x4_t Gacc[C::NGT + RG];
+#pragma unroll
+  for (int e = 0; e < C::NGT + RG; ++e) Gacc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sl = 0; sl < C::NSL; ++sl) {
+    __syncthreads();
+    constexpr int CH = Q * C::NSW / 8;  // 16-byte chunks of the slice
+#pragma unroll
+    for (int q = 0; q < (CH + C::THREADS - 1) / C::THREADS; ++q) {
+      const int ci = tid + q * C::THREADS;
+      if (ci < CH) {
+        const int j = ci / (C::NSW / 8), n0 = 8 * (ci % (C::NSW / 8));
+        st16(sB + j * C::BPITCH + n0,
+             ld16_keep(Bm + ((b * L + t0 + min(j, rows - 1)) * G + g) * N + sl * 128 + n0, j < rows));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < C::NGT + RG; ++e) {
+      int k, t;
+      slot_rg_tile(e, k, t);
+      // slots whose tile a row group does not need (RG == 1 tail) stay unused
+      const int row = 16 * (t < 0 ? 0 : (t > R - 1 ? R - 1 : t)) + r16;
+#pragma unroll
+      for (int kk = 0; kk < C::NSW / 32 + (C::NSW < 32 ? 1 : 0); ++kk) {
+        const int ks = sl * 4 + kk;
+        const int nl = 32 * kk + 8 * g4;
+        const bf16x8_t bfrag = as_bf16x8(nl < C::NSW ? ld16(sB + row * C::BPITCH + nl) : make_uint4(0, 0, 0, 0));
+        bf16x8_t cfrag;
+        if constexpr (C::PARK_C) {
+          cfrag = as_bf16x8(cpark[(k * NK + ks) * 64 + lane]);
+        } else {
+          cfrag = Cr[0][ks];
+#pragma unroll
+          for (int k2 = 1; k2 < RG; ++k2)
+            if (k == k2) cfrag = Cr[k2][ks];
+        }
+        Gacc[e] = mfma_16x16x32(bfrag, cfrag, Gacc[e]);
+      }
+    }
+  }
+  uint2 Gt[C::NGT], Gd[RG];
+#pragma unroll
+  for (int e = 0; e < C::NGT; ++e)
+    Gt[e] = make_uint2(pack_bf16x2(Gacc[e][0], Gacc[e][1]), pack_bf16x2(Gacc[e][2], Gacc[e][3]));
+#pragma unroll
+  for (int k = 0; k < RG; ++k)
+    Gd[k] = make_uint2(pack_bf16x2(Gacc[C::NGT + k][0], Gacc[C::NGT + k][1]),
+                       pack_bf16x2(Gacc[C::NGT + k][2], Gacc[C::NGT + k][3]));
+  __syncthreads();  // the B staging area is reused below
+
+  // ---- per-head inputs: global -> registers (one head ahead) -> LDS ----
+  uint4 xr[C::XPT][4];
   uint4 hr[C::HPT];
-  uint4 xfull[C::XPT][4];
+  float lpre[C::FPT], dpre[C::FPT];
   auto fetch_head = [&](int h) {
 #pragma unroll
     for (int k = 0; k < C::XPT; ++k) {
@@ -133,7 +260,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) void chunk_scan_mfma_kernel(
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int j = 4 * jb + rr;
-          xfull[k][rr] = j < rows ? ld16(x + ((b * L + t0 + j) * H + h) * P + 8 * cb) : make_uint4(0, 0, 0, 0);
+          xr[k][rr] = ld16_keep(x + ((b * L + t0 + min(j, rows - 1)) * H + h) * P + 8 * cb, j < rows);
         }
       }
     }
@@ -143,6 +270,16 @@ __global__ __launch_bounds__(kScanThreads<Q>) void chunk_scan_mfma_kernel(
       const int ci = tid + k * C::THREADS;
       if (ci < C::HCH) hr[k] = ld16(hin + 8 * ci);
     }
+    const float* lc = dA_cs + ((b * H + h) * nc + c) * Q;
+    const float* dc = dtc + ((b * H + h) * nc + c) * Q;
+#pragma unroll
+    for (int k = 0; k < C::FPT; ++k) {
+      const int i = tid + k * C::THREADS;
+      if (i < Q) {
+        lpre[k] = lc[i];
+        dpre[k] = dc[i];
+      }
+    }
   };
   auto stage_head = [&]() {
 #pragma unroll
@@ -150,15 +287,23 @@ __global__ __launch_bounds__(kScanThreads<Q>) void chunk_scan_mfma_kernel(
       const int bi = tid + k * C::THREADS;
       if (bi < C::XBLK) {
         const int cb = bi % (P / 8), jb = bi / (P / 8);
-        // column s of the 4x8 block -> 4 bf16 along j
+        const int j0 = 4 * jb;
+        const int m = j0 >> 5, half = (j0 >> 4) & 1, jg = (j0 >> 2) & 3;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
+        for (int s = 0; s < 8; ++s) {  // column p = 8cb + s: four bf16 along j
           const uint32_t sel = (s & 1) ? 0x07060302u : 0x05040100u;
-          const int m = s >> 1;
-          auto word = [&](const uint4& v) { return m == 0 ? v.x : m == 1 ? v.y : m == 2 ? v.z : v.w; };
-          const uint32_t w0 = __builtin_amdgcn_perm(word(xfull[k][1]), word(xfull[k][0]), sel);
-          const uint32_t w1 = __builtin_amdgcn_perm(word(xfull[k][3]), word(xfull[k][2]), sel);
-          *reinterpret_cast<uint2*>(sX + (8 * cb + s) * C::QP + 4 * jb) = make_uint2(w0, w1);
+          const int mw = s >> 1;
+          auto word = [&](const uint4& v) { return mw == 0 ? v.x : mw == 1 ? v.y : mw == 2 ? v.z : v.w; };
+          const uint32_t w0 = __builtin_amdgcn_perm(word(xr[k][1]), word(xr[k][0]), sel);
+          const uint32_t w1 = __builtin_amdgcn_perm(word(xr[k][3]), word(xr[k][2]), sel);
+          const int p = 8 * cb + s;
+          const int pt = p >> 4;
+          uint4* blk = sXf + (pt * NM + m) * 64;
+          reinterpret_cast<uint2*>(blk + xslot(p & 15, jg, pt))[half] = make_uint2(w0, w1);
+        }
+        if constexpr (C::USE_XN) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) st16(sXn + (j0 + rr) * C::XN_PITCH + 8 * cb, xr[k][rr]);
         }
       }
     }
@@ -166,133 +311,167 @@ __global__ __launch_bounds__(kScanThreads<Q>) void chunk_scan_mfma_kernel(
     for (int k = 0; k < C::HPT; ++k) {
       const int ci = tid + k * C::THREADS;
       if (ci < C::HCH) {
-        const int p = (8 * ci) / N, n = (8 * ci) % N;
-        st16(sH + p * C::NP + n, hr[k]);
+        const int p = ci / (N / 8), n0 = 8 * (ci % (N / 8));
+        sHf[((p >> 4) * NK + (n0 >> 5)) * 64 + hslot(p & 15, (n0 >> 3) & 3)] = hr[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < C::FPT; ++k) {
+      const int i = tid + k * C::THREADS;
+      if (i < Q) {  // Q is a multiple of 64: whole wavefronts take this branch
+        const float lend = __shfl(lpre[k], lane | 15, 64);  // l at the end of the 16-row tile
+        sL[i] = lpre[k];
+        sDt[i] = dpre[k];
+        sCol[i] = __expf(lend - lpre[k]) * dpre[k];
       }
     }
   };
-  auto stage_factors = [&](int h) {
-    const float* lc = dA_cs + ((b * H + h) * nc + c) * Q;
-    const float* dc = dtc + ((b * H + h) * nc + c) * Q;
-    for (int i = tid; i < Q; i += C::THREADS) {
-      const float li = lc[i];
-      const float dj = dc[i];
-      sL[i] = li;
-      sDt[i] = dj;
-      sEl[i] = __expf(li);
-      sRow[i] = __expf(li - lc[i & ~15]);
-      sCol[i] = __expf(lc[i | 15] - li) * dj;
-    }
-    for (int e = tid; e < R * R; e += C::THREADS) {
-      const int r = e / R, t = e % R;
-      sT[e] = t < r ? __expf(lc[16 * r] - lc[16 * t + 15]) : 0.f;
-    }
-  };
 
+  if (N < 32) {  // fragment slots past N stay zero for the whole workgroup
+    for (int e = tid; e < NTP * NK * 64; e += C::THREADS) sHf[e] = make_uint4(0, 0, 0, 0);
+  }
   fetch_head(h0);
   for (int hh = 0; hh < HB; ++hh) {
     const int h = h0 + hh;
     __syncthreads();  // the previous head is done with LDS
     stage_head();
-    stage_factors(h);
     __syncthreads();
     if (hh + 1 < HB) fetch_head(h + 1);  // in flight during this head's products
 
-    f32x4_t acc1[C::NTP], acc2[C::NTP];
+    // per-wavefront decay scalars
+    float lk[RG], rf[RG], el[RG];
 #pragma unroll
-    for (int pt = 0; pt < C::NTP; ++pt) {
-      acc1[pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      acc2[pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < RG; ++k) {
+      lk[k] = sL[ik[k]];
+      el[k] = __expf(lk[k]);
+      rf[k] = __expf(lk[k] - sL[16 * rk[k]]);
     }
-    // chunk output: Y^T[p][i] = sum_n Hin[p][n] C_i[n], scaled by exp(l_i) below
+    float tv = 0.f;  // lane 16k + t: exp(l_{16 r_k} - l_{16t+15}) for t < r_k
+    {
+      const int k = lane >> 4, t = lane & 15;
+      int rr = -1;
 #pragma unroll
-    for (int ks = 0; ks < C::NK; ++ks) {
-      const int n = 32 * ks + 8 * g4;
-#pragma unroll
-      for (int pt = 0; pt < C::NTP; ++pt) {
-        const bf16x8_t a = as_bf16x8(n < N ? ld16(sH + (16 * pt + r16) * C::NP + n) : make_uint4(0, 0, 0, 0));
-        acc1[pt] = mfma_16x16x32(a, C1[ks], acc1[pt]);
-        acc2[pt] = mfma_16x16x32(a, C2[ks], acc2[pt]);
-      }
+      for (int kk = 0; kk < RG; ++kk)
+        if (kk == k) rr = rk[kk];
+      if (t < rr) tv = __expf(sL[16 * rr] - sL[16 * t + 15]);
     }
-    const float el1 = sEl[i1], el2 = sEl[i2];
-    const float li1 = sL[i1], li2 = sL[i2];
-    const float rf1 = sRow[i1], rf2 = sRow[i2];
-#pragma unroll
-    for (int pt = 0; pt < C::NTP; ++pt) {
-      acc1[pt] *= el1;
-      acc2[pt] *= el2;
-    }
-
-    // intra-chunk: pairs of 16-row column tiles -> one 32-deep operand
-#pragma unroll
-    for (int kp = 0; kp < (R + 2) / 2; ++kp) {
-      const int k = 2 * kp;
-      const bool in2 = k > r1;
-      const int r = in2 ? r2 : r1;
-      const int t = in2 ? k - r1 - 1 : k;
-      const int i = in2 ? i2 : i1;
-      const float li = in2 ? li2 : li1;
-      const float rf = in2 ? rf2 : rf1;
-      uint32_t wq[4];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int tt = t + half;
-        const f32x4_t gv = (k + half <= R) ? Gt[k + half < R + 1 ? k + half : R] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int j0 = 16 * tt + 4 * g4;
-        float w[4];
-        if (tt < r) {
-          const float s = rf * sT[r * R + tt];
-          const float4 cf = *reinterpret_cast<const float4*>(sCol + j0);
-          w[0] = gv[0] * s * cf.x;
-          w[1] = gv[1] * s * cf.y;
-          w[2] = gv[2] * s * cf.z;
-          w[3] = gv[3] * s * cf.w;
-        } else if (tt == r) {
-          const float4 lj = *reinterpret_cast<const float4*>(sL + j0);
-          const float4 dj = *reinterpret_cast<const float4*>(sDt + j0);
-          const float ljv[4] = {lj.x, lj.y, lj.z, lj.w};
-          const float djv[4] = {dj.x, dj.y, dj.z, dj.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            w[q] = (j0 + q <= i) ? gv[q] * __expf(li - ljv[q]) * djv[q] : 0.f;
-        } else {
-          w[0] = w[1] = w[2] = w[3] = 0.f;
-        }
-        wq[2 * half] = pack_bf16x2(w[0], w[1]);
-        wq[2 * half + 1] = pack_bf16x2(w[2], w[3]);
-      }
-      const bf16x8_t wop = as_bf16x8(make_uint4(wq[0], wq[1], wq[2], wq[3]));
-      const int ja = 16 * t + 4 * g4, jb2 = 16 * (t + 1) + 4 * g4;
-#pragma unroll
-      for (int pt = 0; pt < C::NTP; ++pt) {
-        const uint16_t* row = sX + (16 * pt + r16) * C::QP;
-        const uint2 lo = *reinterpret_cast<const uint2*>(row + ja);
-        const uint2 hi = (t + 1) * 16 < Q ? *reinterpret_cast<const uint2*>(row + jb2) : make_uint2(0, 0);
-        const bf16x8_t a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-        if (in2)
-          acc2[pt] = mfma_16x16x32(a, wop, acc2[pt]);
-        else
-          acc1[pt] = mfma_16x16x32(a, wop, acc1[pt]);
-      }
-    }
-
-    // epilogue: + D x, store; lane holds Y^T[p = 16pt + 4g4 + q][i]
     const float dh = D != nullptr ? D[h] : 0.f;
+
+    f32x4_t acc[RG][NTP];
+    // chunk output: Y^T[p][i] = sum_n Hin[p][n] C_i[n], scaled by exp(l_i)
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int i = half ? i2 : i1;
+    for (int ks = 0; ks < NK; ++ks) {
+      bf16x8_t ck[RG];
+#pragma unroll
+      for (int k = 0; k < RG; ++k) ck[k] = C::PARK_C ? as_bf16x8(cpark[(k * NK + ks) * 64 + lane]) : Cr[k][ks];
+#pragma unroll
+      for (int pt = 0; pt < NTP; ++pt) {
+        const bf16x8_t a = as_bf16x8(sHf[(pt * NK + ks) * 64 + hslot(r16, g4)]);
+#pragma unroll
+        for (int k = 0; k < RG; ++k)
+          acc[k][pt] = mfma_16x16x32(a, ck[k], ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[k][pt]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < RG; ++k)
+#pragma unroll
+      for (int pt = 0; pt < NTP; ++pt) acc[k][pt] *= el[k];
+
+    // intra-chunk, off-diagonal tiles: all row groups walk the same pairs of
+    // column tiles (2kp, 2kp+1), so one x fragment feeds every row group.
+    // All factors are <= 1: exp(l_i - l_r0) * exp(l_r0 - l_te) * c_j.
+    auto xfrag = [&](int m, int pt) { return sXf[(pt * NM + m) * 64 + xslot(r16, g4, pt)]; };
+    auto colf = [&](int t) { return *reinterpret_cast<const float4*>(sCol + 16 * t + 4 * g4); };
+    auto wpair = [&](uint2 ga, float sa, float4 ca, uint2 gb, float sb, float4 cb) {
+      const float w0 = bf16_lo(ga.x) * sa * ca.x, w1 = bf16_hi(ga.x) * sa * ca.y;
+      const float w2 = bf16_lo(ga.y) * sa * ca.z, w3 = bf16_hi(ga.y) * sa * ca.w;
+      const float w4 = bf16_lo(gb.x) * sb * cb.x, w5 = bf16_hi(gb.x) * sb * cb.y;
+      const float w6 = bf16_lo(gb.y) * sb * cb.z, w7 = bf16_hi(gb.y) * sb * cb.w;
+      return as_bf16x8(make_uint4(pack_bf16x2(w0, w1), pack_bf16x2(w2, w3), pack_bf16x2(w4, w5),
+                                  pack_bf16x2(w6, w7)));
+    };
+    auto lanef = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tv), l)); };
+
+    uint4 an[NTP];
+    float4 can = colf(0), cbn = colf(1);
+#pragma unroll
+    for (int pt = 0; pt < NTP; ++pt) an[pt] = xfrag(0, pt);
+#pragma unroll
+    for (int kp = 0; kp < NM; ++kp) {
+      uint4 a[NTP];
+#pragma unroll
+      for (int pt = 0; pt < NTP; ++pt) a[pt] = an[pt];
+      const float4 ca = can, cb = cbn;
+      if (kp + 1 < NM) {  // compile-time: prefetch the next pair
+#pragma unroll
+        for (int pt = 0; pt < NTP; ++pt) an[pt] = xfrag(kp + 1, pt);
+        can = colf(2 * kp + 2);
+        cbn = colf(2 * kp + 3);
+      }
+      const int ta = 2 * kp, tb = 2 * kp + 1;
+#pragma unroll
+      for (int k = 0; k < RG; ++k) {
+        if (ta < rk[k]) {  // tile tb == r_k is the diagonal: excluded here
+          const float sa = rf[k] * lanef(16 * k + ta);
+          const float sb = tb < rk[k] ? rf[k] * lanef(16 * k + tb) : 0.f;
+          const bf16x8_t w = wpair(Gt[gslot(k, ta)], sa, ca, Gt[gslot(k, tb)], sb, cb);
+#pragma unroll
+          for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(as_bf16x8(a[pt]), w, acc[k][pt]);
+        }
+      }
+    }
+
+    // diagonal tiles: mask (j > i) before the exponential
+#pragma unroll
+    for (int k = 0; k < RG; ++k) {
+      const int t = rk[k], i = ik[k];
+      const int j0 = 16 * t + 4 * g4;
+      const float4 lj = *reinterpret_cast<const float4*>(sL + j0);
+      const float4 dj = *reinterpret_cast<const float4*>(sDt + j0);
+      const float ljv[4] = {lj.x, lj.y, lj.z, lj.w};
+      const float djv[4] = {dj.x, dj.y, dj.z, dj.w};
+      const uint2 gp = Gd[k];
+      const float gv[4] = {bf16_lo(gp.x), bf16_hi(gp.x), bf16_lo(gp.y), bf16_hi(gp.y)};
+      float w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int jq = j0 + q;
+        const float e = __expf(jq <= i ? lk[k] - ljv[q] : -INFINITY);
+        w[q] = gv[q] * e * djv[q];
+      }
+      const uint32_t w01 = pack_bf16x2(w[0], w[1]), w23 = pack_bf16x2(w[2], w[3]);
+      const bool upper = t & 1;  // which half of the 32-deep pair holds tile t
+      const bf16x8_t wop = as_bf16x8(upper ? make_uint4(0, 0, w01, w23) : make_uint4(w01, w23, 0, 0));
+#pragma unroll
+      for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(as_bf16x8(xfrag(t >> 1, pt)), wop, acc[k][pt]);
+    }
+
+    // epilogue: + D_h x_i in fp32, store; lane holds Y^T[p = 16pt + 4g4 + q][i]
+#pragma unroll
+    for (int k = 0; k < RG; ++k) {
+      const int i = ik[k];
       if (i < rows) {
         const int64_t off = ((b * L + t0 + i) * H + h) * P;
 #pragma unroll
-        for (int pt = 0; pt < C::NTP; ++pt) {
+        for (int pt = 0; pt < NTP; ++pt) {
           const int p = 16 * pt + 4 * g4;
-          const uint2 xv = *reinterpret_cast<const uint2*>(x + off + p);
-          const f32x4_t v = half ? acc2[pt] : acc1[pt];
-          const float o0 = v[0] + dh * bf16_lo(xv.x);
-          const float o1 = v[1] + dh * bf16_hi(xv.x);
-          const float o2 = v[2] + dh * bf16_lo(xv.y);
-          const float o3 = v[3] + dh * bf16_hi(xv.y);
+          float xv[4];
+          if constexpr (C::USE_XN) {
+            const uint2 xx = *reinterpret_cast<const uint2*>(sXn + i * C::XN_PITCH + p);
+            xv[0] = bf16_lo(xx.x); xv[1] = bf16_hi(xx.x); xv[2] = bf16_lo(xx.y); xv[3] = bf16_hi(xx.y);
+          } else {
+            const unsigned char* xb = reinterpret_cast<const unsigned char*>(sXf);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int pq = p + q;
+              const int o = (((pq >> 4) * NM + (i >> 5)) * 64 + xslot(pq & 15, (i >> 2) & 3, pq >> 4)) * 16 +
+                            ((i >> 4) & 1) * 8 + (i & 3) * 2;
+              xv[q] = __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(xb + o)) << 16);
+            }
+          }
+          const f32x4_t v = acc[k][pt];
+          const float o0 = fmaf(dh, xv[0], v[0]), o1 = fmaf(dh, xv[1], v[1]);
+          const float o2 = fmaf(dh, xv[2], v[2]), o3 = fmaf(dh, xv[3], v[3]);
           *reinterpret_cast<uint2*>(y + off + p) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
         }
       }
@@ -300,13 +479,14 @@ __global__ __launch_bounds__(kScanThreads<Q>) void chunk_scan_mfma_kernel(
   }
 }
 
-// Heads per workgroup: a divisor of the heads in one B/C group, as large as
-// keeps the grid at >= 1024 workgroups, at most 8.
+// Heads per workgroup: a divisor of the heads in one B/C group, at most 8,
+// as large as keeps at least two workgroups per compute unit (the G^T set-up
+// is amortised over more heads; one workgroup fills a compute unit's LDS).
 int pick_heads_per_wg(const Plan& p) {
   const int64_t hpg = p.H / p.G;
   const int64_t base = p.batch * p.nc * p.H;
   int hb = 1;
-  while (hb < 8 && hpg % (hb * 2) == 0 && base / (hb * 2) >= 1024) hb *= 2;
+  while (hb < 8 && hpg % (hb * 2) == 0 && base / (hb * 2) >= 512) hb *= 2;
   return hb;
 }
 

@@ -79,8 +79,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
         const int j = 8 * jb + rr;
-        r[rr] = j < rows ? ld16(Bm + ((b * L + t0 + j) * G + g) * N + nb * NB + 8 * cb)
-                         : make_uint4(0, 0, 0, 0);
+        r[rr] = ld16_keep(Bm + ((b * L + t0 + min(j, rows - 1)) * G + g) * N + nb * NB + 8 * cb, j < rows);
       }
       transpose8x8(r, o);
 #pragma unroll
@@ -104,8 +103,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
           const int j = 8 * jb + rr;
-          xr[k][rr] = j < rows ? ld16(x + ((b * L + t0 + j) * H + h) * P + 8 * cb)
-                               : make_uint4(0, 0, 0, 0);
+          xr[k][rr] = ld16_keep(x + ((b * L + t0 + min(j, rows - 1)) * H + h) * P + 8 * cb, j < rows);
         }
         lr[k][0] = *reinterpret_cast<const float4*>(lc + 8 * jb);
         lr[k][1] = *reinterpret_cast<const float4*>(lc + 8 * jb + 4);

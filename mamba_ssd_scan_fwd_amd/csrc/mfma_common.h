@@ -36,6 +36,14 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
 }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Load 16 bytes from an address that is always valid (the caller clamps it)
+// and keep them only when `keep` holds. Unlike `keep ? ld16(p) : 0` this is
+// branch-free, so many such loads can be in flight at once.
+__device__ __forceinline__ uint4 ld16_keep(const void* p, bool keep) {
+  const uint4 v = ld16(p);
+  return keep ? v : make_uint4(0, 0, 0, 0);
+}
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // Transpose an 8x8 block of bf16 held as eight rows of 16 bytes: out[s] holds

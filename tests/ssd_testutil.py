@@ -68,6 +68,24 @@ def rel_err(got, ref):
     return float(np.max(np.abs(got - ref))) / max(scale, 1e-30)
 
 
+OUT_EPS = {"bf16": 2.0 ** -8, "fp32": 2.0 ** -23}
+
+
+def check_ssm_part(y_got, y_ref, dx, tol, what, out_eps):
+    """The bar applied to the state-space part y - D x, against its own
+    maximum. The skip term D x can dominate max|y| and would otherwise hide
+    errors in the state-space part; y itself is stored in the io dtype, so
+    each element may also carry one rounding of |y_ref| * out_eps."""
+    y_got = np.asarray(y_got, np.float64)
+    y_ref = np.asarray(y_ref, np.float64)
+    ssm = y_ref - (0.0 if dx is None else np.asarray(dx, np.float64))
+    excess = np.maximum(np.abs(y_got - y_ref) - out_eps * np.abs(y_ref), 0.0)
+    e = float(np.max(excess)) / max(float(np.max(np.abs(ssm))), 1e-30)
+    note(f"    {what} (ssm part, beyond output rounding): {e:.3e} (bar {tol:.0e})")
+    assert e <= tol, f"{what}: state-space part error {e:.3e} > {tol:.0e}"
+    return e
+
+
 def check_rel(got, ref, tol, what):
     e = rel_err(got, ref)
     note(f"    {what}: max|err|/max|ref| = {e:.3e} (bar {tol:.0e})")

@@ -25,7 +25,7 @@ from oracle import chunk_entry_states as o_entry
 from oracle import chunk_local_states as o_local
 from oracle import ssd_recurrent
 from ssd_inputs import CONFIGS, make_inputs
-from ssd_testutil import TOL, check_rel, note, np64, oracle_sampled
+from ssd_testutil import OUT_EPS, TOL, check_rel, check_ssm_part, note, np64, oracle_sampled
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +54,9 @@ def full_check(inp, tol, tag, **kw):
     y, hT = run(inp, **kw)
     yr, hr = ssd_recurrent(*(np64(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "init_state")))
     check_rel(np64(y), yr, tol, f"{tag} y")
+    io = "bf16" if inp["x"].dtype == torch.bfloat16 else "fp32"
+    dx = None if inp["D"] is None else np64(inp["x"]) * np64(inp["D"])[:, None]
+    check_ssm_part(np64(y), yr, dx, tol, f"{tag} y", OUT_EPS[io])
     if hT is not None:
         check_rel(np64(hT), hr, tol, f"{tag} final_state")
     return y, hT
@@ -63,8 +66,15 @@ def sampled_check(inp, pairs, tol, tag, **kw):
     note(f"[gpu] {tag}: x{tuple(inp['x'].shape)} B{tuple(inp['B'].shape)} {inp['x'].dtype} pairs={pairs}")
     y, hT = run(inp, **kw)
     ref = oracle_sampled(inp, pairs)
-    ey = check_rel(np.stack([np64(y[b, :, h]) for b, h in pairs]),
-                   np.stack([ref[p][0] for p in pairs]), tol, f"{tag} y (sampled)")
+    yg = np.stack([np64(y[b, :, h]) for b, h in pairs])
+    yo = np.stack([ref[p][0] for p in pairs])
+    ey = check_rel(yg, yo, tol, f"{tag} y (sampled)")
+    dx = None
+    if inp["D"] is not None:
+        xs = np.stack([np64(inp["x"][b, :, h]) for b, h in pairs])
+        dx = np.array([float(inp["D"][h]) for b, h in pairs])[:, None, None] * xs
+    io = "bf16" if inp["x"].dtype == torch.bfloat16 else "fp32"
+    check_ssm_part(yg, yo, dx, tol, f"{tag} y (sampled)", OUT_EPS[io])
     eh = check_rel(np.stack([np64(hT[b, h]) for b, h in pairs]),
                    np.stack([ref[p][1] for p in pairs]), tol, f"{tag} final_state (sampled)")
     assert torch.isfinite(y.float()).all() and torch.isfinite(hT).all()
