@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
   const int g = h0 / (H / G);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int r16 = lane & 15, g4 = lane >> 4;
   const int64_t t0 = c * Q;
   const int rows = (int)(L - t0 < Q ? L - t0 : Q);
@@ -213,25 +213,31 @@ __global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
       }
     }
     __syncthreads();
+    int srow[C::NGT + RG], sk[C::NGT + RG];
 #pragma unroll
     for (int e = 0; e < C::NGT + RG; ++e) {
       int k, t;
       slot_rg_tile(e, k, t);
       // slots whose tile a row group does not need (RG == 1 tail) stay unused
-      const int row = 16 * (t < 0 ? 0 : (t > R - 1 ? R - 1 : t)) + r16;
+      srow[e] = 16 * (t < 0 ? 0 : (t > R - 1 ? R - 1 : t)) + r16;
+      sk[e] = k;
+    }
 #pragma unroll
-      for (int kk = 0; kk < C::NSW / 32 + (C::NSW < 32 ? 1 : 0); ++kk) {
-        const int ks = sl * 4 + kk;
-        const int nl = 32 * kk + 8 * g4;
-        const bf16x8_t bfrag = as_bf16x8(nl < C::NSW ? ld16(sB + row * C::BPITCH + nl) : make_uint4(0, 0, 0, 0));
+    for (int kk = 0; kk < C::NSW / 32 + (C::NSW < 32 ? 1 : 0); ++kk) {
+      const int ks = sl * 4 + kk;
+      const int nl = 32 * kk + 8 * g4;
+#pragma unroll
+      for (int e = 0; e < C::NGT + RG; ++e) {
+        const bf16x8_t bfrag =
+            as_bf16x8(nl < C::NSW ? ld16(sB + srow[e] * C::BPITCH + nl) : make_uint4(0, 0, 0, 0));
         bf16x8_t cfrag;
         if constexpr (C::PARK_C) {
-          cfrag = as_bf16x8(cpark[(k * NK + ks) * 64 + lane]);
+          cfrag = as_bf16x8(cpark[(sk[e] * NK + ks) * 64 + lane]);
         } else {
           cfrag = Cr[0][ks];
 #pragma unroll
           for (int k2 = 1; k2 < RG; ++k2)
-            if (k == k2) cfrag = Cr[k2][ks];
+            if (sk[e] == k2) cfrag = Cr[k2][ks];
         }
         Gacc[e] = mfma_16x16x32(bfrag, cfrag, Gacc[e]);
       }
@@ -251,7 +257,9 @@ __global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
   uint4 xr[C::XPT][4];
   uint4 hr[C::HPT];
   float lpre[C::FPT], dpre[C::FPT];
+  float dnext = 0.f;
   auto fetch_head = [&](int h) {
+    dnext = D != nullptr ? D[h] : 0.f;
 #pragma unroll
     for (int k = 0; k < C::XPT; ++k) {
       const int bi = tid + k * C::THREADS;
@@ -259,8 +267,10 @@ __global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
         const int cb = bi % (P / 8), jb = bi / (P / 8);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
+          // raw load (clamped row, always in bounds); rows past the end are
+          // zeroed when staged, so nothing here waits for the data
           const int j = 4 * jb + rr;
-          xr[k][rr] = ld16_keep(x + ((b * L + t0 + min(j, rows - 1)) * H + h) * P + 8 * cb, j < rows);
+          xr[k][rr] = ld16(x + ((b * L + t0 + min(j, rows - 1)) * H + h) * P + 8 * cb);
         }
       }
     }
@@ -289,6 +299,9 @@ __global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
         const int cb = bi % (P / 8), jb = bi / (P / 8);
         const int j0 = 4 * jb;
         const int m = j0 >> 5, half = (j0 >> 4) & 1, jg = (j0 >> 2) & 3;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          if (j0 + rr >= rows) xr[k][rr] = make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {  // column p = 8cb + s: four bf16 along j
           const uint32_t sel = (s & 1) ? 0x07060302u : 0x05040100u;
@@ -330,13 +343,19 @@ __global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
   if (N < 32) {  // fragment slots past N stay zero for the whole workgroup
     for (int e = tid; e < NTP * NK * 64; e += C::THREADS) sHf[e] = make_uint4(0, 0, 0, 0);
   }
+  // The loop is rotated by hand: head h's inputs are staged at the end of
+  // iteration h-1, after its stores, so the only path into each staging step
+  // has the same loads and stores outstanding and the wait for the prefetched
+  // inputs does not also wait for the y stores that follow them.
   fetch_head(h0);
+  stage_head();
+  __syncthreads();
   for (int hh = 0; hh < HB; ++hh) {
     const int h = h0 + hh;
-    __syncthreads();  // the previous head is done with LDS
-    stage_head();
-    __syncthreads();
-    if (hh + 1 < HB) fetch_head(h + 1);  // in flight during this head's products
+    const float dh = dnext;
+    // in flight during this head's products (the last head re-reads itself,
+    // which keeps the memory-operation count the same on every iteration)
+    fetch_head(hh + 1 < HB ? h + 1 : h);
 
     // per-wavefront decay scalars
     float lk[RG], rf[RG], el[RG];
@@ -355,8 +374,6 @@ __global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
         if (kk == k) rr = rk[kk];
       if (t < rr) tv = __expf(sL[16 * rr] - sL[16 * t + 15]);
     }
-    const float dh = D != nullptr ? D[h] : 0.f;
-
     f32x4_t acc[RG][NTP];
     // chunk output: Y^T[p][i] = sum_n Hin[p][n] C_i[n], scaled by exp(l_i)
 #pragma unroll
@@ -446,35 +463,42 @@ __global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
       for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(as_bf16x8(xfrag(t >> 1, pt)), wop, acc[k][pt]);
     }
 
-    // epilogue: + D_h x_i in fp32, store; lane holds Y^T[p = 16pt + 4g4 + q][i]
+    // epilogue: + D_h x_i in fp32, store; lane holds Y^T[p = 16pt + 4g4 + q][i].
+    // Rows past the end of the sequence fall outside the buffer range and are
+    // dropped, so the store sequence is the same for every chunk.
+    uint16_t* ybase = y + ((b * L + t0) * H + h) * P;
+    const __amdgpu_buffer_rsrc_t yr = buffer_range(ybase, (uint32_t)(((rows - 1) * (int64_t)H + 1) * P * 2));
 #pragma unroll
     for (int k = 0; k < RG; ++k) {
       const int i = ik[k];
-      if (i < rows) {
-        const int64_t off = ((b * L + t0 + i) * H + h) * P;
+      const uint32_t rowoff = (uint32_t)(i * (int64_t)H * P * 2);
 #pragma unroll
-        for (int pt = 0; pt < NTP; ++pt) {
-          const int p = 16 * pt + 4 * g4;
-          float xv[4];
-          if constexpr (C::USE_XN) {
-            const uint2 xx = *reinterpret_cast<const uint2*>(sXn + i * C::XN_PITCH + p);
-            xv[0] = bf16_lo(xx.x); xv[1] = bf16_hi(xx.x); xv[2] = bf16_lo(xx.y); xv[3] = bf16_hi(xx.y);
-          } else {
-            const unsigned char* xb = reinterpret_cast<const unsigned char*>(sXf);
+      for (int pt = 0; pt < NTP; ++pt) {
+        const int p = 16 * pt + 4 * g4;
+        float xv[4];
+        if constexpr (C::USE_XN) {
+          const uint2 xx = *reinterpret_cast<const uint2*>(sXn + i * C::XN_PITCH + p);
+          xv[0] = bf16_lo(xx.x); xv[1] = bf16_hi(xx.x); xv[2] = bf16_lo(xx.y); xv[3] = bf16_hi(xx.y);
+        } else {
+          const unsigned char* xb = reinterpret_cast<const unsigned char*>(sXf);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int pq = p + q;
-              const int o = (((pq >> 4) * NM + (i >> 5)) * 64 + xslot(pq & 15, (i >> 2) & 3, pq >> 4)) * 16 +
-                            ((i >> 4) & 1) * 8 + (i & 3) * 2;
-              xv[q] = __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(xb + o)) << 16);
-            }
+          for (int q = 0; q < 4; ++q) {
+            const int pq = p + q;
+            const int o = (((pq >> 4) * NM + (i >> 5)) * 64 + xslot(pq & 15, (i >> 2) & 3, pq >> 4)) * 16 +
+                          ((i >> 4) & 1) * 8 + (i & 3) * 2;
+            xv[q] = __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(xb + o)) << 16);
           }
-          const f32x4_t v = acc[k][pt];
-          const float o0 = fmaf(dh, xv[0], v[0]), o1 = fmaf(dh, xv[1], v[1]);
-          const float o2 = fmaf(dh, xv[2], v[2]), o3 = fmaf(dh, xv[3], v[3]);
-          *reinterpret_cast<uint2*>(y + off + p) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
         }
+        const f32x4_t v = acc[k][pt];
+        const float o0 = fmaf(dh, xv[0], v[0]), o1 = fmaf(dh, xv[1], v[1]);
+        const float o2 = fmaf(dh, xv[2], v[2]), o3 = fmaf(dh, xv[3], v[3]);
+        buffer_st8(make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)), yr, rowoff + p * 2);
       }
+    }
+    __syncthreads();  // every wavefront is done with this head's LDS tiles
+    if (hh + 1 < HB) {
+      stage_head();
+      __syncthreads();
     }
   }
 }
@@ -529,6 +553,8 @@ hipError_t launch_p(const Plan& p, const void* x, const void* B, const void* Cm,
 }  // namespace
 
 bool mfma_chunk_scan_supported(const Plan& p) {
+  // byte offsets inside one chunk's rows of y must fit the 32-bit buffer range
+  if (int64_t(p.Q) * p.H * p.P * 2 >= (int64_t(1) << 31)) return false;
   return p.io == kBF16 && (p.P == 16 || p.P == 32 || p.P == 64 || p.P == 128) &&
          (p.N == 16 || p.N == 32 || p.N == 64 || p.N == 128 || p.N == 256) &&
          (p.Q == 64 || p.Q == 128 || p.Q == 256);

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   const int g = h0 / (H / G);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int64_t t0 = c * Q;
   const int rows = (int)(L - t0 < Q ? L - t0 : Q);  // valid positions in this chunk
 
@@ -103,7 +103,9 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
           const int j = 8 * jb + rr;
-          xr[k][rr] = ld16_keep(x + ((b * L + t0 + min(j, rows - 1)) * H + h) * P + 8 * cb, j < rows);
+          // raw load (clamped row, always in bounds): rows past the end are
+          // zeroed when staged, so nothing here waits for the data
+          xr[k][rr] = ld16(x + ((b * L + t0 + min(j, rows - 1)) * H + h) * P + 8 * cb);
         }
         lr[k][0] = *reinterpret_cast<const float4*>(lc + 8 * jb);
         lr[k][1] = *reinterpret_cast<const float4*>(lc + 8 * jb + 4);
@@ -125,7 +127,10 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
                              dr[k][1].x, dr[k][1].y, dr[k][1].z, dr[k][1].w};
         float w[8];
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) w[rr] = __expf(lam - l8[rr]) * d8[rr];
+        for (int rr = 0; rr < 8; ++rr) {
+          w[rr] = __expf(lam - l8[rr]) * d8[rr];
+          if (8 * jb + rr >= rows) xr[k][rr] = make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           uint32_t q[4];

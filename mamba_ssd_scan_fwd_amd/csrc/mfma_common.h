@@ -46,6 +46,18 @@ __device__ __forceinline__ uint4 ld16_keep(const void* p, bool keep) {
 }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// A raw buffer resource covering [base, base + bytes): stores at offsets at or
+// past `bytes` are discarded by the hardware's range check. This lets a
+// ragged tail be written with the same unconditional store sequence as a full
+// tile (no divergent branch around the stores).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void buffer_st8(const uint2& v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(v2i{(int)v.x, (int)v.y}, r, (int)off, 0, 0);
+}
+
 // Transpose an 8x8 block of bf16 held as eight rows of 16 bytes: out[s] holds
 // column s (rows 0..7, row 0 in the low half of word 0).
 __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
