@@ -6,21 +6,25 @@
 // changed in practice").
 //
 // As a matrix product per (b, c, h): S^T[N x P] = B_c^T[N x Q] * Xs[Q x P],
-// with Xs = diag(w) x_c. The contraction runs over the chunk positions j, and
+// with Xs = diag(w) x_c. The contraction runs over the chunk positions j and
 // both operands are stored position-major in HBM (row j holds a contiguous P
-// or N vector), so each 16-byte operand fragment of eight consecutive j must
-// be gathered from eight rows. Tiles are therefore staged through LDS
-// transposed ([n][j] and [p][j], j contiguous): every thread loads an 8x8
-// block with eight coalesced 16-byte row reads, transposes it in registers
-// (x is scaled by w_j and rounded to bf16 on the way), and writes eight
-// 16-byte LDS rows; the matrix-core loop then reads each fragment with one
-// 16-byte LDS read.
+// or N vector), so every 16-byte operand fragment of eight consecutive j is
+// gathered from eight rows: tiles are transposed in registers (an 8x8 block
+// per thread, eight coalesced 16-byte row reads) on their way into LDS.
 //
 // Work split: one workgroup (4 wavefronts) per (b, c, group of HB heads that
-// share a B/C group, block of up to 128 state columns). B_c^T is staged once
-// and reused by the HB heads; the next head's x block is loaded into
-// registers while the current head's products run. Output tiles hold four
-// consecutive n per lane, written as 8-byte stores into states[b,h,c][p][n].
+// share a B/C group, block of up to 128 state columns).
+//  * B_c^T is staged through LDS once; each wavefront then keeps the
+//    fragments of its own n tiles in registers for all HB heads, and the LDS
+//    is reused as a double buffer for the scaled x of successive heads.
+//  * LDS tiles are fragment-major (each lane's 16-byte fragment contiguous,
+//    so operand reads are conflict-free) with a lane-slot swizzle that spreads
+//    the staging writes over the banks.
+//  * The next head's x rows, l and dt are loaded into registers while the
+//    current head's products run; they are scaled by w_j, rounded to bf16 and
+//    written transposed into the other LDS buffer; one barrier per head.
+//  * Output tiles hold four consecutive n per lane: 8-byte stores into
+//    states[b,h,c][p][n].
 #include "mfma_common.h"
 
 namespace ssd {
@@ -30,18 +34,26 @@ constexpr int kThreads = 256;
 
 template <int P, int NB, int Q>
 struct StateCfg {
-  static constexpr int QP = Q + 8;  // LDS row pitch (bf16): 16-byte pad spreads banks
   static constexpr int NT_N = NB / 16, NT_P = P / 16;
   static constexpr int WN = NT_N >= 4 ? 4 : NT_N;  // wavefronts along n
   static constexpr int WP = 4 / WN;                // wavefronts along p
   static constexpr int TN = NT_N / WN;             // n tiles per wavefront
   static constexpr int TP = (NT_P + WP - 1) / WP;  // p tiles per wavefront
-  static constexpr int XBLK = (Q / 8) * (P / 8);   // 8x8 blocks in the x tile
-  static constexpr int BBLK = (Q / 8) * (NB / 8);  // 8x8 blocks in the B tile
+  static constexpr int KS = Q / 32;                // 32-deep steps over the chunk
+  static constexpr int XBLK = (Q / 8) * (P / 8);   // 8x8 blocks of the x tile
+  static constexpr int BBLK = (Q / 8) * (NB / 8);  // 8x8 blocks of the B tile
   static constexpr int XPT = (XBLK + kThreads - 1) / kThreads;
   static constexpr int BPT = (BBLK + kThreads - 1) / kThreads;
-  static constexpr size_t lds_bytes = size_t(NB + P) * QP * 2;
+  static constexpr int X_FRAGS = NT_P * KS * 64;   // 16-byte fragments of one x buffer
+  static constexpr int B_FRAGS = NT_N * KS * 64;
+  static constexpr int LDS_FRAGS = (2 * X_FRAGS > B_FRAGS ? 2 * X_FRAGS : B_FRAGS);
 };
+
+// slot of lane (r16, g4) inside a 1 KB fragment block (a bijection, so the
+// matrix-core reads stay conflict-free; it spreads the transposed writes)
+__device__ __forceinline__ int sslot(int r16, int g4, int tile) {
+  return 16 * g4 + ((r16 + 2 * g4 + (tile & 1)) & 15);
+}
 
 template <int P, int NB, int Q>
 __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
@@ -49,8 +61,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const float* __restrict__ dA_cs, const float* __restrict__ dtc,
     uint16_t* __restrict__ states, int64_t L, int H, int G, int N, int64_t nc, int HB) {
   using C = StateCfg<P, NB, Q>;
-  __shared__ __align__(16) uint16_t sB[NB * C::QP];
-  __shared__ __align__(16) uint16_t sX[P * C::QP];
+  constexpr int KS = C::KS;
+  __shared__ __align__(16) uint4 lds[C::LDS_FRAGS];
 
   const int nnb = N / NB;
   const int nhg = H / HB;
@@ -66,10 +78,12 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
+  const int r16 = lane & 15, g4 = lane >> 4;
   const int64_t t0 = c * Q;
   const int rows = (int)(L - t0 < Q ? L - t0 : Q);  // valid positions in this chunk
+  const int wn = wave % C::WN, wp = wave / C::WN;
 
-  // ---- B_c^T -> sB[n][j] (once per workgroup) ----
+  // ---- B_c^T -> LDS fragments [nt][ks][slot] (once), then into registers ----
 #pragma unroll
   for (int k = 0; k < C::BPT; ++k) {
     const int bi = tid + k * kThreads;
@@ -82,40 +96,49 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         r[rr] = ld16_keep(Bm + ((b * L + t0 + min(j, rows - 1)) * G + g) * N + nb * NB + 8 * cb, j < rows);
       }
       transpose8x8(r, o);
+      // column n = 8cb + s holds B[8jb .. 8jb+7][n]: one fragment slot
 #pragma unroll
-      for (int s = 0; s < 8; ++s) st16(sB + (8 * cb + s) * C::QP + 8 * jb, o[s]);
+      for (int s = 0; s < 8; ++s) {
+        const int n = 8 * cb + s, nt = n >> 4;
+        lds[(nt * KS + (jb >> 2)) * 64 + sslot(n & 15, jb & 3, nt)] = o[s];
+      }
     }
   }
+  __syncthreads();
+  bf16x8_t bt[C::TN][KS];
+#pragma unroll
+  for (int tn = 0; tn < C::TN; ++tn) {
+    const int nt = wn * C::TN + tn;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bt[tn][ks] = as_bf16x8(lds[(nt * KS + ks) * 64 + sslot(r16, g4, nt)]);
+  }
+  __syncthreads();  // the LDS becomes the x double buffer
 
-  // ---- x block loader: thread block bi covers rows 8jb..8jb+7, cols 8cb..8cb+7 ----
+  // ---- x of one head: raw rows into registers; scaled, transposed into LDS ----
   uint4 xr[C::XPT][8];
   float4 lr[C::XPT][2], dr[C::XPT][2];
   float lam = 0.f;
-  auto load_x = [&](int h) {
+  auto fetch_x = [&](int h) {
     const float* lc = dA_cs + ((b * H + h) * nc + c) * Q;
     const float* dc = dtc + ((b * H + h) * nc + c) * Q;
     lam = lc[Q - 1];
 #pragma unroll
     for (int k = 0; k < C::XPT; ++k) {
       const int bi = tid + k * kThreads;
-      if (bi < C::XBLK) {
-        const int cb = bi % (P / 8), jb = bi / (P / 8);
+      const int cb = bi % (P / 8), jb = (bi / (P / 8)) % (Q / 8);
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          const int j = 8 * jb + rr;
-          // raw load (clamped row, always in bounds): rows past the end are
-          // zeroed when staged, so nothing here waits for the data
-          xr[k][rr] = ld16(x + ((b * L + t0 + min(j, rows - 1)) * H + h) * P + 8 * cb);
-        }
-        lr[k][0] = *reinterpret_cast<const float4*>(lc + 8 * jb);
-        lr[k][1] = *reinterpret_cast<const float4*>(lc + 8 * jb + 4);
-        dr[k][0] = *reinterpret_cast<const float4*>(dc + 8 * jb);
-        dr[k][1] = *reinterpret_cast<const float4*>(dc + 8 * jb + 4);
+      for (int rr = 0; rr < 8; ++rr) {
+        // clamped row, always in bounds; rows past the end are zeroed later
+        const int j = 8 * jb + rr;
+        xr[k][rr] = ld16(x + ((b * L + t0 + min(j, rows - 1)) * H + h) * P + 8 * cb);
       }
+      lr[k][0] = *reinterpret_cast<const float4*>(lc + 8 * jb);
+      lr[k][1] = *reinterpret_cast<const float4*>(lc + 8 * jb + 4);
+      dr[k][0] = *reinterpret_cast<const float4*>(dc + 8 * jb);
+      dr[k][1] = *reinterpret_cast<const float4*>(dc + 8 * jb + 4);
     }
   };
-  // scale rows by w_j = exp(Lam - l_j) dt_j, round to bf16, write transposed
-  auto store_x = [&]() {
+  auto stage_x = [&](uint4* buf) {
 #pragma unroll
     for (int k = 0; k < C::XPT; ++k) {
       const int bi = tid + k * kThreads;
@@ -127,57 +150,52 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
                              dr[k][1].x, dr[k][1].y, dr[k][1].z, dr[k][1].w};
         float w[8];
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          w[rr] = __expf(lam - l8[rr]) * d8[rr];
-          if (8 * jb + rr >= rows) xr[k][rr] = make_uint4(0, 0, 0, 0);
-        }
+        for (int rr = 0; rr < 8; ++rr)
+          w[rr] = 8 * jb + rr < rows ? __expf(lam - l8[rr]) * d8[rr] : 0.f;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
+        for (int s = 0; s < 8; ++s) {  // column p = 8cb + s: eight scaled bf16 along j
           uint32_t q[4];
 #pragma unroll
           for (int m = 0; m < 4; ++m)
-            q[m] = pack_bf16x2(w[2 * m] * bf16_at(xr[k][2 * m], s),
-                               w[2 * m + 1] * bf16_at(xr[k][2 * m + 1], s));
-          st16(sX + (8 * cb + s) * C::QP + 8 * jb, make_uint4(q[0], q[1], q[2], q[3]));
+            q[m] = pack_bf16x2(w[2 * m] * bf16_at(xr[k][2 * m], s), w[2 * m + 1] * bf16_at(xr[k][2 * m + 1], s));
+          const int p = 8 * cb + s, pt = p >> 4;
+          buf[(pt * KS + (jb >> 2)) * 64 + sslot(p & 15, jb & 3, pt)] = make_uint4(q[0], q[1], q[2], q[3]);
         }
       }
     }
   };
 
-  const int wn = wave % C::WN, wp = wave / C::WN;
-  const int r16 = lane & 15, g4 = lane >> 4;
   const int ksteps = (rows + 31) / 32;
-
-  load_x(h0);
+  fetch_x(h0);
+  stage_x(lds);
+  __syncthreads();
   for (int hh = 0; hh < HB; ++hh) {
     const int h = h0 + hh;
-    __syncthreads();  // previous head's products are done reading sX
-    store_x();
-    __syncthreads();
-    if (hh + 1 < HB) load_x(h + 1);  // in flight during the products below
+    uint4* cur = lds + (hh & 1) * C::X_FRAGS;
+    // in flight during this head's products (the last head re-reads itself,
+    // which keeps the memory-operation count the same on every iteration)
+    fetch_x(hh + 1 < HB ? h + 1 : h);
 
     f32x4_t acc[C::TN][C::TP];
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn)
 #pragma unroll
       for (int tp = 0; tp < C::TP; ++tp) acc[tn][tp] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int ks = 0; ks < ksteps; ++ks) {
-      const int k0 = ks * 32 + 8 * g4;
-      bf16x8_t a[C::TN], bb[C::TP];
 #pragma unroll
-      for (int tn = 0; tn < C::TN; ++tn)
-        a[tn] = as_bf16x8(ld16(sB + ((wn * C::TN + tn) * 16 + r16) * C::QP + k0));
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks < ksteps) {  // uniform: skip steps entirely past the end
+        bf16x8_t bb[C::TP];
 #pragma unroll
-      for (int tp = 0; tp < C::TP; ++tp) {
-        const int pt = wp * C::TP + tp;
-        bb[tp] = pt < C::NT_P ? as_bf16x8(ld16(sX + (pt * 16 + r16) * C::QP + k0))
-                              : as_bf16x8(make_uint4(0, 0, 0, 0));
+        for (int tp = 0; tp < C::TP; ++tp) {
+          const int pt = wp * C::TP + tp;
+          bb[tp] = pt < C::NT_P ? as_bf16x8(cur[(pt * KS + ks) * 64 + sslot(r16, g4, pt)])
+                                : as_bf16x8(make_uint4(0, 0, 0, 0));
+        }
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+          for (int tp = 0; tp < C::TP; ++tp) acc[tn][tp] = mfma_16x16x32(bt[tn][ks], bb[tp], acc[tn][tp]);
       }
-#pragma unroll
-      for (int tn = 0; tn < C::TN; ++tn)
-#pragma unroll
-        for (int tp = 0; tp < C::TP; ++tp) acc[tn][tp] = mfma_16x16x32(a[tn], bb[tp], acc[tn][tp]);
     }
 
     // lane holds S^T[n = 4*g4 + i][p = r16] of each tile: four consecutive n
@@ -196,11 +214,14 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         }
       }
     }
+    if (hh + 1 < HB) stage_x(lds + ((hh + 1) & 1) * C::X_FRAGS);  // the other buffer
+    __syncthreads();
   }
 }
 
-// Heads per workgroup: a divisor of the heads in one B/C group, as large as
-// keeps the grid at >= 1024 workgroups (4 per compute unit), at most 8.
+// Heads per workgroup: a divisor of the heads in one B/C group, at most 8,
+// as large as keeps the grid at >= 1024 workgroups (two resident per compute
+// unit, two rounds).
 int pick_heads_per_wg(const Plan& p, int nnb) {
   const int64_t hpg = p.H / p.G;
   const int64_t base = p.batch * p.nc * nnb * p.H;
