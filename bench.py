@@ -42,7 +42,10 @@ def parse():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--kernel-reps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=2)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=8)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain fp32 elementwise copy (negation) of MIB MiB, "
+                         "the reference kernel for scaling rocprofv3 byte counters")
     return ap.parse_args()
 
 
@@ -98,8 +101,9 @@ def traffic_from_profile(kernel, cfg_name, per_launch_algo):
         return None
 
 
-def cpu_baseline(cfg, inp, nseq):
-    """The fp64 oracle as it stands, on `nseq` whole sequences (all heads)."""
+def cpu_baseline(cfg, inp, nseq, min_seconds=10.0, max_reps=4):
+    """The fp64 oracle as it stands, on `nseq` whole sequences (all heads),
+    repeated until about `min_seconds` of CPU work have been timed."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_limits
@@ -116,21 +120,25 @@ def cpu_baseline(cfg, inp, nseq):
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     if ctx:
         ctx.__enter__()
+    reps, total = 0, 0.0
     try:
-        t0 = time.perf_counter()
-        ssd_recurrent(*args)
-        dt = time.perf_counter() - t0
+        while reps < max_reps and (reps == 0 or total < min_seconds):
+            t0 = time.perf_counter()
+            ssd_recurrent(*args)
+            total += time.perf_counter() - t0
+            reps += 1
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
     tokens = nseq * cfg.seqlen
     return {
-        "value": tokens / dt,
+        "value": tokens * reps / total,
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{nseq} of {cfg.batch} sequences x {cfg.seqlen} tokens, all {cfg.nheads} heads "
-                  f"({tokens} tokens, {dt:.1f} s, fp64 NumPy, one thread, {platform.processor() or platform.machine()})",
+        "sample": f"{nseq} of {cfg.batch} sequences x {cfg.seqlen} tokens, all {cfg.nheads} heads, "
+                  f"{reps} pass(es) ({tokens * reps} tokens in {total:.1f} s; fp64 NumPy sequential "
+                  f"recurrence, one thread, {platform.processor() or platform.machine()})",
     }
 
 
@@ -165,6 +173,15 @@ def main():
     def step():
         ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], chunk_size=args.chunk,
                     y=y, final_state=hT, workspace=ws)
+
+    if args.copy_calibration:
+        # known traffic: reads and writes exactly MIB MiB each
+        src = torch.ones(args.copy_calibration * (1 << 18), dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
   uint16_t* sB = reinterpret_cast<uint16_t*>(lds + C::OFF_B);  // staged B slice [j][n] (setup only)
 
   const int nhg = H / HB;
-  int64_t bid = blockIdx.x;
+  int64_t bid = xcd_local_order(blockIdx.x, gridDim.x);
   const int hg = (int)(bid % nhg);
   bid /= nhg;
   const int64_t c = bid % nc;

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 
   const int nnb = N / NB;
   const int nhg = H / HB;
-  int64_t bid = blockIdx.x;
+  int64_t bid = xcd_local_order(blockIdx.x, gridDim.x);
   const int nb = (int)(bid % nnb);
   bid /= nnb;
   const int hg = (int)(bid % nhg);

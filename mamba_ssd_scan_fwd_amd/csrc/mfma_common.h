@@ -78,6 +78,16 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[
   }
 }
 
+// Workgroups are handed to the eight XCDs (each with its own L2) round-robin
+// by workgroup id. This renumbering gives each XCD one contiguous run of
+// logical ids, so workgroups that share operands (neighbouring logical ids:
+// the heads of one chunk) run on the same XCD and meet in its L2.
+__device__ __forceinline__ int64_t xcd_local_order(int64_t bid, int64_t grid) {
+  constexpr int kXcds = 8;
+  if (grid % kXcds != 0) return bid;
+  return (bid % kXcds) * (grid / kXcds) + bid / kXcds;
+}
+
 // Element e (0..7) of a row of eight bf16 held in a uint4, as fp32.
 __device__ __forceinline__ float bf16_at(const uint4& v, int e) {
   const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
