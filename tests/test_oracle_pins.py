@@ -24,6 +24,9 @@ transposed operand or a wrong head->group map fails at least one of them:
 
 from fractions import Fraction
 
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -143,42 +146,47 @@ def test_single_token_closed_form():
             assert rel(y[b, 0, h], hh @ C[b, 0, 0] + D[h] * x[b, 0, h]) < 1e-14
 
 
-def test_hand_worked_rational_example():
-    # P = N = 1, one head, A = -ln 2 and dt = 1 so each step halves the state;
-    # B = C = 1, D = 1/4, h0 = 8, x = (1, 2, 3).  By hand:
-    #   h0' = 8/2 + 1 = 5        y0 = 5      + 1/4 = 21/4
-    #   h1  = 5/2 + 2 = 9/2      y1 = 9/2    + 2/4 = 5
-    #   h2  = 9/4 + 3 = 21/4     y2 = 21/4   + 3/4 = 6
-    x = np.array([1.0, 2.0, 3.0]).reshape(1, 3, 1, 1)
-    dt = np.ones((1, 3, 1))
-    A = np.array([-np.log(2.0)])
-    B = np.ones((1, 3, 1, 1))
-    C = np.ones((1, 3, 1, 1))
-    D = np.array([0.25])
-    h0 = np.full((1, 1, 1, 1), 8.0)
-    y, hT = ssd_recurrent(x, dt, A, B, C, D, h0)
-    expect_y = [Fraction(21, 4), Fraction(5), Fraction(6)]
-    for t in range(3):
-        assert y[0, t, 0, 0] == pytest.approx(float(expect_y[t]), rel=1e-15)
-    assert hT[0, 0, 0, 0] == pytest.approx(21 / 4, rel=1e-15)
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
-    # two heads sharing one group, P = 2, N = 2: the state is the outer
-    # product dt x B^T, read out through C. With A = 0 (no decay), dt = 1/2:
-    #   h = sum_t (1/2) x_t B_t^T ; y_t = h_t C_t
-    x = np.array([[[[1.0, 0.0], [0.0, 2.0]], [[1.0, 1.0], [3.0, 0.0]]]])  # [1,2,2,2]
-    dt = np.full((1, 2, 2), 0.5)
-    A = np.zeros(2)
-    B = np.array([[[[1.0, 0.0]], [[0.0, 1.0]]]])  # [1,2,1,2]
-    C = np.array([[[[1.0, 1.0]], [[2.0, 0.0]]]])
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+def test_hand_worked_rational_example():
+    # tests/golden/hand_worked_scalar_halving.json: P = N = 1, each step halves
+    # the state; values derived by hand in exact rationals (derivation inside)
+    g = _golden("hand_worked_scalar_halving.json")
+    inp = g["inputs"]
+    x = np.array(inp["x"], dtype=np.float64).reshape(1, 3, 1, 1)
+    dt = np.array(inp["dt"], dtype=np.float64).reshape(1, 3, 1)
+    assert inp["A"] == "-ln 2"
+    A = np.array([-np.log(2.0)])
+    B = np.array(inp["B"], dtype=np.float64).reshape(1, 3, 1, 1)
+    C = np.array(inp["C"], dtype=np.float64).reshape(1, 3, 1, 1)
+    D = np.array([inp["D"]])
+    h0 = np.full((1, 1, 1, 1), float(inp["init_state"]))
+    y, hT = ssd_recurrent(x, dt, A, B, C, D, h0)
+    for t, (num, den) in enumerate(g["expected"]["y"]):
+        assert y[0, t, 0, 0] == pytest.approx(float(Fraction(num, den)), rel=1e-15)
+    num, den = g["expected"]["final_state"]
+    assert hT[0, 0, 0, 0] == pytest.approx(float(Fraction(num, den)), rel=1e-15)
+
+
+def test_hand_worked_outer_product_example():
+    # tests/golden/hand_worked_outer_product.json: two heads of one group,
+    # P = N = 2, no decay; the state is a sum of outer products dt x B^T
+    g = _golden("hand_worked_outer_product.json")
+    inp, exp = g["inputs"], g["expected"]
+    x = np.array(inp["x"], dtype=np.float64)[None]                      # [1, t, head, p]
+    dt = np.full((1, 2, 2), float(inp["dt"]))
+    A = np.array(inp["A"], dtype=np.float64)
+    B = np.array(inp["B"], dtype=np.float64)[None, :, None, :]         # [1, t, 1, n]
+    C = np.array(inp["C"], dtype=np.float64)[None, :, None, :]
     y, hT = ssd_recurrent(x, dt, A, B, C, None, None)
-    # head 0: t0 h = .5*[1,0]^T[1,0] = [[.5,0],[0,0]]; y0 = [.5, 0]
-    #         t1 h += .5*[1,1]^T[0,1] -> [[.5,.5],[0,.5]]; y1 = h [2,0] = [1, 0]
-    # head 1: t0 h = .5*[0,2]^T[1,0] = [[0,0],[1,0]]; y0 = [0, 1]
-    #         t1 h += .5*[3,0]^T[0,1] -> [[0,1.5],[1,0]]; y1 = [0, 2]
-    assert np.allclose(y[0, :, 0], [[0.5, 0.0], [1.0, 0.0]], rtol=0, atol=1e-15)
-    assert np.allclose(y[0, :, 1], [[0.0, 1.0], [0.0, 2.0]], rtol=0, atol=1e-15)
-    assert np.allclose(hT[0, 0], [[0.5, 0.5], [0.0, 0.5]], rtol=0, atol=1e-15)
-    assert np.allclose(hT[0, 1], [[0.0, 1.5], [1.0, 0.0]], rtol=0, atol=1e-15)
+    assert np.allclose(y[0], np.array(exp["y"]), rtol=0, atol=1e-15)
+    assert np.allclose(hT[0], np.array(exp["final_state"]), rtol=0, atol=1e-15)
 
 
 @pytest.mark.parametrize("with_h0", [False, True])
