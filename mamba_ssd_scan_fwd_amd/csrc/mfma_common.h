@@ -50,8 +50,15 @@ __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cas
 // past `bytes` are discarded by the hardware's range check. This lets a
 // ragged tail be written with the same unconditional store sequence as a full
 // tile (no divergent branch around the stores).
+// `base` and `bytes` must be the same in every lane of the wavefront: they
+// are read from the first active lane, which keeps the descriptor in scalar
+// registers (otherwise every store becomes a loop over distinct descriptors).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 __device__ __forceinline__ void buffer_st8(const uint2& v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   typedef int v2i __attribute__((ext_vector_type(2)));
