@@ -47,14 +47,12 @@ template <int P, int N, int Q>
 struct ScanCfg {
   static constexpr int R = Q / 16;            // row groups of 16
   static constexpr int NM = Q / 32;           // 32-deep steps over the chunk positions
-  static constexpr int WAVES = 4;
+  static constexpr int RG = 2;                // row groups per wavefront (a zigzag pair)
+  static constexpr int WAVES = R / RG;        // 2, 4 or 8
   static constexpr int THREADS = WAVES * 64;
-  static constexpr int RG = R / WAVES;        // row groups per wavefront: 1, 2 or 4
   static constexpr int NTP = P / 16;          // p tiles
   static constexpr int NK = (N + 31) / 32;    // 32-deep steps over n
-  static constexpr int NPAIR = RG / 2;        // zigzag pairs of row groups
-  // off-diagonal G^T slots: pair m holds 16m + 7 tiles
-  static constexpr int NGT = RG == 1 ? R - 1 : 16 * (NPAIR * (NPAIR - 1) / 2) + 7 * NPAIR;
+  static constexpr int NGT = R - 1;           // off-diagonal G^T tiles per wavefront
   static constexpr int XBLK = (Q / 4) * (P / 8);  // 4x8 blocks of the x tile
   static constexpr int XPT = (XBLK + THREADS - 1) / THREADS;
   static constexpr int HCH = P * N / 8;           // 16-byte chunks of Hin
@@ -71,7 +69,8 @@ struct ScanCfg {
   static constexpr int C_BYTES = WAVES * RG * NK * 64 * 16;
   static constexpr int F_BYTES = 3 * Q * 4;
   static constexpr int BST_BYTES = Q * BPITCH * 2;
-  static constexpr int LIMIT = 160 * 1024;
+  // LDS per workgroup such that eight wavefronts (two per SIMD) share a CU
+  static constexpr int LIMIT = 160 * 1024 / (8 / WAVES);
   static constexpr bool USE_XN = X_BYTES + H_BYTES + F_BYTES + XN_BYTES <= LIMIT;
   static constexpr int BASE = X_BYTES + H_BYTES + F_BYTES + (USE_XN ? XN_BYTES : 0);
   static constexpr int REST = BASE > BST_BYTES ? BASE : BST_BYTES;
@@ -88,7 +87,7 @@ struct ScanCfg {
 };
 
 template <int Q>
-constexpr int kScanThreads = 256;
+constexpr int kScanThreads = 2 * Q;  // Q/32 wavefronts of two row groups each
 
 // Slot of lane (r16, g4) inside a 1 KB fragment block. Readers cover all 64
 // slots of a block, so any per-block permutation keeps their reads
@@ -97,7 +96,7 @@ __device__ __forceinline__ int xslot(int r16, int g4, int pt) { return 16 * g4 +
 __device__ __forceinline__ int hslot(int r16, int g4) { return 16 * g4 + ((r16 + 4 * g4) & 15); }
 
 template <int P, int N, int Q>
-__global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
+__global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu(2))) void chunk_scan_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const uint16_t* __restrict__ Cm, const float* __restrict__ D,
     const float* __restrict__ dA_cs, const float* __restrict__ dtc,
@@ -130,19 +129,17 @@ __global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
   const int64_t t0 = c * Q;
   const int rows = (int)(L - t0 < Q ? L - t0 : Q);
 
-  // row groups of this wavefront: pair m holds 8m + w and 8m + 7 - w
+  // row groups of this wavefront: w and R-1-w (w + 1 and R - w causal tiles)
   int rk[RG], ik[RG];
+  rk[0] = wave;
+  rk[1] = R - 1 - wave;
 #pragma unroll
-  for (int k = 0; k < RG; ++k) {
-    rk[k] = RG == 1 ? wave : 8 * (k >> 1) + ((k & 1) ? 7 - wave : wave);
-    ik[k] = 16 * rk[k] + r16;
-  }
-  // G^T slot of off-diagonal tile t of row group k (static for static k, t)
+  for (int k = 0; k < RG; ++k) ik[k] = 16 * rk[k] + r16;
+  // G^T slot of off-diagonal tile t of row group k, static for static k and
+  // t: row group 0 fills slots 0.. upwards, row group 1 fills R-2.. downwards
+  // (its tile t at slot R-2-t), and the two runs meet without overlap.
   auto gslot = [&](int k, int t) {
-    if (RG == 1) return t < R - 1 ? t : R - 2;
-    const int m = k >> 1;
-    const int base = 16 * (m * (m - 1) / 2) + 7 * m;
-    int sidx = (k & 1) ? base + 16 * m + 6 - t : base + t;
+    const int sidx = k == 0 ? t : R - 2 - t;
     return sidx < 0 ? 0 : (sidx > C::NGT - 1 ? C::NGT - 1 : sidx);
   };
 
@@ -177,23 +174,12 @@ __global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
       t = rk[k];
       return;
     }
-    if (RG == 1) {
+    if (e < rk[0]) {
       k = 0;
       t = e;
-      return;
-    }
-    int m = 0;
-#pragma unroll
-    for (int mm = 1; mm < C::NPAIR; ++mm)
-      if (e >= 16 * (mm * (mm - 1) / 2) + 7 * mm) m = mm;
-    const int base = 16 * (m * (m - 1) / 2) + 7 * m;
-    const int sp = e - base;
-    if (sp < rk[2 * m]) {
-      k = 2 * m;
-      t = sp;
     } else {
-      k = 2 * m + 1;
-      t = 16 * m + 6 - sp;
+      k = 1;
+      t = R - 2 - e;
     }
   };
   f32x4_t Gacc[C::NGT + RG];
@@ -409,23 +395,14 @@ __global__ __launch_bounds__(256) void chunk_scan_mfma_kernel(
     };
     auto lanef = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tv), l)); };
 
-    uint4 an[NTP];
-    float4 can = colf(0), cbn = colf(1);
-#pragma unroll
-    for (int pt = 0; pt < NTP; ++pt) an[pt] = xfrag(0, pt);
 #pragma unroll
     for (int kp = 0; kp < NM; ++kp) {
+      const int ta = 2 * kp, tb = 2 * kp + 1;
+      if (ta >= rk[1]) break;  // wavefront-uniform: row group 1 has the most tiles
       uint4 a[NTP];
 #pragma unroll
-      for (int pt = 0; pt < NTP; ++pt) a[pt] = an[pt];
-      const float4 ca = can, cb = cbn;
-      if (kp + 1 < NM) {  // compile-time: prefetch the next pair
-#pragma unroll
-        for (int pt = 0; pt < NTP; ++pt) an[pt] = xfrag(kp + 1, pt);
-        can = colf(2 * kp + 2);
-        cbn = colf(2 * kp + 3);
-      }
-      const int ta = 2 * kp, tb = 2 * kp + 1;
+      for (int pt = 0; pt < NTP; ++pt) a[pt] = xfrag(kp, pt);
+      const float4 ca = colf(ta), cb = colf(tb);
 #pragma unroll
       for (int k = 0; k < RG; ++k) {
         if (ta < rk[k]) {  // tile tb == r_k is the diagonal: excluded here
