@@ -9,8 +9,8 @@
 //         + exp(l_i) Hin_c C_i                                   (chunk output)
 //         + D_h x_i
 //
-// Mapping (one workgroup of four wavefronts, one per SIMD, per (b, c) and HB
-// heads of one B/C group):
+// Mapping: one workgroup per (b, c) and HB heads of one B/C group, with Q/32
+// wavefronts (eight at Q = 256: two per SIMD).
 //  * Products are computed transposed, Y^T[p][i], so the score tile never
 //    leaves registers: G^T[j][i] = B_j . C_i comes out of the matrix cores
 //    with each lane holding one column i and four consecutive rows j, which
@@ -18,26 +18,30 @@
 //    16-row tiles of G^T form one 32-deep operand; x fragments are read from
 //    LDS in the same j order).
 //  * G^T (the C B^T of the pages' dual form) depends only on the group: it is
-//    computed once per workgroup, from B staged through LDS, and reused by
-//    the HB heads; only the decay mask is per head. It is held as packed bf16
-//    (rounded once more after the decay is applied).
-//  * The R = Q/16 row groups of 16 rows are dealt out zigzag: with Q = 256,
-//    wavefront w owns row groups w, 7-w, 8+w, 15-w, whose causal tile counts
-//    add up to the same 34 for every wavefront. One x fragment read from LDS
-//    feeds all of a wavefront's row groups.
+//    computed once per workgroup and reused by the HB heads, held as packed
+//    bf16 in registers; only the decay mask is per head. The C fragments,
+//    which also feed the chunk-output product of every head, stay in
+//    registers too.
+//  * The R = Q/16 row groups of 16 rows are dealt out in pairs: wavefront w
+//    owns row groups w and R-1-w, w + 1 and R - w causal tiles, R + 1 for
+//    every wavefront.
 //  * The decay exp(l_i - l_j) is never formed from exp(l_i) * exp(-l_j)
-//    (that overflows); off-diagonal tiles use a factorisation through the
+//    (that overflows). Off-diagonal tiles use a factorisation through the
 //    tile boundaries, exp(l_i - l_r0) * exp(l_r0 - l_te) * exp(l_te - l_j),
-//    with r0 the first row of the row group and te the last row of the
-//    column tile, every factor <= 1; diagonal tiles are masked (j > i -> 0)
-//    before the exponential of l_i - l_j is taken.
-//  * Per head, x (transposed) and Hin are staged in LDS in fragment-major
-//    order: each lane's 16-byte operand fragment is contiguous, so a matrix
-//    core operand is one conflict-free 16-byte LDS read; a swizzle of the
-//    lane slot inside each 1 KB fragment block spreads the staging writes
-//    over the banks. x, Hin, l and dt of the next head are loaded into
-//    registers while the current head's products run.
-//  * The skip term D_h x_i is added in fp32 in the epilogue.
+//    r0 the first row of the row group and te the last row of the column
+//    tile, every factor <= 1; the three factors are tabulated per head when
+//    its inputs are staged. Diagonal tiles are masked (j > i -> 0) before the
+//    exponential of l_i - l_j is taken.
+//  * Per head, x (transposed), Hin and the decay tables are staged in LDS,
+//    double-buffered: the inputs of head h+1 are loaded into registers while
+//    the products of head h run (from one buffer) and are then written to
+//    the other buffer. One barrier per head. Operand tiles are fragment-major: each lane's 16-byte operand
+//    fragment is contiguous, so a matrix-core operand is one conflict-free
+//    16-byte LDS read; a swizzle of the lane slot inside each 1 KB fragment
+//    block spreads the staging writes over the banks.
+//  * The skip term D_h x_i is one more product on the diagonal tiles' x
+//    operand, against D_h times the identity (D_h split into two bf16 parts,
+//    so the term is exact to 16 bits of D_h in the fp32 accumulator).
 #include "mfma_common.h"
 
 namespace ssd {
@@ -47,9 +51,9 @@ template <int P, int N, int Q>
 struct ScanCfg {
   static constexpr int R = Q / 16;            // row groups of 16
   static constexpr int NM = Q / 32;           // 32-deep steps over the chunk positions
-  static constexpr int RG = 2;                // row groups per wavefront (a zigzag pair)
+  static constexpr int RG = 2;                // row groups per wavefront
   static constexpr int WAVES = R / RG;        // 2, 4 or 8
-  static constexpr int THREADS = WAVES * 64;
+  static constexpr int THREADS = WAVES * 64;  // = 2 Q
   static constexpr int NTP = P / 16;          // p tiles
   static constexpr int NK = (N + 31) / 32;    // 32-deep steps over n
   static constexpr int NGT = R - 1;           // off-diagonal G^T tiles per wavefront
@@ -57,37 +61,27 @@ struct ScanCfg {
   static constexpr int XPT = (XBLK + THREADS - 1) / THREADS;
   static constexpr int HCH = P * N / 8;           // 16-byte chunks of Hin
   static constexpr int HPT = (HCH + THREADS - 1) / THREADS;
-  static constexpr int FPT = (Q + THREADS - 1) / THREADS;
   static constexpr int NSL = (N + 127) / 128;     // n slices when staging B
   static constexpr int NSW = N < 128 ? N : 128;   // width of one slice
   static constexpr int BPITCH = NSW + 8;          // staged B row pitch (bf16)
-  // LDS carve-up (bytes)
+  // one staging buffer (bytes): x^T fragments, Hin fragments, then per
+  // position l, dt, (row factor, exp(l)), column factor, and the R x R
+  // table of tile-boundary factors
   static constexpr int X_BYTES = NTP * NM * 64 * 16;
   static constexpr int H_BYTES = NTP * NK * 64 * 16;
-  static constexpr int XN_PITCH = P + 8;          // natural-layout x row pitch (bf16)
-  static constexpr int XN_BYTES = Q * XN_PITCH * 2;
-  static constexpr int C_BYTES = WAVES * RG * NK * 64 * 16;
-  static constexpr int F_BYTES = 3 * Q * 4;
+  static constexpr int OFF_X = 0, OFF_H = X_BYTES, OFF_L = OFF_H + H_BYTES;
+  static constexpr int OFF_DT = OFF_L + Q * 4, OFF_RE = OFF_DT + Q * 4;
+  static constexpr int OFF_COL = OFF_RE + Q * 8, OFF_T = OFF_COL + Q * 4;
+  static constexpr int BUF = OFF_T + R * R * 4;
   static constexpr int BST_BYTES = Q * BPITCH * 2;
-  // LDS per workgroup such that eight wavefronts (two per SIMD) share a CU
-  static constexpr int LIMIT = 160 * 1024 / (8 / WAVES);
-  static constexpr bool USE_XN = X_BYTES + H_BYTES + F_BYTES + XN_BYTES <= LIMIT;
-  static constexpr int BASE = X_BYTES + H_BYTES + F_BYTES + (USE_XN ? XN_BYTES : 0);
-  static constexpr int REST = BASE > BST_BYTES ? BASE : BST_BYTES;
-  static constexpr bool PARK_C = C_BYTES + REST <= LIMIT;
-  static constexpr int C_SZ = PARK_C ? C_BYTES : 0;
-  static constexpr int TOTAL = C_SZ + REST;
-  // offsets: [C frags][x frags][Hin frags][l, dt, col][x natural]; the B
-  // staging area aliases everything after the C fragments (it is used
-  // before any of those buffers)
-  static constexpr int OFF_C = 0;
-  static constexpr int OFF_X = C_SZ, OFF_H = OFF_X + X_BYTES, OFF_F = OFF_H + H_BYTES;
-  static constexpr int OFF_XN = OFF_F + F_BYTES;
-  static constexpr int OFF_B = C_SZ;
+  // two buffers when they fit the LDS, else one (and a second barrier per head)
+  static constexpr bool DB = 2 * BUF <= 160 * 1024;
+  static constexpr int NBUF = DB ? 2 : 1;
+  static constexpr int TOTAL = NBUF * BUF > BST_BYTES ? NBUF * BUF : BST_BYTES;
 };
 
 template <int Q>
-constexpr int kScanThreads = 2 * Q;  // Q/32 wavefronts of two row groups each
+constexpr int kScanThreads = 2 * Q;
 
 // Slot of lane (r16, g4) inside a 1 KB fragment block. Readers cover all 64
 // slots of a block, so any per-block permutation keeps their reads
@@ -105,14 +99,6 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   using C = ScanCfg<P, N, Q>;
   constexpr int R = C::R, NM = C::NM, RG = C::RG, NTP = C::NTP, NK = C::NK;
   __shared__ __align__(16) unsigned char lds[C::TOTAL];
-  uint4* sXf = reinterpret_cast<uint4*>(lds + C::OFF_X);   // x^T fragments [pt][m][slot]
-  uint4* sHf = reinterpret_cast<uint4*>(lds + C::OFF_H);   // Hin fragments [pt][ks][slot]
-  float* sL = reinterpret_cast<float*>(lds + C::OFF_F);    // l_j
-  float* sDt = sL + Q;                                     // dt_j
-  float* sCol = sL + 2 * Q;                                // exp(l_{16*floor(j/16)+15} - l_j) * dt_j
-  uint16_t* sXn = reinterpret_cast<uint16_t*>(lds + C::OFF_XN);  // x [j][p] (when it fits)
-  uint4* sCf = reinterpret_cast<uint4*>(lds + C::OFF_C);   // C fragments per wavefront (when parked)
-  uint16_t* sB = reinterpret_cast<uint16_t*>(lds + C::OFF_B);  // staged B slice [j][n] (setup only)
 
   const int nhg = H / HB;
   int64_t bid = xcd_local_order(blockIdx.x, gridDim.x);
@@ -129,7 +115,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   const int64_t t0 = c * Q;
   const int rows = (int)(L - t0 < Q ? L - t0 : Q);
 
-  // row groups of this wavefront: w and R-1-w (w + 1 and R - w causal tiles)
+  // row groups of this wavefront: w and R-1-w
   int rk[RG], ik[RG];
   rk[0] = wave;
   rk[1] = R - 1 - wave;
@@ -143,51 +129,50 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
     return sidx < 0 ? 0 : (sidx > C::NGT - 1 ? C::NGT - 1 : sidx);
   };
 
-  // ---- C fragments of the row groups (B operand: column i, 8 consecutive n) ----
+  // ---- C fragments of the row groups (B operand: column i, 8 consecutive n),
+  // kept in registers: they also feed the chunk-output product of every head.
+  // Rows past the end re-read the last row (their outputs are never stored).
   bf16x8_t Cr[RG][NK];
+  {
+    const uint16_t* cbase = Cm + ((b * L + t0) * G + g) * N;
 #pragma unroll
-  for (int k = 0; k < RG; ++k)
+    for (int k = 0; k < RG; ++k) {
+      const uint32_t coff = (uint32_t)((min(ik[k], rows - 1) * G * N + (8 * g4 < N ? 8 * g4 : 0)) * 2);
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      const int n = 32 * ks + 8 * g4;
-      const bool ok = n < N && ik[k] < rows;
-      Cr[k][ks] = as_bf16x8(ld16_keep(Cm + ((b * L + t0 + min(ik[k], rows - 1)) * G + g) * N + (n < N ? n : 0), ok));
+      for (int ks = 0; ks < NK; ++ks) {
+        const uint4 v = ld16_at(cbase, coff + (32 * ks < N ? 64 * ks : 0));
+        Cr[k][ks] = as_bf16x8(32 * ks + 8 * g4 < N ? v : make_uint4(0, 0, 0, 0));
+      }
     }
-
-  // C fragments parked in this wavefront's LDS region (when they fit): the
-  // G^T set-up below and every head's chunk-output product read them there.
-  uint4* cpark = sCf + wave * (RG * NK * 64);
-  if constexpr (C::PARK_C) {
-#pragma unroll
-    for (int k = 0; k < RG; ++k)
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks) cpark[(k * NK + ks) * 64 + lane] = __builtin_bit_cast(uint4, Cr[k][ks]);
   }
 
   // ---- G^T = B C^T for every tile a row group needs, B staged through LDS.
-  // Slot e < NGT holds an off-diagonal tile; slot NGT + k the diagonal tile of
-  // row group k. Which (row group, tile) a slot holds depends on the
-  // wavefront only, so the loop over slots is static and branch-free. ----
-  auto slot_rg_tile = [&](int e, int& k, int& t) {
+  // Slot e < NGT holds an off-diagonal tile, slot NGT + k the diagonal tile
+  // of row group k; the loop over slots is static and branch-free. ----
+  uint16_t* sB = reinterpret_cast<uint16_t*>(lds);
+  f32x4_t Gacc[C::NGT + RG];
+#pragma unroll
+  for (int e = 0; e < C::NGT + RG; ++e) Gacc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int srow[C::NGT + RG], sk[C::NGT + RG];
+#pragma unroll
+  for (int e = 0; e < C::NGT + RG; ++e) {
+    int k, t;
     if (e >= C::NGT) {
       k = e - C::NGT;
       t = rk[k];
-      return;
-    }
-    if (e < rk[0]) {
+    } else if (e < rk[0]) {
       k = 0;
       t = e;
     } else {
       k = 1;
       t = R - 2 - e;
     }
-  };
-  f32x4_t Gacc[C::NGT + RG];
-#pragma unroll
-  for (int e = 0; e < C::NGT + RG; ++e) Gacc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    srow[e] = 16 * t + r16;
+    sk[e] = k;
+  }
 #pragma unroll
   for (int sl = 0; sl < C::NSL; ++sl) {
-    __syncthreads();
+    if (sl > 0) __syncthreads();
     constexpr int CH = Q * C::NSW / 8;  // 16-byte chunks of the slice
 #pragma unroll
     for (int q = 0; q < (CH + C::THREADS - 1) / C::THREADS; ++q) {
@@ -199,15 +184,6 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
       }
     }
     __syncthreads();
-    int srow[C::NGT + RG], sk[C::NGT + RG];
-#pragma unroll
-    for (int e = 0; e < C::NGT + RG; ++e) {
-      int k, t;
-      slot_rg_tile(e, k, t);
-      // slots whose tile a row group does not need (RG == 1 tail) stay unused
-      srow[e] = 16 * (t < 0 ? 0 : (t > R - 1 ? R - 1 : t)) + r16;
-      sk[e] = k;
-    }
 #pragma unroll
     for (int kk = 0; kk < C::NSW / 32 + (C::NSW < 32 ? 1 : 0); ++kk) {
       const int ks = sl * 4 + kk;
@@ -216,15 +192,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
       for (int e = 0; e < C::NGT + RG; ++e) {
         const bf16x8_t bfrag =
             as_bf16x8(nl < C::NSW ? ld16(sB + srow[e] * C::BPITCH + nl) : make_uint4(0, 0, 0, 0));
-        bf16x8_t cfrag;
-        if constexpr (C::PARK_C) {
-          cfrag = as_bf16x8(cpark[(sk[e] * NK + ks) * 64 + lane]);
-        } else {
-          cfrag = Cr[0][ks];
-#pragma unroll
-          for (int k2 = 1; k2 < RG; ++k2)
-            if (sk[e] == k2) cfrag = Cr[k2][ks];
-        }
+        const bf16x8_t cfrag = sk[e] == 0 ? Cr[0][ks] : Cr[1][ks];
         Gacc[e] = mfma_16x16x32(bfrag, cfrag, Gacc[e]);
       }
     }
@@ -237,47 +205,50 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   for (int k = 0; k < RG; ++k)
     Gd[k] = make_uint2(pack_bf16x2(Gacc[C::NGT + k][0], Gacc[C::NGT + k][1]),
                        pack_bf16x2(Gacc[C::NGT + k][2], Gacc[C::NGT + k][3]));
-  __syncthreads();  // the B staging area is reused below
+  __syncthreads();  // the B staging area becomes the two head buffers
 
-  // ---- per-head inputs: global -> registers (one head ahead) -> LDS ----
+  // ---- per-head inputs: global -> registers (two heads ahead) -> LDS ----
   uint4 xr[C::XPT][4];
   uint4 hr[C::HPT];
-  float lpre[C::FPT], dpre[C::FPT];
-  float dnext = 0.f;
+  float lpre = 0.f, dpre = 0.f, tl1 = 0.f, tl2 = 0.f;
+  // thread e < R*R tabulates exp(l_{16 r} - l_{16 t + 15}), r = e / R, t = e % R.
+  // Staging and fetching use an opaque copy of the thread index, so their
+  // per-thread addresses are not kept live through the products.
+  // Every load is issued unconditionally, from a clamped (always valid)
+  // index where a thread has nothing to fetch: a fixed count of memory
+  // operations lets each wait cover exactly the loads it needs.
   auto fetch_head = [&](int h) {
-    dnext = D != nullptr ? D[h] : 0.f;
+    const int tid = opaque(threadIdx.x);
+    const uint16_t* xh = x + ((b * L + t0) * H + h) * P;
 #pragma unroll
     for (int k = 0; k < C::XPT; ++k) {
-      const int bi = tid + k * C::THREADS;
-      if (bi < C::XBLK) {
-        const int cb = bi % (P / 8), jb = bi / (P / 8);
+      const int bi = min(tid + k * C::THREADS, C::XBLK - 1);
+      const int cb = bi % (P / 8), jb = bi / (P / 8);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          // raw load (clamped row, always in bounds); rows past the end are
-          // zeroed when staged, so nothing here waits for the data
-          const int j = 4 * jb + rr;
-          xr[k][rr] = ld16(x + ((b * L + t0 + min(j, rows - 1)) * H + h) * P + 8 * cb);
-        }
+      for (int rr = 0; rr < 4; ++rr) {
+        // raw load (clamped row, always in bounds); rows past the end are
+        // zeroed when staged, so nothing here waits for the data
+        const int j = 4 * jb + rr;
+        xr[k][rr] = ld16_at(xh, (uint32_t)((min(j, rows - 1) * H * P + 8 * cb) * 2));
       }
     }
     const uint16_t* hin = states + ((b * H + h) * nc + c) * (int64_t)P * N;
 #pragma unroll
-    for (int k = 0; k < C::HPT; ++k) {
-      const int ci = tid + k * C::THREADS;
-      if (ci < C::HCH) hr[k] = ld16(hin + 8 * ci);
-    }
+    for (int k = 0; k < C::HPT; ++k) hr[k] = ld16_at(hin, (uint32_t)(16 * min(tid + k * C::THREADS, C::HCH - 1)));
     const float* lc = dA_cs + ((b * H + h) * nc + c) * Q;
     const float* dc = dtc + ((b * H + h) * nc + c) * Q;
-#pragma unroll
-    for (int k = 0; k < C::FPT; ++k) {
-      const int i = tid + k * C::THREADS;
-      if (i < Q) {
-        lpre[k] = lc[i];
-        dpre[k] = dc[i];
-      }
-    }
+    const int tq = min(tid, Q - 1), te = min(tid, R * R - 1);
+    lpre = ld4f_at(lc, 4 * tq);
+    dpre = ld4f_at(dc, 4 * tq);
+    tl1 = ld4f_at(lc, 64 * (te / R));
+    tl2 = ld4f_at(lc, 64 * (te % R) + 60);
   };
-  auto stage_head = [&]() {
+  auto stage_head = [&](unsigned char* buf) {
+    const int tid = opaque(threadIdx.x);
+    const int lane = tid & 63;
+    const int tr = tid / R, tt = tid % R;
+    uint4* sXf = reinterpret_cast<uint4*>(buf + C::OFF_X);
+    uint4* sHf = reinterpret_cast<uint4*>(buf + C::OFF_H);
 #pragma unroll
     for (int k = 0; k < C::XPT; ++k) {
       const int bi = tid + k * C::THREADS;
@@ -300,10 +271,6 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
           uint4* blk = sXf + (pt * NM + m) * 64;
           reinterpret_cast<uint2*>(blk + xslot(p & 15, jg, pt))[half] = make_uint2(w0, w1);
         }
-        if constexpr (C::USE_XN) {
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) st16(sXn + (j0 + rr) * C::XN_PITCH + 8 * cb, xr[k][rr]);
-        }
       }
     }
 #pragma unroll
@@ -314,65 +281,68 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
         sHf[((p >> 4) * NK + (n0 >> 5)) * 64 + hslot(p & 15, (n0 >> 3) & 3)] = hr[k];
       }
     }
-#pragma unroll
-    for (int k = 0; k < C::FPT; ++k) {
-      const int i = tid + k * C::THREADS;
-      if (i < Q) {  // Q is a multiple of 64: whole wavefronts take this branch
-        const float lend = __shfl(lpre[k], lane | 15, 64);  // l at the end of the 16-row tile
-        sL[i] = lpre[k];
-        sDt[i] = dpre[k];
-        sCol[i] = __expf(lend - lpre[k]) * dpre[k];
-      }
+    float* sL = reinterpret_cast<float*>(buf + C::OFF_L);
+    float* sDt = reinterpret_cast<float*>(buf + C::OFF_DT);
+    float2* sRE = reinterpret_cast<float2*>(buf + C::OFF_RE);
+    float* sCol = reinterpret_cast<float*>(buf + C::OFF_COL);
+    float* sT = reinterpret_cast<float*>(buf + C::OFF_T);
+    if (tid < Q) {  // Q is a multiple of 64: whole wavefronts take this branch
+      const float lbeg = __shfl(lpre, lane & ~15, 64);  // l at the start of the 16-row tile
+      const float lend = __shfl(lpre, lane | 15, 64);   // l at its end
+      sL[tid] = lpre;
+      sDt[tid] = dpre;
+      sRE[tid] = make_float2(__expf(lpre - lbeg), __expf(lpre));
+      sCol[tid] = __expf(lend - lpre) * dpre;
     }
+    if (tid < R * R) sT[tid] = tt < tr ? __expf(tl1 - tl2) : 0.f;
   };
 
   if (N < 32) {  // fragment slots past N stay zero for the whole workgroup
-    for (int e = tid; e < NTP * NK * 64; e += C::THREADS) sHf[e] = make_uint4(0, 0, 0, 0);
+    for (int e = tid; e < NTP * NK * 64; e += C::THREADS) {
+#pragma unroll
+      for (int nb = 0; nb < C::NBUF; ++nb)
+        reinterpret_cast<uint4*>(lds + nb * C::BUF + C::OFF_H)[e] = make_uint4(0, 0, 0, 0);
+    }
   }
-  // The loop is rotated by hand: head h's inputs are staged at the end of
-  // iteration h-1, after its stores, so the only path into each staging step
-  // has the same loads and stores outstanding and the wait for the prefetched
-  // inputs does not also wait for the y stores that follow them.
+  const int hlast = h0 + HB - 1;
   fetch_head(h0);
-  stage_head();
+  stage_head(lds);
   __syncthreads();
+
   for (int hh = 0; hh < HB; ++hh) {
     const int h = h0 + hh;
-    const float dh = dnext;
-    // in flight during this head's products (the last head re-reads itself,
-    // which keeps the memory-operation count the same on every iteration)
-    fetch_head(hh + 1 < HB ? h + 1 : h);
+    const unsigned char* buf = lds + (C::DB ? (hh & 1) * C::BUF : 0);
+    const uint4* sXf = reinterpret_cast<const uint4*>(buf + C::OFF_X);
+    const uint4* sHf = reinterpret_cast<const uint4*>(buf + C::OFF_H);
+    const float* sL = reinterpret_cast<const float*>(buf + C::OFF_L);
+    const float* sDt = reinterpret_cast<const float*>(buf + C::OFF_DT);
+    const float2* sRE = reinterpret_cast<const float2*>(buf + C::OFF_RE);
+    const float* sCol = reinterpret_cast<const float*>(buf + C::OFF_COL);
+    const float* sT = reinterpret_cast<const float*>(buf + C::OFF_T);
 
-    // per-wavefront decay scalars
-    float lk[RG], rf[RG], el[RG];
+    // per-lane decay factors: exp(l_i - l_r0), exp(l_i), and (lanes 16k + t)
+    // the tile-boundary factor exp(l_r0 - l_te) of row group k, column tile t
+    float rf[RG], el[RG];
 #pragma unroll
     for (int k = 0; k < RG; ++k) {
-      lk[k] = sL[ik[k]];
-      el[k] = __expf(lk[k]);
-      rf[k] = __expf(lk[k] - sL[16 * rk[k]]);
+      const float2 re = sRE[ik[k]];
+      rf[k] = re.x;
+      el[k] = re.y;
     }
-    float tv = 0.f;  // lane 16k + t: exp(l_{16 r_k} - l_{16t+15}) for t < r_k
-    {
-      const int k = lane >> 4, t = lane & 15;
-      int rr = -1;
-#pragma unroll
-      for (int kk = 0; kk < RG; ++kk)
-        if (kk == k) rr = rk[kk];
-      if (t < rr) tv = __expf(sL[16 * rr] - sL[16 * t + 15]);
-    }
+    const int tcol = lane & 15;
+    const float tv = lane < 16 * RG && tcol < R ? sT[rk[lane >> 4] * R + tcol] : 0.f;
+    auto lanef = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tv), l)); };
+
     f32x4_t acc[RG][NTP];
     // chunk output: Y^T[p][i] = sum_n Hin[p][n] C_i[n], scaled by exp(l_i)
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
-      bf16x8_t ck[RG];
-#pragma unroll
-      for (int k = 0; k < RG; ++k) ck[k] = C::PARK_C ? as_bf16x8(cpark[(k * NK + ks) * 64 + lane]) : Cr[k][ks];
 #pragma unroll
       for (int pt = 0; pt < NTP; ++pt) {
         const bf16x8_t a = as_bf16x8(sHf[(pt * NK + ks) * 64 + hslot(r16, g4)]);
 #pragma unroll
         for (int k = 0; k < RG; ++k)
-          acc[k][pt] = mfma_16x16x32(a, ck[k], ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[k][pt]);
+          acc[k][pt] = mfma_16x16x32(a, Cr[k][ks], ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[k][pt]);
       }
     }
 #pragma unroll
@@ -380,8 +350,15 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int pt = 0; pt < NTP; ++pt) acc[k][pt] *= el[k];
 
-    // intra-chunk, off-diagonal tiles: all row groups walk the same pairs of
-    // column tiles (2kp, 2kp+1), so one x fragment feeds every row group.
+    // loads for the next head, in flight during this head's products (the
+    // last head re-reads itself, so every iteration has the same sequence of
+    // memory operations and the wait before staging covers exactly these
+    // loads); issued here rather than at the barrier, where every wavefront
+    // would queue its loads at once
+    fetch_head(min(h + 1, hlast));
+
+    // intra-chunk, off-diagonal tiles: both row groups walk the same pairs of
+    // column tiles (2kp, 2kp+1), so one x fragment feeds both.
     // All factors are <= 1: exp(l_i - l_r0) * exp(l_r0 - l_te) * c_j.
     auto xfrag = [&](int m, int pt) { return sXf[(pt * NM + m) * 64 + xslot(r16, g4, pt)]; };
     auto colf = [&](int t) { return *reinterpret_cast<const float4*>(sCol + 16 * t + 4 * g4); };
@@ -393,12 +370,13 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
       return as_bf16x8(make_uint4(pack_bf16x2(w0, w1), pack_bf16x2(w2, w3), pack_bf16x2(w4, w5),
                                   pack_bf16x2(w6, w7)));
     };
-    auto lanef = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tv), l)); };
-
 #pragma unroll
     for (int kp = 0; kp < NM; ++kp) {
       const int ta = 2 * kp, tb = 2 * kp + 1;
       if (ta >= rk[1]) break;  // wavefront-uniform: row group 1 has the most tiles
+      // keep each pair's loads next to its products (no hoisting of every
+      // pair's operands, which would exhaust the registers)
+      __builtin_amdgcn_sched_barrier(0);
       uint4 a[NTP];
 #pragma unroll
       for (int pt = 0; pt < NTP; ++pt) a[pt] = xfrag(kp, pt);
@@ -415,6 +393,22 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
       }
     }
 
+    // The skip term D_h x_i rides on the diagonal tiles' x operand: an extra
+    // product with D_h times the identity, D_h split into two bf16 parts
+    // (hi + lo carries 16 bits of D_h; bf16 x times either part is exact in
+    // the fp32 accumulator). Lane (i, g4) holds the one identity entry
+    // j == i when 4 g4 <= i < 4 g4 + 4.
+    const float dh = D != nullptr ? D[h] : 0.f;
+    const uint32_t dhi_bits = pack_bf16x2(dh, 0.f) & 0xffffu;
+    const uint32_t dlo_bits = pack_bf16x2(dh - bf16_lo(dhi_bits), 0.f) & 0xffffu;
+    const int dq = r16 - 4 * g4;
+    const bool don = dq >= 0 && dq < 4;
+    auto ident = [&](uint32_t bits, bool upper) {
+      const uint32_t wv = don ? bits << (16 * (dq & 1)) : 0u;
+      const uint32_t w0 = (dq >> 1) == 0 ? wv : 0u, w1 = (dq >> 1) == 1 ? wv : 0u;
+      return as_bf16x8(upper ? make_uint4(0, 0, w0, w1) : make_uint4(w0, w1, 0, 0));
+    };
+
     // diagonal tiles: mask (j > i) before the exponential
 #pragma unroll
     for (int k = 0; k < RG; ++k) {
@@ -422,6 +416,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
       const int j0 = 16 * t + 4 * g4;
       const float4 lj = *reinterpret_cast<const float4*>(sL + j0);
       const float4 dj = *reinterpret_cast<const float4*>(sDt + j0);
+      const float li = sL[i];
       const float ljv[4] = {lj.x, lj.y, lj.z, lj.w};
       const float djv[4] = {dj.x, dj.y, dj.z, dj.w};
       const uint2 gp = Gd[k];
@@ -430,59 +425,49 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int jq = j0 + q;
-        const float e = __expf(jq <= i ? lk[k] - ljv[q] : -INFINITY);
+        const float e = __expf(jq <= i ? li - ljv[q] : -INFINITY);
         w[q] = gv[q] * e * djv[q];
       }
       const uint32_t w01 = pack_bf16x2(w[0], w[1]), w23 = pack_bf16x2(w[2], w[3]);
       const bool upper = t & 1;  // which half of the 32-deep pair holds tile t
       const bf16x8_t wop = as_bf16x8(upper ? make_uint4(0, 0, w01, w23) : make_uint4(w01, w23, 0, 0));
+      const bf16x8_t dop_hi = ident(dhi_bits, upper), dop_lo = ident(dlo_bits, upper);
 #pragma unroll
-      for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(as_bf16x8(xfrag(t >> 1, pt)), wop, acc[k][pt]);
+      for (int pt = 0; pt < NTP; ++pt) {
+        const bf16x8_t a = as_bf16x8(xfrag(t >> 1, pt));
+        acc[k][pt] = mfma_16x16x32(a, wop, acc[k][pt]);
+        acc[k][pt] = mfma_16x16x32(a, dop_hi, acc[k][pt]);
+        acc[k][pt] = mfma_16x16x32(a, dop_lo, acc[k][pt]);
+      }
     }
 
-    // epilogue: + D_h x_i in fp32, store; lane holds Y^T[p = 16pt + 4g4 + q][i].
-    // Rows past the end of the sequence fall outside the buffer range and are
-    // dropped, so the store sequence is the same for every chunk.
+    // epilogue: store. Rows past the end of the sequence fall outside the
+    // buffer range and are dropped, so the store sequence is the same for
+    // every chunk.
     uint16_t* ybase = y + ((b * L + t0) * H + h) * P;
     const __amdgpu_buffer_rsrc_t yr = buffer_range(ybase, (uint32_t)(((rows - 1) * (int64_t)H + 1) * P * 2));
 #pragma unroll
     for (int k = 0; k < RG; ++k) {
-      const int i = ik[k];
-      const uint32_t rowoff = (uint32_t)(i * (int64_t)H * P * 2);
+      const uint32_t rowoff = (uint32_t)(ik[k] * (int64_t)H * P * 2);
 #pragma unroll
       for (int pt = 0; pt < NTP; ++pt) {
         const int p = 16 * pt + 4 * g4;
-        float xv[4];
-        if constexpr (C::USE_XN) {
-          const uint2 xx = *reinterpret_cast<const uint2*>(sXn + i * C::XN_PITCH + p);
-          xv[0] = bf16_lo(xx.x); xv[1] = bf16_hi(xx.x); xv[2] = bf16_lo(xx.y); xv[3] = bf16_hi(xx.y);
-        } else {
-          const unsigned char* xb = reinterpret_cast<const unsigned char*>(sXf);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int pq = p + q;
-            const int o = (((pq >> 4) * NM + (i >> 5)) * 64 + xslot(pq & 15, (i >> 2) & 3, pq >> 4)) * 16 +
-                          ((i >> 4) & 1) * 8 + (i & 3) * 2;
-            xv[q] = __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(xb + o)) << 16);
-          }
-        }
         const f32x4_t v = acc[k][pt];
-        const float o0 = fmaf(dh, xv[0], v[0]), o1 = fmaf(dh, xv[1], v[1]);
-        const float o2 = fmaf(dh, xv[2], v[2]), o3 = fmaf(dh, xv[3], v[3]);
-        buffer_st8(make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)), yr, rowoff + p * 2);
+        buffer_st8(make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])), yr, rowoff + p * 2);
       }
     }
-    __syncthreads();  // every wavefront is done with this head's LDS tiles
-    if (hh + 1 < HB) {
-      stage_head();
-      __syncthreads();
-    }
+
+    // inputs of the next head into the other buffer (nobody reads it during
+    // this head)
+    if constexpr (!C::DB) __syncthreads();  // one buffer: everyone is done with it
+    if (hh + 1 < HB) stage_head(lds + (C::DB ? ((hh + 1) & 1) * C::BUF : 0));
+    __syncthreads();
   }
 }
 
 // Heads per workgroup: a divisor of the heads in one B/C group, at most 8,
-// as large as keeps at least two workgroups per compute unit (the G^T set-up
-// is amortised over more heads; one workgroup fills a compute unit's LDS).
+// as large as keeps enough workgroups to fill the chip (the G^T set-up is
+// amortised over more heads).
 int pick_heads_per_wg(const Plan& p) {
   const int64_t hpg = p.H / p.G;
   const int64_t base = p.batch * p.nc * p.H;

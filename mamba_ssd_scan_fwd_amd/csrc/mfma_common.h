@@ -46,6 +46,19 @@ __device__ __forceinline__ uint4 ld16_keep(const void* p, bool keep) {
 }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// Loads at a wavefront-uniform base plus a 32-bit per-lane byte offset: the
+// address takes one vector register (scalar base + vector offset) instead of
+// a 64-bit pointer per lane.
+__device__ __forceinline__ uint4 ld16_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(base) + byte_off);
+}
+__device__ __forceinline__ uint2 ld8_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const uint2*>(reinterpret_cast<const unsigned char*>(base) + byte_off);
+}
+__device__ __forceinline__ float ld4f_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(base) + byte_off);
+}
+
 // A raw buffer resource covering [base, base + bytes): stores at offsets at or
 // past `bytes` are discarded by the hardware's range check. This lets a
 // ragged tail be written with the same unconditional store sequence as a full
@@ -93,6 +106,14 @@ __device__ __forceinline__ int64_t xcd_local_order(int64_t bid, int64_t grid) {
   constexpr int kXcds = 8;
   if (grid % kXcds != 0) return bid;
   return (bid % kXcds) * (grid / kXcds) + bid / kXcds;
+}
+
+// The same value, but opaque to the optimiser: addresses derived from it are
+// recomputed where they are used instead of being hoisted out of a loop and
+// kept live in registers for its whole length.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // Element e (0..7) of a row of eight bf16 held in a uint4, as fp32.
