@@ -432,13 +432,16 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
       const bool upper = t & 1;  // which half of the 32-deep pair holds tile t
       const bf16x8_t wop = as_bf16x8(upper ? make_uint4(0, 0, w01, w23) : make_uint4(w01, w23, 0, 0));
       const bf16x8_t dop_hi = ident(dhi_bits, upper), dop_lo = ident(dlo_bits, upper);
+      bf16x8_t a[NTP];
 #pragma unroll
-      for (int pt = 0; pt < NTP; ++pt) {
-        const bf16x8_t a = as_bf16x8(xfrag(t >> 1, pt));
-        acc[k][pt] = mfma_16x16x32(a, wop, acc[k][pt]);
-        acc[k][pt] = mfma_16x16x32(a, dop_hi, acc[k][pt]);
-        acc[k][pt] = mfma_16x16x32(a, dop_lo, acc[k][pt]);
-      }
+      for (int pt = 0; pt < NTP; ++pt) a[pt] = as_bf16x8(xfrag(t >> 1, pt));
+      // three rounds over the p tiles, so consecutive products are independent
+#pragma unroll
+      for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(a[pt], wop, acc[k][pt]);
+#pragma unroll
+      for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(a[pt], dop_hi, acc[k][pt]);
+#pragma unroll
+      for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(a[pt], dop_lo, acc[k][pt]);
     }
 
     // epilogue: store. Rows past the end of the sequence fall outside the
@@ -472,7 +475,7 @@ int pick_heads_per_wg(const Plan& p) {
   const int64_t hpg = p.H / p.G;
   const int64_t base = p.batch * p.nc * p.H;
   int hb = 1;
-  while (hb < 8 && hpg % (hb * 2) == 0 && base / (hb * 2) >= 512) hb *= 2;
+  while (hb < 16 && hpg % (hb * 2) == 0 && base / (hb * 2) >= 256) hb *= 2;
   return hb;
 }
 
