@@ -220,13 +220,13 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 }
 
 // Heads per workgroup: a divisor of the heads in one B/C group, at most 8,
-// as large as keeps the grid at >= 1024 workgroups (two resident per compute
-// unit, two rounds).
+// as large as keeps the grid at >= 512 workgroups (two resident per compute
+// unit; the B^T staging is amortised over more heads).
 int pick_heads_per_wg(const Plan& p, int nnb) {
   const int64_t hpg = p.H / p.G;
   const int64_t base = p.batch * p.nc * nnb * p.H;
   int hb = 1;
-  while (hb < 8 && hpg % (hb * 2) == 0 && base / (hb * 2) >= 1024) hb *= 2;
+  while (hb < 8 && hpg % (hb * 2) == 0 && base / (hb * 2) >= 512) hb *= 2;
   return hb;
 }
 
