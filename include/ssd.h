@@ -145,6 +145,15 @@ SSD_API ssd_status_t ssd_chunk_state(const ssd_desc_t* desc, const void* x, cons
                              const float* dA_cumsum, const float* dt_chunked,
                              void* states, void* stream);
 
+/* Steps 1 and 2 in one launch: the chunk cumsum of dt*A and the local
+ * chunk states. Writes the same dA_cumsum, dt_chunked and states, bit for
+ * bit, as ssd_chunk_cumsum followed by ssd_chunk_state; ssd_forward uses it.
+ * Same arguments, layouts and alignment as those two calls. */
+SSD_API ssd_status_t ssd_cumsum_chunk_state(const ssd_desc_t* desc, const void* x, const void* B,
+                                    const float* dt, const float* A,
+                                    float* dA_cumsum, float* dt_chunked,
+                                    void* states, void* stream);
+
 /* Step 3, inter-chunk state passing (same section: the per-chunk states are
  * recombined). In place over `states`: on return states[b,h,c] holds the
  * state entering chunk c,  H_{-1} = init_state (or 0),

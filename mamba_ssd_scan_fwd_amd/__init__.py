@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     chunk_cumsum,
     chunk_scan,
     chunk_state,
+    cumsum_chunk_state,
     effective_chunk_size,
     forward,
     lib_path,

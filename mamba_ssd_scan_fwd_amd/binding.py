@@ -25,6 +25,7 @@ __all__ = [
     "forward",
     "chunk_cumsum",
     "chunk_state",
+    "cumsum_chunk_state",
     "state_passing",
     "chunk_scan",
     "EXPORTED_SYMBOLS",
@@ -40,6 +41,7 @@ EXPORTED_SYMBOLS = (
     "ssd_forward",
     "ssd_chunk_cumsum",
     "ssd_chunk_state",
+    "ssd_cumsum_chunk_state",
     "ssd_state_passing",
     "ssd_chunk_scan",
 )
@@ -104,6 +106,8 @@ def load_library():
         lib.ssd_chunk_cumsum.restype = ctypes.c_int
         lib.ssd_chunk_state.argtypes = [dp, vp, vp, vp, vp, vp, vp]
         lib.ssd_chunk_state.restype = ctypes.c_int
+        lib.ssd_cumsum_chunk_state.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.ssd_cumsum_chunk_state.restype = ctypes.c_int
         lib.ssd_state_passing.argtypes = [dp, vp, vp, vp, vp, vp]
         lib.ssd_state_passing.restype = ctypes.c_int
         lib.ssd_chunk_scan.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -266,6 +270,25 @@ def chunk_state(x, B, dA_cumsum, dt_chunked, *, chunk_size=0, stream=None):
                                           _ptr(dt_chunked), _ptr(states), _stream(stream, dev)),
            "ssd_chunk_state")
     return states
+
+
+def cumsum_chunk_state(x, B, dt, A, *, chunk_size=0, stream=None):
+    """Steps 1 and 2 in one call. Returns (dA_cumsum, dt_chunked, states)."""
+    dev = x.device
+    _need(x, "x", device=dev)
+    _need(B, "B", x.dtype, dev)
+    desc = _desc_from(x, B, chunk_size)
+    q, nc = _chunk_shape(desc)
+    bsz, L, H, P = x.shape
+    _need(dt, "dt", torch.float32, dev, (bsz, L, H))
+    _need(A, "A", torch.float32, dev, (H,))
+    cs = torch.empty((bsz, H, nc, q), dtype=torch.float32, device=dev)
+    dtc = torch.empty_like(cs)
+    states = torch.empty((bsz, H, nc, P, B.shape[3]), dtype=x.dtype, device=dev)
+    _check(load_library().ssd_cumsum_chunk_state(ctypes.byref(desc), _ptr(x), _ptr(B), _ptr(dt), _ptr(A),
+                                                 _ptr(cs), _ptr(dtc), _ptr(states), _stream(stream, dev)),
+           "ssd_cumsum_chunk_state")
+    return cs, dtc, states
 
 
 def state_passing(states, dA_cumsum, init_state=None, *, seqlen, ngroups=1, chunk_size=0,

@@ -23,6 +23,10 @@ bool mfma_chunk_scan_supported(const Plan& p);
 hipError_t launch_chunk_state_mfma(const Plan& p, const void* x, const void* B,
                                    const float* dA_cs, const float* dtc, void* states,
                                    hipStream_t s);
+// steps 1 and 2 in one launch (writes dA_cs and dtc as step 1 does)
+hipError_t launch_cumsum_chunk_state_mfma(const Plan& p, const void* x, const void* B, const float* dt,
+                                          const float* A, float* dA_cs, float* dtc, void* states,
+                                          hipStream_t s);
 hipError_t launch_chunk_scan_mfma(const Plan& p, const void* x, const void* B, const void* C,
                                   const float* D, const float* dA_cs, const float* dtc,
                                   const void* states, void* y, hipStream_t s);
@@ -126,6 +130,15 @@ hipError_t run_chunk_state(const Plan& p, const void* x, const void* B, const fl
   if (mfma_chunk_state_supported(p)) return launch_chunk_state_mfma(p, x, B, cs, dtc, st, s);
   return launch_chunk_state_simt(p, x, B, cs, dtc, st, s);
 }
+// Steps 1 and 2. bf16: the chunk-state kernel also computes the cumsum of
+// its chunk and heads (one launch fewer); fp32: the two stand-alone steps.
+hipError_t run_cumsum_chunk_state(const Plan& p, const void* x, const void* B, const float* dt,
+                                  const float* A, float* cs, float* dtc, void* st, hipStream_t s) {
+  if (mfma_chunk_state_supported(p)) return launch_cumsum_chunk_state_mfma(p, x, B, dt, A, cs, dtc, st, s);
+  hipError_t e = launch_chunk_cumsum(p, dt, A, cs, dtc, s);
+  if (e == hipSuccess) e = run_chunk_state(p, x, B, cs, dtc, st, s);
+  return e;
+}
 hipError_t run_chunk_scan(const Plan& p, const void* x, const void* B, const void* C,
                           const float* D, const float* cs, const float* dtc, const void* st,
                           void* y, hipStream_t s) {
@@ -227,8 +240,7 @@ ssd_status_t ssd_forward(const ssd_desc_t* desc, const void* x, const float* dt,
                  ssd::mfma_chunk_state_supported(p) ? "mfma" : "simt",
                  ssd::mfma_chunk_scan_supported(p) ? "mfma" : "simt");
 
-  hipError_t e = ssd::launch_chunk_cumsum(p, dt, A, cs, dtc, s);
-  if (e == hipSuccess) e = ssd::run_chunk_state(p, x, B, cs, dtc, states, s);
+  hipError_t e = ssd::run_cumsum_chunk_state(p, x, B, dt, A, cs, dtc, states, s);
   if (e == hipSuccess) e = ssd::launch_state_passing(p, states, cs, init_state, final_state, s);
   if (e == hipSuccess) e = ssd::run_chunk_scan(p, x, B, C, D, cs, dtc, states, y, s);
   if (owned) {
@@ -263,6 +275,20 @@ ssd_status_t ssd_chunk_state(const ssd_desc_t* desc, const void* x, const void* 
     return SSD_ERR_ALIGNMENT;
   return ssd::from_hip(ssd::run_chunk_state(p, x, B, dA_cumsum, dt_chunked, states,
                                             static_cast<hipStream_t>(stream)));
+}
+
+ssd_status_t ssd_cumsum_chunk_state(const ssd_desc_t* desc, const void* x, const void* B,
+                                    const float* dt, const float* A, float* dA_cumsum,
+                                    float* dt_chunked, void* states, void* stream) {
+  Plan p;
+  ssd_status_t st = ssd::make_plan(desc, &p);
+  if (st != SSD_OK) return st;
+  if (!x || !B || !dt || !A || !dA_cumsum || !dt_chunked || !states) return SSD_ERR_NULL_POINTER;
+  if (!ssd::aligned(x, 16) || !ssd::aligned(B, 16) || !ssd::aligned(dt, 4) || !ssd::aligned(A, 4) ||
+      !ssd::aligned(dA_cumsum, 16) || !ssd::aligned(dt_chunked, 16) || !ssd::aligned(states, 16))
+    return SSD_ERR_ALIGNMENT;
+  return ssd::from_hip(ssd::run_cumsum_chunk_state(p, x, B, dt, A, dA_cumsum, dt_chunked, states,
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 ssd_status_t ssd_state_passing(const ssd_desc_t* desc, void* states, const float* dA_cumsum,

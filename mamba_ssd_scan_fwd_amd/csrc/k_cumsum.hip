@@ -14,7 +14,7 @@
 // axis) into LDS; then one wavefront per head scans the Q positions: each lane
 // owns Q/64 consecutive positions, scans them serially, and the lane totals
 // are combined with a log-step wavefront scan (__shfl_up).
-#include "ssd_internal.h"
+#include "chunk_cumsum.h"
 
 namespace ssd {
 namespace {
@@ -50,25 +50,13 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(
     const int h = h0 + hh;
     const float a = A[h];
     float d[QPL], s[QPL];
-    float run = 0.f;
 #pragma unroll
-    for (int k = 0; k < QPL; ++k) {
-      d[k] = tile[lane * QPL + k][hh];
-      run += d[k] * a;
-      s[k] = run;
-    }
-    // inclusive wavefront scan of the lane totals
-    float incl = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
-    }
-    const float excl = incl - run;
+    for (int k = 0; k < QPL; ++k) d[k] = tile[lane * QPL + k][hh];
+    wave_chunk_cumsum(d, a, s, lane);
     const int64_t base = (((b * H + h) * nc) + c) * Q + lane * QPL;
 #pragma unroll
     for (int k = 0; k < QPL; ++k) {
-      dA_cs[base + k] = s[k] + excl;
+      dA_cs[base + k] = s[k];
       dtc[base + k] = d[k];
     }
   }

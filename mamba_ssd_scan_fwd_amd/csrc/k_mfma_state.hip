@@ -25,12 +25,14 @@
 //    written transposed into the other LDS buffer; one barrier per head.
 //  * Output tiles hold four consecutive n per lane: 8-byte stores into
 //    states[b,h,c][p][n].
+#include "chunk_cumsum.h"
 #include "mfma_common.h"
 
 namespace ssd {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMaxHB = 8;  // heads per workgroup, at most
 
 template <int P, int NB, int Q>
 struct StateCfg {
@@ -47,6 +49,8 @@ struct StateCfg {
   static constexpr int X_FRAGS = NT_P * KS * 64;   // 16-byte fragments of one x buffer
   static constexpr int B_FRAGS = NT_N * KS * 64;
   static constexpr int LDS_FRAGS = (2 * X_FRAGS > B_FRAGS ? 2 * X_FRAGS : B_FRAGS);
+  // fused cumsum: per head l and dt of the chunk, for up to kMaxHB heads
+  static constexpr int TAB_FLOATS = kMaxHB * 2 * Q;
 };
 
 // slot of lane (r16, g4) inside a 1 KB fragment block (a bijection, so the
@@ -55,14 +59,21 @@ __device__ __forceinline__ int sslot(int r16, int g4, int tile) {
   return 16 * g4 + ((r16 + 2 * g4 + (tile & 1)) & 15);
 }
 
-template <int P, int NB, int Q>
+// FUSED: the workgroup also computes the chunk's dA_cumsum and dt_chunked
+// for its heads from dt and A (step 1), keeps them in LDS, and writes them to
+// the workspace for the later steps (the workgroup of the first block of
+// state columns does). Otherwise it reads them from dA_cs / dtc.
+template <int P, int NB, int Q, bool FUSED>
 __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
-    const float* __restrict__ dA_cs, const float* __restrict__ dtc,
+    const float* __restrict__ dt, const float* __restrict__ A,
+    float* __restrict__ dA_cs, float* __restrict__ dtc,
     uint16_t* __restrict__ states, int64_t L, int H, int G, int N, int64_t nc, int HB) {
   using C = StateCfg<P, NB, Q>;
   constexpr int KS = C::KS;
-  __shared__ __align__(16) uint4 lds[C::LDS_FRAGS];
+  constexpr int TAB_U4 = FUSED ? C::TAB_FLOATS / 4 : 0;
+  __shared__ __align__(16) uint4 lds[C::LDS_FRAGS + TAB_U4];
+  float* tab = reinterpret_cast<float*>(lds + C::LDS_FRAGS);  // [hh][l | dt][Q] (FUSED)
 
   const int nnb = N / NB;
   const int nhg = H / HB;
@@ -82,6 +93,34 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   const int64_t t0 = c * Q;
   const int rows = (int)(L - t0 < Q ? L - t0 : Q);  // valid positions in this chunk
   const int wn = wave % C::WN, wp = wave / C::WN;
+
+  if constexpr (FUSED) {
+    // ---- step 1 for this chunk and these heads: dt tile, then one
+    // wavefront scan per head ----
+    if (tid < Q) {
+      const float* drow = dt + (b * L + t0 + min(tid, rows - 1)) * H + h0;
+      for (int hh = 0; hh < HB; ++hh) tab[(2 * hh + 1) * Q + tid] = tid < rows ? drow[hh] : 0.f;
+    }
+    __syncthreads();
+    constexpr int QPL = Q / 64;
+    for (int hh = wave; hh < HB; hh += kThreads / 64) {
+      float d[QPL], sc[QPL];
+#pragma unroll
+      for (int k = 0; k < QPL; ++k) d[k] = tab[(2 * hh + 1) * Q + lane * QPL + k];
+      wave_chunk_cumsum(d, A[h0 + hh], sc, lane);
+#pragma unroll
+      for (int k = 0; k < QPL; ++k) tab[2 * hh * Q + lane * QPL + k] = sc[k];
+      if (nb == 0) {
+        const int64_t base = ((b * H + h0 + hh) * nc + c) * Q + lane * QPL;
+#pragma unroll
+        for (int k = 0; k < QPL; ++k) {
+          dA_cs[base + k] = sc[k];
+          dtc[base + k] = d[k];
+        }
+      }
+    }
+    // the barrier after the B^T staging below also orders these LDS writes
+  }
 
   // ---- B_c^T -> LDS fragments [nt][ks][slot] (once), then into registers ----
 #pragma unroll
@@ -119,9 +158,19 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   float4 lr[C::XPT][2], dr[C::XPT][2];
   float lam = 0.f;
   auto fetch_x = [&](int h) {
-    const float* lc = dA_cs + ((b * H + h) * nc + c) * Q;
-    const float* dc = dtc + ((b * H + h) * nc + c) * Q;
-    lam = lc[Q - 1];
+    if constexpr (!FUSED) {
+      const float* lc = dA_cs + ((b * H + h) * nc + c) * Q;
+      const float* dc = dtc + ((b * H + h) * nc + c) * Q;
+      lam = lc[Q - 1];
+#pragma unroll
+      for (int k = 0; k < C::XPT; ++k) {
+        const int jb = ((tid + k * kThreads) / (P / 8)) % (Q / 8);
+        lr[k][0] = *reinterpret_cast<const float4*>(lc + 8 * jb);
+        lr[k][1] = *reinterpret_cast<const float4*>(lc + 8 * jb + 4);
+        dr[k][0] = *reinterpret_cast<const float4*>(dc + 8 * jb);
+        dr[k][1] = *reinterpret_cast<const float4*>(dc + 8 * jb + 4);
+      }
+    }
 #pragma unroll
     for (int k = 0; k < C::XPT; ++k) {
       const int bi = tid + k * kThreads;
@@ -132,13 +181,21 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         const int j = 8 * jb + rr;
         xr[k][rr] = ld16(x + ((b * L + t0 + min(j, rows - 1)) * H + h) * P + 8 * cb);
       }
-      lr[k][0] = *reinterpret_cast<const float4*>(lc + 8 * jb);
-      lr[k][1] = *reinterpret_cast<const float4*>(lc + 8 * jb + 4);
-      dr[k][0] = *reinterpret_cast<const float4*>(dc + 8 * jb);
-      dr[k][1] = *reinterpret_cast<const float4*>(dc + 8 * jb + 4);
     }
   };
-  auto stage_x = [&](uint4* buf) {
+  auto stage_x = [&](uint4* buf, int hh) {
+    if constexpr (FUSED) {  // l and dt of this head from the LDS table
+      const float* lt = tab + 2 * hh * Q;
+      lam = lt[Q - 1];
+#pragma unroll
+      for (int k = 0; k < C::XPT; ++k) {
+        const int jb = ((tid + k * kThreads) / (P / 8)) % (Q / 8);
+        lr[k][0] = *reinterpret_cast<const float4*>(lt + 8 * jb);
+        lr[k][1] = *reinterpret_cast<const float4*>(lt + 8 * jb + 4);
+        dr[k][0] = *reinterpret_cast<const float4*>(lt + Q + 8 * jb);
+        dr[k][1] = *reinterpret_cast<const float4*>(lt + Q + 8 * jb + 4);
+      }
+    }
 #pragma unroll
     for (int k = 0; k < C::XPT; ++k) {
       const int bi = tid + k * kThreads;
@@ -167,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 
   const int ksteps = (rows + 31) / 32;
   fetch_x(h0);
-  stage_x(lds);
+  stage_x(lds, 0);
   __syncthreads();
   for (int hh = 0; hh < HB; ++hh) {
     const int h = h0 + hh;
@@ -214,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         }
       }
     }
-    if (hh + 1 < HB) stage_x(lds + ((hh + 1) & 1) * C::X_FRAGS);  // the other buffer
+    if (hh + 1 < HB) stage_x(lds + ((hh + 1) & 1) * C::X_FRAGS, hh + 1);  // the other buffer
     __syncthreads();
   }
 }
@@ -226,41 +283,53 @@ int pick_heads_per_wg(const Plan& p, int nnb) {
   const int64_t hpg = p.H / p.G;
   const int64_t base = p.batch * p.nc * nnb * p.H;
   int hb = 1;
-  while (hb < 8 && hpg % (hb * 2) == 0 && base / (hb * 2) >= 512) hb *= 2;
+  while (hb < kMaxHB && hpg % (hb * 2) == 0 && base / (hb * 2) >= 512) hb *= 2;
   return hb;
 }
 
-template <int P, int NB, int Q>
-hipError_t launch_pnq(const Plan& p, const void* x, const void* B, const float* cs,
-                      const float* dtc, void* st, hipStream_t s) {
+template <int P, int NB, int Q, bool FUSED>
+hipError_t launch_pnq(const Plan& p, const void* x, const void* B, const float* dt, const float* A,
+                      float* cs, float* dtc, void* st, hipStream_t s) {
   const int nnb = (int)(p.N / NB);
   const int hb = pick_heads_per_wg(p, nnb);
   const int64_t grid = p.batch * p.nc * (p.H / hb) * nnb;
-  chunk_state_mfma_kernel<P, NB, Q><<<dim3((unsigned)grid), kThreads, 0, s>>>(
-      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), cs, dtc,
+  chunk_state_mfma_kernel<P, NB, Q, FUSED><<<dim3((unsigned)grid), kThreads, 0, s>>>(
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), dt, A, cs, dtc,
       static_cast<uint16_t*>(st), p.L, (int)p.H, (int)p.G, (int)p.N, p.nc, hb);
   return hipGetLastError();
 }
 
-template <int P, int NB>
-hipError_t launch_pn(const Plan& p, const void* x, const void* B, const float* cs,
-                     const float* dtc, void* st, hipStream_t s) {
+template <int P, int NB, bool FUSED>
+hipError_t launch_pn(const Plan& p, const void* x, const void* B, const float* dt, const float* A,
+                     float* cs, float* dtc, void* st, hipStream_t s) {
   switch (p.Q) {
-    case 64: return launch_pnq<P, NB, 64>(p, x, B, cs, dtc, st, s);
-    case 128: return launch_pnq<P, NB, 128>(p, x, B, cs, dtc, st, s);
-    case 256: return launch_pnq<P, NB, 256>(p, x, B, cs, dtc, st, s);
+    case 64: return launch_pnq<P, NB, 64, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
+    case 128: return launch_pnq<P, NB, 128, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
+    case 256: return launch_pnq<P, NB, 256, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int P>
-hipError_t launch_p(const Plan& p, const void* x, const void* B, const float* cs,
-                    const float* dtc, void* st, hipStream_t s) {
+template <int P, bool FUSED>
+hipError_t launch_p(const Plan& p, const void* x, const void* B, const float* dt, const float* A,
+                    float* cs, float* dtc, void* st, hipStream_t s) {
   switch (p.N) {
-    case 16: return launch_pn<P, 16>(p, x, B, cs, dtc, st, s);
-    case 32: return launch_pn<P, 32>(p, x, B, cs, dtc, st, s);
-    case 64: return launch_pn<P, 64>(p, x, B, cs, dtc, st, s);
-    default: return launch_pn<P, 128>(p, x, B, cs, dtc, st, s);  // 128, 256
+    case 16: return launch_pn<P, 16, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
+    case 32: return launch_pn<P, 32, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
+    case 64: return launch_pn<P, 64, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
+    default: return launch_pn<P, 128, FUSED>(p, x, B, dt, A, cs, dtc, st, s);  // 128, 256
+  }
+}
+
+template <bool FUSED>
+hipError_t launch_any(const Plan& p, const void* x, const void* B, const float* dt, const float* A,
+                      float* cs, float* dtc, void* st, hipStream_t s) {
+  switch (p.P) {
+    case 16: return launch_p<16, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
+    case 32: return launch_p<32, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
+    case 64: return launch_p<64, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
+    case 128: return launch_p<128, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -275,13 +344,14 @@ bool mfma_chunk_state_supported(const Plan& p) {
 hipError_t launch_chunk_state_mfma(const Plan& p, const void* x, const void* B,
                                    const float* dA_cs, const float* dtc, void* states,
                                    hipStream_t s) {
-  switch (p.P) {
-    case 16: return launch_p<16>(p, x, B, dA_cs, dtc, states, s);
-    case 32: return launch_p<32>(p, x, B, dA_cs, dtc, states, s);
-    case 64: return launch_p<64>(p, x, B, dA_cs, dtc, states, s);
-    case 128: return launch_p<128>(p, x, B, dA_cs, dtc, states, s);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_any<false>(p, x, B, nullptr, nullptr, const_cast<float*>(dA_cs), const_cast<float*>(dtc),
+                           states, s);
+}
+
+hipError_t launch_cumsum_chunk_state_mfma(const Plan& p, const void* x, const void* B, const float* dt,
+                                          const float* A, float* dA_cs, float* dtc, void* states,
+                                          hipStream_t s) {
+  return launch_any<true>(p, x, B, dt, A, dA_cs, dtc, states, s);
 }
 
 }  // namespace ssd

@@ -198,6 +198,10 @@ def test_step_entry_points_validate_too():
     d = desc()
     assert L.ssd_chunk_cumsum(ctypes.byref(d), None, *([ctypes.c_void_p(BASE)] * 3), None) == NULLP
     assert L.ssd_chunk_state(ctypes.byref(d), *([ctypes.c_void_p(BASE + 2)] * 5), None) == ALIGN
+    p7 = [ctypes.c_void_p(BASE)] * 7
+    assert L.ssd_cumsum_chunk_state(ctypes.byref(d), *p7[:6], None, None) == NULLP
+    assert L.ssd_cumsum_chunk_state(ctypes.byref(d), ctypes.c_void_p(BASE + 2), *p7[1:], None) == ALIGN
+    assert L.ssd_cumsum_chunk_state(ctypes.byref(desc(headdim=48)), *p7, None) == UNSUP
     assert L.ssd_state_passing(ctypes.byref(d), None, ctypes.c_void_p(BASE), None, None, None) == NULLP
     p0 = ctypes.c_void_p(BASE)
     assert L.ssd_state_passing(ctypes.byref(d), p0, p0, ctypes.c_void_p(BASE + 4096),

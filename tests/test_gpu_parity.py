@@ -353,3 +353,38 @@ def test_step_chunk_scan(io, Q, L):
     torch.cuda.synchronize()
     yr, _ = ssd_recurrent(*(np64(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "init_state")))
     check_rel(np64(y), yr, TOL[io], f"chunk scan y {io} Q={Q}")
+
+
+@pytest.mark.parametrize("io,Q,L,G", [("bf16", 256, 600, 2), ("bf16", 128, 333, 1), ("bf16", 64, 200, 4),
+                                      ("fp32", 128, 333, 2)])
+def test_forward_equals_its_steps_bitwise(io, Q, L, G):
+    """ssd_forward (which may fuse steps into fewer launches) leaves in its
+    workspace exactly what the stand-alone steps compute, and returns the
+    same y and final state, bit for bit."""
+    cfg = BASE.with_(seqlen=L, io_dtype=io, ngroups=G, nheads=8, init_state=True)
+    inp = make_inputs(cfg, seed=24)
+    d = to_dev(inp)
+    lib = ssd()
+    desc = lib.make_desc(cfg.batch, L, cfg.nheads, cfg.headdim, cfg.dstate, G, io, Q)
+    nws = lib.workspace_bytes(desc)
+    ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device=DEV)
+    note(f"[gpu] forward vs steps {io} Q={Q} L={L} G={G}")
+    y, hT = lib.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], chunk_size=Q,
+                        workspace=ws)
+    cs, dtc = lib.chunk_cumsum(d["dt"], d["A"], headdim=cfg.headdim, dstate=cfg.dstate, ngroups=G,
+                               io_dtype=io, chunk_size=Q)
+    st = lib.chunk_state(d["x"], d["B"], cs, dtc, chunk_size=Q)
+    cs3, dtc3, st3 = lib.cumsum_chunk_state(d["x"], d["B"], d["dt"], d["A"], chunk_size=Q)
+    torch.cuda.synchronize()
+    assert torch.equal(cs3, cs) and torch.equal(dtc3, dtc) and torch.equal(st3, st)
+    st, hT2 = lib.state_passing(st, cs, d["init_state"], seqlen=L, ngroups=G, chunk_size=Q)
+    y2 = lib.chunk_scan(d["x"], d["B"], d["C"], d["D"], cs, dtc, st, chunk_size=Q)
+    torch.cuda.synchronize()
+    # workspace layout: dA_cumsum, dt_chunked, states, each on a 256-byte boundary
+    n = cs.numel() * 4
+    off_dt = (n + 255) // 256 * 256
+    ws_cs = ws[:n].view(torch.float32).view(cs.shape)
+    ws_dt = ws[off_dt:off_dt + n].view(torch.float32).view(cs.shape)
+    assert torch.equal(ws_cs, cs), "dA_cumsum in the workspace differs from step 1"
+    assert torch.equal(ws_dt, dtc), "dt_chunked in the workspace differs from step 1"
+    assert torch.equal(y, y2) and torch.equal(hT, hT2)
