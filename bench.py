@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--kernel-reps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--cpu-sample-seqs", type=int, default=8)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain fp32 elementwise copy (negation) of MIB MiB, "
@@ -143,6 +144,40 @@ def cpu_baseline(cfg, inp, nseq, min_seconds=10.0, max_reps=4):
                   f"{reps} pass(es) ({tokens * reps} tokens in {total:.1f} s; fp64 NumPy sequential "
                   f"recurrence, one thread, {platform.processor() or platform.machine()})",
     }
+
+
+def decode_measure(cfg, batch, steps, dev):
+    """The recurrent (decode) step on the layer shape of `cfg` for `batch`
+    sequences: average time per step (HIP events on the launch stream) and
+    algorithmic bytes (fp32 state read and written once, plus x, y, dt, B, C)."""
+    import torch
+
+    import mamba_ssd_scan_fwd_amd as ssd
+    from ssd_inputs import make_inputs
+
+    inp = make_inputs(cfg.with_(batch=batch, seqlen=1, init_state=True), seed=101)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    x, dt, Bm, Cm = d["x"][:, 0], d["dt"][:, 0], d["B"][:, 0], d["C"][:, 0]
+    state = d["init_state"]
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(3):
+        ssd.decode_step(x, dt, d["A"], Bm, Cm, d["D"], state, y=y)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        ssd.decode_step(x, dt, d["A"], Bm, Cm, d["D"], state, y=y)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1e3
+    s = 2 if cfg.io_dtype == "bf16" else 4
+    H, P, N, G = cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
+    nbytes = batch * (2 * 4 * H * P * N + 2 * H * P * s + 2 * G * N * s + 4 * H)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"decode step, {batch} sequences x {cfg.name} layer (H {H}, P {P}, N {N}, G {G})",
+            "batch": batch, "avg_us": round(us, 2), "tokens_per_s": round(batch / (us * 1e-6), 1),
+            "algo_bytes": nbytes, "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def main():
@@ -310,6 +345,10 @@ def main():
         "mfma_frac_useful": round(m["flops"] / (durations[dom] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
     }
 
+    decode = None
+    if not args.no_decode:
+        decode = [decode_measure(cfg, bsz, 50, dev) for bsz in (cfg.batch, 256)]
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, inp, min(args.cpu_sample_seqs, cfg.batch))
@@ -336,6 +375,7 @@ def main():
         "roofline": roofline,
         "kernels": per_kernel,
         "cpu_baseline": cpu,
+        "decode_step": decode,
     }
     print(json.dumps(line), flush=True)
 

@@ -172,6 +172,25 @@ SSD_API ssd_status_t ssd_chunk_scan(const ssd_desc_t* desc, const void* x, const
                             const float* D, const float* dA_cumsum, const float* dt_chunked,
                             const void* states, void* y, void* stream);
 
+/* ---- the recurrent (decode) step ------------------------------------------ */
+
+/* One token of a batch of sequences through the recurrence, the state kept
+ * between calls ("Mamba-2 vs Transformers", table "Evaluation criteria ...":
+ * recurrent mode, O(1) state per token). desc->seqlen must be 1 (chunk_size
+ * is ignored); shapes are those of ssd_forward with L = 1:
+ *     x, y     [batch, H, P]      io dtype
+ *     dt       [batch, H]         fp32, used as given
+ *     A, D     [H]                fp32 (D nullable: no skip term)
+ *     B, C     [batch, G, N]      io dtype
+ *     state    [batch, H, P, N]   fp32, read and overwritten in place:
+ *     state <- exp(dt A) state + dt x B^T;  y = state C + D x  (the new state).
+ * The same result as ssd_forward on the one token with init_state = state and
+ * final_state = state. state and y must not overlap each other or any input.
+ * Base pointers 16-byte aligned (dt, A, D: 4). No workspace. */
+SSD_API ssd_status_t ssd_decode_step(const ssd_desc_t* desc, const void* x, const float* dt,
+                             const float* A, const void* B, const void* C, const float* D,
+                             float* state, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

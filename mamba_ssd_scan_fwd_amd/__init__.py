@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     chunk_scan,
     chunk_state,
     cumsum_chunk_state,
+    decode_step,
     effective_chunk_size,
     forward,
     lib_path,

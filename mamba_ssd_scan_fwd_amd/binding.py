@@ -28,6 +28,7 @@ __all__ = [
     "cumsum_chunk_state",
     "state_passing",
     "chunk_scan",
+    "decode_step",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -44,6 +45,7 @@ EXPORTED_SYMBOLS = (
     "ssd_cumsum_chunk_state",
     "ssd_state_passing",
     "ssd_chunk_scan",
+    "ssd_decode_step",
 )
 
 SSD_DTYPE_F32 = 0
@@ -112,6 +114,8 @@ def load_library():
         lib.ssd_state_passing.restype = ctypes.c_int
         lib.ssd_chunk_scan.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.ssd_chunk_scan.restype = ctypes.c_int
+        lib.ssd_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.ssd_decode_step.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -331,4 +335,28 @@ def chunk_scan(x, B, C, D, dA_cumsum, dt_chunked, states, *, chunk_size=0, y=Non
     _check(load_library().ssd_chunk_scan(ctypes.byref(desc), _ptr(x), _ptr(B), _ptr(C), _ptr(D),
                                          _ptr(dA_cumsum), _ptr(dt_chunked), _ptr(states), _ptr(y),
                                          _stream(stream, dev)), "ssd_chunk_scan")
+    return y
+
+
+def decode_step(x, dt, A, B, C, D, state, *, y=None, stream=None):
+    """One recurrent step: x [b, H, P], dt [b, H], B/C [b, G, N], state
+    [b, H, P, N] fp32 updated in place. Returns y [b, H, P] (io dtype)."""
+    dev = x.device
+    _need(x, "x", device=dev)
+    bsz, H, P = x.shape
+    _need(dt, "dt", torch.float32, dev, (bsz, H))
+    _need(A, "A", torch.float32, dev, (H,))
+    _need(B, "B", x.dtype, dev)
+    _need(C, "C", x.dtype, dev, tuple(B.shape))
+    if D is not None:
+        _need(D, "D", torch.float32, dev, (H,))
+    G, N = B.shape[1], B.shape[2]
+    _need(state, "state", torch.float32, dev, (bsz, H, P, N))
+    io = "bf16" if x.dtype == torch.bfloat16 else "fp32"
+    desc = make_desc(bsz, 1, H, P, N, G, io, 0)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(load_library().ssd_decode_step(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                          _ptr(D), _ptr(state), _ptr(y), _stream(stream, dev)),
+           "ssd_decode_step")
     return y

@@ -324,4 +324,30 @@ ssd_status_t ssd_chunk_scan(const ssd_desc_t* desc, const void* x, const void* B
                                            static_cast<hipStream_t>(stream)));
 }
 
+ssd_status_t ssd_decode_step(const ssd_desc_t* desc, const void* x, const float* dt, const float* A,
+                             const void* B, const void* C, const float* D, float* state, void* y,
+                             void* stream) {
+  Plan p;
+  ssd_status_t st = ssd::make_plan(desc, &p);
+  if (st != SSD_OK) return st;
+  if (p.L != 1) return SSD_ERR_BAD_SHAPE;
+  if (!x || !dt || !A || !B || !C || !state || !y) return SSD_ERR_NULL_POINTER;
+  if (!ssd::aligned(x, 16) || !ssd::aligned(B, 16) || !ssd::aligned(C, 16) || !ssd::aligned(y, 16) ||
+      !ssd::aligned(state, 16) || !ssd::aligned(dt, 4) || !ssd::aligned(A, 4) || !ssd::aligned(D, 4))
+    return SSD_ERR_ALIGNMENT;
+  const size_t io = p.io_bytes();
+  const ssd::Range rs = ssd::range_of(state, size_t(p.batch * p.H * p.P * p.N) * sizeof(float));
+  const ssd::Range ry = ssd::range_of(y, size_t(p.batch * p.H * p.P) * io);
+  const ssd::Range ins[] = {ssd::range_of(x, size_t(p.batch * p.H * p.P) * io),
+                            ssd::range_of(dt, size_t(p.batch * p.H) * sizeof(float)),
+                            ssd::range_of(A, size_t(p.H) * sizeof(float)),
+                            ssd::range_of(B, size_t(p.batch * p.G * p.N) * io),
+                            ssd::range_of(C, size_t(p.batch * p.G * p.N) * io),
+                            ssd::range_of(D, D ? size_t(p.H) * sizeof(float) : 0)};
+  if (ssd::overlap(rs, ry)) return SSD_ERR_ALIAS;
+  for (const ssd::Range& r : ins)
+    if (ssd::overlap(rs, r) || ssd::overlap(ry, r)) return SSD_ERR_ALIAS;
+  return ssd::from_hip(ssd::launch_decode_step(p, x, dt, A, B, C, D, state, y, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

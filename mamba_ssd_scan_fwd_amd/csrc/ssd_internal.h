@@ -32,6 +32,9 @@ hipError_t launch_chunk_scan(const Plan& p, const void* x, const void* B, const 
                              const float* D, const float* dA_cs, const float* dtc,
                              const void* states, void* y, hipStream_t s);
 
+hipError_t launch_decode_step(const Plan& p, const void* x, const float* dt, const float* A, const void* B,
+                              const void* C, const float* D, float* state, void* y, hipStream_t s);
+
 // Element conversion helpers used by every kernel file.
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(__hip_bfloat16 v) { return __bfloat162float(v); }

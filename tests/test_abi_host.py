@@ -212,3 +212,22 @@ def test_step_entry_points_validate_too():
 def test_desc_struct_layout():
     # int64 x 6 followed by two int32: 56 bytes, no padding surprises
     assert ctypes.sizeof(SSDDesc) == 56
+
+
+def test_decode_step_validates():
+    L = lib()
+    p = [ctypes.c_void_p(BASE + k * (1 << 24)) for k in range(8)]  # x dt A B C D state y, disjoint
+    d1 = desc(seqlen=1)
+    assert L.ssd_decode_step(ctypes.byref(desc(seqlen=2)), *p, None) == SHAPE
+    assert L.ssd_decode_step(ctypes.byref(d1), None, *p[1:], None) == NULLP
+    assert L.ssd_decode_step(ctypes.byref(d1), *p[:6], None, p[7], None) == NULLP
+    q = list(p)
+    q[6] = ctypes.c_void_p(BASE + 6 * (1 << 24) + 8)
+    assert L.ssd_decode_step(ctypes.byref(d1), *q, None) == ALIGN
+    q = list(p)
+    q[7] = p[0]  # y over x
+    assert L.ssd_decode_step(ctypes.byref(d1), *q, None) == ALIAS
+    q = list(p)
+    q[6] = p[3]  # state over B
+    assert L.ssd_decode_step(ctypes.byref(d1), *q, None) == ALIAS
+    assert L.ssd_decode_step(ctypes.byref(desc(seqlen=1, headdim=48)), *p, None) == UNSUP

@@ -388,3 +388,71 @@ def test_forward_equals_its_steps_bitwise(io, Q, L, G):
     assert torch.equal(ws_cs, cs), "dA_cumsum in the workspace differs from step 1"
     assert torch.equal(ws_dt, dtc), "dt_chunked in the workspace differs from step 1"
     assert torch.equal(y, y2) and torch.equal(hT, hT2)
+
+
+# ---- the recurrent (decode) step -----------------------------------------
+
+def _decode_inputs(cfg, seed):
+    """One token per sequence: the L = 1 slice of the seeded recipe, plus a
+    0.1 N(0,1) state."""
+    inp = make_inputs(cfg.with_(seqlen=1, init_state=True), seed=seed)
+    return inp
+
+
+@pytest.mark.parametrize("io,P,N,H,G,withD", [("bf16", 64, 128, 8, 1, True), ("bf16", 16, 16, 4, 2, True),
+                                              ("bf16", 32, 256, 4, 4, False), ("bf16", 128, 64, 2, 1, True),
+                                              ("fp32", 64, 32, 4, 2, True)])
+def test_decode_step_matches_oracle(io, P, N, H, G, withD):
+    cfg = BASE.with_(batch=3, io_dtype=io, headdim=P, dstate=N, nheads=H, ngroups=G)
+    inp = _decode_inputs(cfg, seed=30)
+    if not withD:
+        inp["D"] = None
+    d = to_dev(inp)
+    state = d["init_state"].clone()
+    note(f"[gpu] decode step {io} P={P} N={N} H={H} G={G} D={withD}")
+    y = ssd().decode_step(d["x"][:, 0], d["dt"][:, 0], d["A"], d["B"][:, 0], d["C"][:, 0], d["D"], state)
+    torch.cuda.synchronize()
+    yr, hr = ssd_recurrent(*(np64(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "init_state")))
+    tol = TOL[io]
+    check_rel(np64(y), yr[:, 0], tol, f"decode y {io}")
+    # the state stays fp32: only fp32 rounding of one update
+    check_rel(np64(state), hr, 1e-6, f"decode state {io}")
+
+
+def test_decode_steps_continue_a_prefill():
+    """Prefill L0 tokens with ssd_forward, then decode the next T tokens one
+    at a time from its final state: every y and the last state match the
+    oracle recurrence over all L0 + T tokens."""
+    L0, T = 300, 24
+    cfg = BASE.with_(seqlen=L0 + T, nheads=4, ngroups=2, init_state=True)
+    inp = make_inputs(cfg, seed=31)
+    d = to_dev(inp)
+    note(f"[gpu] prefill {L0} + decode {T}")
+    _, state = ssd().forward(*(d[k][:, :L0].contiguous() if k in ("x", "dt", "B", "C") else d[k]
+                               for k in ("x", "dt", "A", "B", "C", "D", "init_state")))
+    ys = []
+    for t in range(L0, L0 + T):
+        ys.append(ssd().decode_step(d["x"][:, t].contiguous(), d["dt"][:, t].contiguous(), d["A"],
+                                    d["B"][:, t].contiguous(), d["C"][:, t].contiguous(), d["D"], state))
+    torch.cuda.synchronize()
+    yr, hr = ssd_recurrent(*(np64(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "init_state")))
+    got = np.stack([np64(v) for v in ys], axis=1)
+    check_rel(got, yr[:, L0:], TOL["bf16"], "decoded y after prefill")
+    check_rel(np64(state), hr, TOL["bf16"], "state after prefill + decode")
+
+
+def test_decode_step_large_batch_sampled():
+    """The decode workload bench.py times (batch 256 of the headline layer),
+    checked on sampled sequences."""
+    cfg = CONFIGS[1].with_(batch=256)
+    inp = _decode_inputs(cfg, seed=32)
+    d = to_dev(inp)
+    state = d["init_state"].clone()
+    note("[gpu] decode step batch 256 H=64 P=64 N=128")
+    y = ssd().decode_step(d["x"][:, 0], d["dt"][:, 0], d["A"], d["B"][:, 0], d["C"][:, 0], d["D"], state)
+    torch.cuda.synchronize()
+    for b in (0, 77, 255):
+        sl = {k: (v[b:b + 1] if k in ("x", "dt", "B", "C", "init_state") else v) for k, v in inp.items()}
+        yr, hr = ssd_recurrent(*(np64(sl[k]) for k in ("x", "dt", "A", "B", "C", "D", "init_state")))
+        check_rel(np64(y[b:b + 1]), yr[:, 0], TOL["bf16"], f"decode y b={b}")
+        check_rel(np64(state[b:b + 1]), hr, 1e-6, f"decode state b={b}")
