@@ -47,6 +47,9 @@
  *                                          state of each chunk, overwritten in
  *                                          place by the state entering it.
  *
+ * dt: every entry point applies the descriptor's dt preprocessing (bias,
+ * softplus, clamp) when asked to; with the zero default dt is used as given.
+ *
  * Supported: io dtype fp32 or bf16; P in {16, 32, 64, 128};
  * N in {16, 32, 64, 128, 256}; H % G == 0; chunk_size in {0 (default), 64,
  * 128, 256}. Base pointers of x, B, C, y, init_state, final_state must be
@@ -84,7 +87,8 @@ typedef enum {
   SSD_ERR_HIP = 7           /* the HIP runtime reported an error               */
 } ssd_status_t;
 
-/* Problem description. Plain data; the library reads it during the call only. */
+/* Problem description. Plain data; the library reads it during the call only.
+ * A zero-initialised tail (dt_bias .. dt_max) means dt is used as given. */
 typedef struct {
   int64_t batch;
   int64_t seqlen;     /* L  */
@@ -94,6 +98,16 @@ typedef struct {
   int64_t ngroups;    /* G  */
   int32_t io_dtype;   /* ssd_dtype_t: dtype of x, B, C, y (and of states)     */
   int32_t chunk_size; /* Q: 0 picks the library default for the shape         */
+  /* dt preprocessing of the Mamba-2 layer, applied to every dt the entry
+   * points read, in this order (positions past the end of a sequence keep
+   * dt = 0):  z = dt + dt_bias[h]      when dt_bias != NULL
+   *           z = log(1 + exp(z))      when dt_softplus != 0
+   *           z = min(max(z, dt_min), dt_max)   when dt_clamp != 0  */
+  const float* dt_bias; /* [H] fp32 device pointer, nullable, 4-byte aligned   */
+  int32_t dt_softplus;
+  int32_t dt_clamp;     /* requires dt_min <= dt_max                           */
+  float dt_min;
+  float dt_max;
 } ssd_desc_t;
 
 /* Human-readable name of a status code (static string, never NULL). */

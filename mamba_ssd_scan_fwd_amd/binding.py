@@ -68,6 +68,11 @@ class SSDDesc(ctypes.Structure):
         ("ngroups", ctypes.c_int64),
         ("io_dtype", ctypes.c_int32),
         ("chunk_size", ctypes.c_int32),
+        ("dt_bias", ctypes.c_void_p),
+        ("dt_softplus", ctypes.c_int32),
+        ("dt_clamp", ctypes.c_int32),
+        ("dt_min", ctypes.c_float),
+        ("dt_max", ctypes.c_float),
     ]
 
 
@@ -129,7 +134,11 @@ def _check(status: int, where: str):
         raise SSDError(status, where)
 
 
-def make_desc(batch, seqlen, nheads, headdim, dstate, ngroups, io_dtype, chunk_size=0) -> SSDDesc:
+def make_desc(batch, seqlen, nheads, headdim, dstate, ngroups, io_dtype, chunk_size=0, *,
+              dt_bias=None, dt_softplus=False, dt_limit=None) -> SSDDesc:
+    """The C descriptor. dt preprocessing: ``dt_bias`` (fp32 [H] device
+    tensor) is added to dt, ``dt_softplus`` applies log(1 + e^z), and
+    ``dt_limit = (lo, hi)`` clamps the result."""
     if isinstance(io_dtype, torch.dtype):
         io = {torch.float32: SSD_DTYPE_F32, torch.bfloat16: SSD_DTYPE_BF16}.get(io_dtype)
         if io is None:
@@ -140,8 +149,15 @@ def make_desc(batch, seqlen, nheads, headdim, dstate, ngroups, io_dtype, chunk_s
         io = SSD_DTYPE_BF16
     else:
         io = int(io_dtype)
-    return SSDDesc(int(batch), int(seqlen), int(nheads), int(headdim), int(dstate), int(ngroups), io,
-                   int(chunk_size))
+    d = SSDDesc(int(batch), int(seqlen), int(nheads), int(headdim), int(dstate), int(ngroups), io,
+                int(chunk_size))
+    if dt_bias is not None:
+        d.dt_bias = dt_bias.data_ptr()
+    d.dt_softplus = 1 if dt_softplus else 0
+    if dt_limit is not None:
+        d.dt_clamp = 1
+        d.dt_min, d.dt_max = float(dt_limit[0]), float(dt_limit[1])
+    return d
 
 
 def effective_chunk_size(desc: SSDDesc) -> int:
@@ -182,22 +198,33 @@ def _need(t, name, dtype=None, device=None, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def _desc_from(x, B, chunk_size):
+def _desc_from(x, B, chunk_size, dt_pre=None):
     bsz, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    return make_desc(bsz, L, H, P, N, G, x.dtype, chunk_size)
+    return make_desc(bsz, L, H, P, N, G, x.dtype, chunk_size, **_dt_kw(dt_pre, H, x.device))
+
+
+def _dt_kw(dt_pre, H, dev):
+    """dt_pre: None or dict(bias=tensor|None, softplus=bool, limit=(lo, hi)|None)."""
+    if not dt_pre:
+        return {}
+    bias = dt_pre.get("bias")
+    if bias is not None:
+        _need(bias, "dt bias", torch.float32, dev, (H,))
+    return dict(dt_bias=bias, dt_softplus=bool(dt_pre.get("softplus", False)), dt_limit=dt_pre.get("limit"))
 
 
 def forward(x, dt, A, B, C, D=None, init_state=None, *, chunk_size: int = 0,
             return_final_state: bool = True, y=None, final_state=None, workspace=None,
-            library_workspace: bool = False, stream=None):
+            library_workspace: bool = False, dt_pre=None, stream=None):
     """SSD forward pass on the GPU. Returns (y, final_state or None).
 
     x [b, L, H, P] and B, C [b, L, G, N] in fp32 or bf16 (all the same);
     dt [b, L, H], A [H], D [H] (optional) and init_state [b, H, P, N]
     (optional) in fp32. ``final_state`` may be passed as ``init_state`` for an
     in-place state update. With ``library_workspace=True`` the library
-    allocates its workspace itself, in stream order.
+    allocates its workspace itself, in stream order. ``dt_pre`` asks for the
+    dt preprocessing: dict(bias=[H] fp32 tensor, softplus=True, limit=(lo, hi)).
     """
     dev = x.device
     _need(x, "x", device=dev)
@@ -212,7 +239,7 @@ def forward(x, dt, A, B, C, D=None, init_state=None, *, chunk_size: int = 0,
         _need(D, "D", torch.float32, dev, (H,))
     if init_state is not None:
         _need(init_state, "init_state", torch.float32, dev, (bsz, H, P, N))
-    desc = _desc_from(x, B, chunk_size)
+    desc = _desc_from(x, B, chunk_size, dt_pre)
     if y is None:
         y = torch.empty_like(x)
     else:
@@ -244,13 +271,14 @@ def _chunk_shape(desc):
     return q, nc
 
 
-def chunk_cumsum(dt, A, *, headdim, dstate, ngroups=1, io_dtype=torch.bfloat16, chunk_size=0, stream=None):
+def chunk_cumsum(dt, A, *, headdim, dstate, ngroups=1, io_dtype=torch.bfloat16, chunk_size=0, dt_pre=None,
+                 stream=None):
     """Step 1 alone. Returns (dA_cumsum, dt_chunked), each [b, H, nc, Q] fp32."""
     dev = dt.device
     _need(dt, "dt", torch.float32, dev)
     bsz, L, H = dt.shape
     _need(A, "A", torch.float32, dev, (H,))
-    desc = make_desc(bsz, L, H, headdim, dstate, ngroups, io_dtype, chunk_size)
+    desc = make_desc(bsz, L, H, headdim, dstate, ngroups, io_dtype, chunk_size, **_dt_kw(dt_pre, H, dev))
     q, nc = _chunk_shape(desc)
     cs = torch.empty((bsz, H, nc, q), dtype=torch.float32, device=dev)
     dtc = torch.empty_like(cs)
@@ -276,12 +304,12 @@ def chunk_state(x, B, dA_cumsum, dt_chunked, *, chunk_size=0, stream=None):
     return states
 
 
-def cumsum_chunk_state(x, B, dt, A, *, chunk_size=0, stream=None):
+def cumsum_chunk_state(x, B, dt, A, *, chunk_size=0, dt_pre=None, stream=None):
     """Steps 1 and 2 in one call. Returns (dA_cumsum, dt_chunked, states)."""
     dev = x.device
     _need(x, "x", device=dev)
     _need(B, "B", x.dtype, dev)
-    desc = _desc_from(x, B, chunk_size)
+    desc = _desc_from(x, B, chunk_size, dt_pre)
     q, nc = _chunk_shape(desc)
     bsz, L, H, P = x.shape
     _need(dt, "dt", torch.float32, dev, (bsz, L, H))
@@ -338,7 +366,7 @@ def chunk_scan(x, B, C, D, dA_cumsum, dt_chunked, states, *, chunk_size=0, y=Non
     return y
 
 
-def decode_step(x, dt, A, B, C, D, state, *, y=None, stream=None):
+def decode_step(x, dt, A, B, C, D, state, *, y=None, dt_pre=None, stream=None):
     """One recurrent step: x [b, H, P], dt [b, H], B/C [b, G, N], state
     [b, H, P, N] fp32 updated in place. Returns y [b, H, P] (io dtype)."""
     dev = x.device
@@ -353,7 +381,7 @@ def decode_step(x, dt, A, B, C, D, state, *, y=None, stream=None):
     G, N = B.shape[1], B.shape[2]
     _need(state, "state", torch.float32, dev, (bsz, H, P, N))
     io = "bf16" if x.dtype == torch.bfloat16 else "fp32"
-    desc = make_desc(bsz, 1, H, P, N, G, io, 0)
+    desc = make_desc(bsz, 1, H, P, N, G, io, 0, **_dt_kw(dt_pre, H, dev))
     if y is None:
         y = torch.empty_like(x)
     _check(load_library().ssd_decode_step(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),

@@ -52,6 +52,8 @@ int default_chunk(const ssd_desc_t& d) {
   return (d.headdim <= 64 && d.dstate <= 128) ? 256 : 128;
 }
 
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
 ssd_status_t make_plan(const ssd_desc_t* d, Plan* p) {
   if (d == nullptr || p == nullptr) return SSD_ERR_NULL_POINTER;
   if (d->batch <= 0 || d->seqlen <= 0 || d->nheads <= 0 || d->headdim <= 0 ||
@@ -81,6 +83,9 @@ ssd_status_t make_plan(const ssd_desc_t* d, Plan* p) {
   p->io = d->io_dtype == SSD_DTYPE_BF16 ? kBF16 : kF32;
   p->Q = Q;
   p->nc = nc;
+  if (d->dt_clamp && !(d->dt_min <= d->dt_max)) return SSD_ERR_BAD_SHAPE;
+  if (!aligned(d->dt_bias, 4)) return SSD_ERR_ALIGNMENT;
+  p->dto = DtOpts{d->dt_bias, d->dt_softplus != 0, d->dt_clamp != 0, d->dt_min, d->dt_max};
   return SSD_OK;
 }
 
@@ -99,7 +104,6 @@ WsLayout ws_layout(const Plan& p) {
   return w;
 }
 
-bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)

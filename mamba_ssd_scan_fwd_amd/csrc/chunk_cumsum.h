@@ -10,6 +10,16 @@
 
 namespace ssd {
 
+// dt as the entry points use it: optional per-head bias, softplus
+// log(1 + e^z) (z itself above 20, where the two agree in fp32), then an
+// optional clamp. Applied to positions inside the sequence only.
+__device__ __forceinline__ float dt_pre(float v, int h, const DtOpts& o) {
+  if (o.bias != nullptr) v += o.bias[h];
+  if (o.softplus) v = v > 20.f ? v : log1pf(expf(v));
+  if (o.clamp) v = fminf(fmaxf(v, o.lo), o.hi);
+  return v;
+}
+
 // Lane `lane` owns the QPL = Q/64 consecutive positions lane*QPL .. +QPL-1 of
 // the chunk; d[] holds their dt (0 past the sequence end). On return s[k] is
 // the inclusive sum of dt*a over positions 0 .. lane*QPL + k.

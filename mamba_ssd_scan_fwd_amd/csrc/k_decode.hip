@@ -12,7 +12,7 @@
 // 16-byte load and store), TPR = N/4 threads share a row and reduce y with
 // cross-lane shuffles; a thread handles RPT rows so that several loads are in
 // flight before the first use.
-#include "ssd_internal.h"
+#include "chunk_cumsum.h"
 
 namespace ssd {
 namespace {
@@ -36,7 +36,7 @@ template <typename TIO, int N>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const TIO* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const TIO* __restrict__ Bm, const TIO* __restrict__ Cm, const float* __restrict__ D,
-    float* __restrict__ state, TIO* __restrict__ y, int64_t rows, int H, int P, int G) {
+    float* __restrict__ state, TIO* __restrict__ y, int64_t rows, int H, int P, int G, DtOpts dto) {
   constexpr int TPR = N / 4;                        // threads per state row
   constexpr int RPW = kThreads / TPR;               // rows per workgroup and pass
   const int tid = threadIdx.x;
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const int h = (int)(bh % H);
     const int64_t b = bh / H;
     const int g = h / (H / G);
-    const float d = dt[bh];
+    const float d = dt_pre(dt[bh], h, dto);
     const float alpha = __expf(d * A[h]);
     const float xp = to_f32(x[r]);
     const float4 bv = IO4<TIO>::load(Bm + (b * G + g) * N + 4 * sub);
@@ -93,7 +93,7 @@ hipError_t launch_io(const Plan& p, const void* x, const float* dt, const float*
     const int64_t grid = (rows + per_wg - 1) / per_wg;
     kern<<<dim3((unsigned)grid), kThreads, 0, s>>>(
         static_cast<const TIO*>(x), dt, A, static_cast<const TIO*>(B), static_cast<const TIO*>(C), D, state,
-        static_cast<TIO*>(y), rows, (int)p.H, (int)p.P, (int)p.G);
+        static_cast<TIO*>(y), rows, (int)p.H, (int)p.P, (int)p.G, p.dto);
     return hipGetLastError();
   };
   switch (p.N) {

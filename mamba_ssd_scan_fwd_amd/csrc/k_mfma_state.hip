@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const float* __restrict__ dt, const float* __restrict__ A,
     float* __restrict__ dA_cs, float* __restrict__ dtc,
-    uint16_t* __restrict__ states, int64_t L, int H, int G, int N, int64_t nc, int HB) {
+    uint16_t* __restrict__ states, int64_t L, int H, int G, int N, int64_t nc, int HB, DtOpts dto) {
   using C = StateCfg<P, NB, Q>;
   constexpr int KS = C::KS;
   constexpr int TAB_U4 = FUSED ? C::TAB_FLOATS / 4 : 0;
@@ -99,7 +99,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     // wavefront scan per head ----
     if (tid < Q) {
       const float* drow = dt + (b * L + t0 + min(tid, rows - 1)) * H + h0;
-      for (int hh = 0; hh < HB; ++hh) tab[(2 * hh + 1) * Q + tid] = tid < rows ? drow[hh] : 0.f;
+      for (int hh = 0; hh < HB; ++hh)
+        tab[(2 * hh + 1) * Q + tid] = tid < rows ? dt_pre(drow[hh], h0 + hh, dto) : 0.f;
     }
     __syncthreads();
     constexpr int QPL = Q / 64;
@@ -295,7 +296,7 @@ hipError_t launch_pnq(const Plan& p, const void* x, const void* B, const float* 
   const int64_t grid = p.batch * p.nc * (p.H / hb) * nnb;
   chunk_state_mfma_kernel<P, NB, Q, FUSED><<<dim3((unsigned)grid), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), dt, A, cs, dtc,
-      static_cast<uint16_t*>(st), p.L, (int)p.H, (int)p.G, (int)p.N, p.nc, hb);
+      static_cast<uint16_t*>(st), p.L, (int)p.H, (int)p.G, (int)p.N, p.nc, hb, p.dto);
   return hipGetLastError();
 }
 

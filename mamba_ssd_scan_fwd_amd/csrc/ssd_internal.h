@@ -10,8 +10,16 @@ namespace ssd {
 
 enum IoType : int { kF32 = 0, kBF16 = 1 };
 
+// dt preprocessing (bias, softplus, clamp) as the descriptor asks for it.
+struct DtOpts {
+  const float* bias;  // [H] or nullptr
+  int softplus, clamp;
+  float lo, hi;
+};
+
 // A validated problem plus the chosen chunk length.
 struct Plan {
+  DtOpts dto;
   int64_t batch, L, H, P, N, G;
   int io;       // IoType of x, B, C, y and of the chunk states
   int Q;        // chunk length

@@ -16,6 +16,8 @@ Contents (all in ``oracle.ssd_oracle``):
 * ``chunk_cumsum``, ``chunk_local_states``, ``chunk_entry_states`` -- the
   intermediate quantities each step of the chunked path produces, computed
   from their plain definitions, for per-step parity.
+* ``dt_preprocess``    -- the optional dt transformation (bias, softplus,
+  clamp) applied before the recurrence.
 
 Every function is pinned by ``tests/test_oracle_pins.py``.
 """
@@ -29,4 +31,5 @@ from .ssd_oracle import (  # noqa: F401
     chunk_local_states,
     chunk_entry_states,
     group_of_head,
+    dt_preprocess,
 )

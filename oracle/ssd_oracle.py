@@ -54,6 +54,7 @@ __all__ = [
     "chunk_local_states",
     "chunk_entry_states",
     "group_of_head",
+    "dt_preprocess",
 ]
 
 
@@ -94,6 +95,25 @@ def _expand_groups(M, H):
     """[b, L, G, N] -> [b, L, H, N] with the contiguous head->group map."""
     G = M.shape[2]
     return np.repeat(M, H // G, axis=2)
+
+
+def dt_preprocess(dt, dt_bias=None, softplus=False, limit=None):
+    """dt as the layer may transform it before the recurrence, fp64: a
+    per-head bias added first, then softplus(z) = log(1 + e^z), then a clamp
+    to [lo, hi]. The pages do not spell this step out (they name the layer's
+    parts only); the order is the one the workloads' dt recipe uses (softplus,
+    then the clamp), with the bias inside the softplus.
+
+    dt [..., H], dt_bias [H] or None, limit (lo, hi) or None.
+    """
+    z = _f64(dt)
+    if dt_bias is not None:
+        z = z + _f64(dt_bias)
+    if softplus:
+        z = np.logaddexp(0.0, z)  # log(e^0 + e^z), without overflow
+    if limit is not None:
+        z = np.minimum(np.maximum(z, float(limit[0])), float(limit[1]))
+    return z
 
 
 def ssd_recurrent(x, dt, A, B, C, D=None, init_state=None):

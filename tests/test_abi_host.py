@@ -210,8 +210,21 @@ def test_step_entry_points_validate_too():
 
 
 def test_desc_struct_layout():
-    # int64 x 6 followed by two int32: 56 bytes, no padding surprises
-    assert ctypes.sizeof(SSDDesc) == 56
+    # int64 x 6, two int32, a pointer, two int32, two float: 80 bytes
+    assert ctypes.sizeof(SSDDesc) == 80
+    assert SSDDesc.dt_bias.offset == 56 and SSDDesc.dt_max.offset == 76
+
+
+def test_dt_preprocessing_fields_are_validated():
+    L = lib()
+    n = ctypes.c_size_t()
+    d = desc()
+    d.dt_clamp, d.dt_min, d.dt_max = 1, 0.2, 0.1
+    assert L.ssd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == SHAPE
+    d.dt_min = 0.1
+    assert L.ssd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == OK
+    d.dt_bias = BASE + 2
+    assert L.ssd_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == ALIGN
 
 
 def test_decode_step_validates():

@@ -456,3 +456,74 @@ def test_decode_step_large_batch_sampled():
         yr, hr = ssd_recurrent(*(np64(sl[k]) for k in ("x", "dt", "A", "B", "C", "D", "init_state")))
         check_rel(np64(y[b:b + 1]), yr[:, 0], TOL["bf16"], f"decode y b={b}")
         check_rel(np64(state[b:b + 1]), hr, 1e-6, f"decode state b={b}")
+
+
+# ---- dt preprocessing (bias, softplus, clamp) on every entry point -----------
+
+def _raw_dt_case(cfg, seed):
+    """The workload's inputs with dt replaced by raw pre-activation values
+    z ~ N(mu, 1) and a per-head bias ~ N(0, 0.5^2), both drawn from a seeded
+    CPU generator."""
+    inp = make_inputs(cfg, seed=seed)
+    g = torch.Generator().manual_seed(1000 + seed)
+    inp["dt"] = torch.randn(inp["dt"].shape, generator=g) + cfg.dt_mu
+    bias = 0.5 * torch.randn(cfg.nheads, generator=g)
+    return inp, bias
+
+
+@pytest.mark.parametrize("io,Q,L,G,limit", [("bf16", 256, 600, 2, (1e-3, 0.1)), ("bf16", 128, 333, 1, None),
+                                            ("fp32", 64, 150, 2, (1e-3, 0.1))])
+def test_forward_with_dt_preprocessing(io, Q, L, G, limit):
+    from oracle import dt_preprocess
+    cfg = BASE.with_(seqlen=L, io_dtype=io, ngroups=G, nheads=4, init_state=True)
+    inp, bias = _raw_dt_case(cfg, seed=33)
+    d = to_dev(inp)
+    pre = dict(bias=bias.to(DEV), softplus=True, limit=limit)
+    note(f"[gpu] forward with dt preprocessing {io} Q={Q} L={L} limit={limit}")
+    y, hT = ssd().forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], chunk_size=Q,
+                          dt_pre=pre)
+    cs, dtc = ssd().chunk_cumsum(d["dt"], d["A"], headdim=cfg.headdim, dstate=cfg.dstate, ngroups=G,
+                                 io_dtype=io, chunk_size=Q, dt_pre=pre)
+    torch.cuda.synchronize()
+    dt_eff = dt_preprocess(np64(inp["dt"]), np64(bias), softplus=True, limit=limit)
+    yr, hr = ssd_recurrent(np64(inp["x"]), dt_eff, *(np64(inp[k]) for k in ("A", "B", "C", "D", "init_state")))
+    check_rel(np64(y), yr, TOL[io], f"y with dt preprocessing {io}")
+    check_rel(np64(hT), hr, TOL[io], f"final state with dt preprocessing {io}")
+    # step 1 alone: dt_chunked is the preprocessed dt (fp32 softplus), 0 past the end
+    dref = np.zeros(np64(dtc).shape)
+    for c in range(dref.shape[2]):
+        n = min(Q, L - c * Q)
+        dref[:, :, c, :n] = dt_eff[:, c * Q:c * Q + n, :].transpose(0, 2, 1)
+    assert np.max(np.abs(np64(dtc) - dref)) <= 2e-6 * np.max(np.abs(dref))
+    assert np.all(np64(dtc)[:, :, -1, L - (dref.shape[2] - 1) * Q:] == 0)
+
+
+def test_decode_step_with_dt_preprocessing():
+    from oracle import dt_preprocess
+    cfg = BASE.with_(batch=3, seqlen=1, nheads=4, ngroups=2, init_state=True)
+    inp, bias = _raw_dt_case(cfg, seed=34)
+    d = to_dev(inp)
+    state = d["init_state"].clone()
+    pre = dict(bias=bias.to(DEV), softplus=True, limit=(1e-3, 0.1))
+    note("[gpu] decode step with dt preprocessing")
+    y = ssd().decode_step(d["x"][:, 0], d["dt"][:, 0], d["A"], d["B"][:, 0], d["C"][:, 0], d["D"], state,
+                          dt_pre=pre)
+    torch.cuda.synchronize()
+    dt_eff = dt_preprocess(np64(inp["dt"]), np64(bias), softplus=True, limit=(1e-3, 0.1))
+    yr, hr = ssd_recurrent(np64(inp["x"]), dt_eff, *(np64(inp[k]) for k in ("A", "B", "C", "D", "init_state")))
+    check_rel(np64(y), yr[:, 0], TOL["bf16"], "decode y with dt preprocessing")
+    check_rel(np64(state), hr, 1e-6, "decode state with dt preprocessing")
+
+
+def test_fused_steps_with_dt_preprocessing_bitwise():
+    cfg = BASE.with_(seqlen=500, nheads=8, ngroups=2)
+    inp, bias = _raw_dt_case(cfg, seed=35)
+    d = to_dev(inp)
+    pre = dict(bias=bias.to(DEV), softplus=True, limit=(1e-3, 0.1))
+    note("[gpu] fused steps 1+2 with dt preprocessing, bitwise")
+    cs, dtc = ssd().chunk_cumsum(d["dt"], d["A"], headdim=cfg.headdim, dstate=cfg.dstate, ngroups=2,
+                                 io_dtype="bf16", dt_pre=pre)
+    st = ssd().chunk_state(d["x"], d["B"], cs, dtc)
+    cs2, dtc2, st2 = ssd().cumsum_chunk_state(d["x"], d["B"], d["dt"], d["A"], dt_pre=pre)
+    torch.cuda.synchronize()
+    assert torch.equal(cs, cs2) and torch.equal(dtc, dtc2) and torch.equal(st, st2)

@@ -31,6 +31,7 @@ import numpy as np
 import pytest
 
 from oracle import (
+    dt_preprocess,
     chunk_cumsum,
     chunk_entry_states,
     chunk_local_states,
@@ -325,3 +326,36 @@ def test_oracle_rejects_bad_shapes():
     x, dt, A, B, C, D, h0 = rand_inputs(rng, b=1, L=4, H=3, P=2, N=2, G=2, h0=True)
     with pytest.raises(ValueError):
         ssd_recurrent(x, dt, A, B, C, D, h0)  # H % G != 0
+
+
+# ---- dt preprocessing (bias, softplus, clamp) -----------------------------
+
+def test_softplus_closed_forms():
+    # softplus(0) = ln 2; softplus(ln(e^a - 1)) = a; softplus(z) - softplus(-z) = z
+    assert dt_preprocess(np.array([0.0]), softplus=True)[0] == pytest.approx(np.log(2.0), rel=1e-15)
+    a = np.array([1e-3, 0.1, 1.0, 7.5])
+    assert np.allclose(dt_preprocess(np.log(np.expm1(a)), softplus=True), a, rtol=1e-13, atol=0)
+    z = np.random.default_rng(40).normal(0, 5, 1000)
+    sp = dt_preprocess(z, softplus=True)
+    sn = dt_preprocess(-z, softplus=True)
+    assert np.max(np.abs(sp - sn - z)) < 1e-12
+    assert np.all(sp > 0) and np.all(sp >= z)
+    # far in the tails: z itself above, e^z below, no overflow
+    big = dt_preprocess(np.array([800.0, -800.0, 40.0]), softplus=True)
+    assert big[0] == 800.0 and big[1] == 0.0 and big[2] == pytest.approx(40.0, rel=1e-15)
+
+
+def test_dt_bias_goes_inside_the_softplus_and_clamp_comes_last():
+    H = 5
+    bias = np.linspace(-1.0, 1.0, H)
+    dt = -np.tile(bias, (2, 3, 1))  # [b, L, H] with dt = -bias: softplus(0) everywhere
+    out = dt_preprocess(dt, bias, softplus=True)
+    assert np.allclose(out, np.log(2.0), rtol=1e-15, atol=0)
+    # clamp after softplus: ln 2 ~ 0.693 is clipped to the upper limit
+    out = dt_preprocess(dt, bias, softplus=True, limit=(0.1, 0.5))
+    assert np.all(out == 0.5)
+    out = dt_preprocess(dt, bias, softplus=True, limit=(0.9, 2.0))
+    assert np.all(out == 0.9)
+    # without softplus the bias is a plain per-head shift
+    raw = np.zeros((1, 2, H))
+    assert np.array_equal(dt_preprocess(raw, bias), np.broadcast_to(bias, raw.shape))
