@@ -186,6 +186,33 @@ SSD_API ssd_status_t ssd_chunk_scan(const ssd_desc_t* desc, const void* x, const
                             const float* D, const float* dA_cumsum, const float* dt_chunked,
                             const void* states, void* y, void* stream);
 
+/* ---- packed variable-length sequences -------------------------------------- */
+
+/* Workspace bytes for ssd_forward_varlen (desc->batch = 1, desc->seqlen = T
+ * total tokens, num_seqs sequences). Pure host computation. */
+SSD_API ssd_status_t ssd_workspace_bytes_varlen(const ssd_desc_t* desc, int64_t num_seqs, size_t* bytes);
+
+/* The forward pass over num_seqs sequences packed back to back: sequence s
+ * holds tokens [cu_seqlens[s], cu_seqlens[s+1]) of the [1, T, ...] arrays and
+ * runs the recurrence of ssd_forward on its own, from init_states[s] (zeros
+ * when init_states is NULL) to final_states[s] (not written when NULL). No
+ * state crosses a sequence boundary; no padding is needed.
+ *   cu_seqlens   [num_seqs + 1] int32, DEVICE pointer: 0 = cu[0] <= cu[1]
+ *                <= ... <= cu[num_seqs] = T. Offsets are clamped into [0, T]
+ *                on the device, so an invalid array gives wrong values but no
+ *                access outside the arguments.
+ *   x, y [1, T, H, P]; dt [1, T, H]; B, C [1, T, G, N]; A, D [H];
+ *   init_states, final_states [num_seqs, H, P, N] fp32 (may be the same
+ *   pointer; other overlaps are rejected).
+ *   workspace    nullable, at least ssd_workspace_bytes_varlen() bytes.
+ * Errors as ssd_forward; SSD_ERR_BAD_SHAPE also when desc->batch != 1,
+ * num_seqs < 1 or T >= 2^31. */
+SSD_API ssd_status_t ssd_forward_varlen(const ssd_desc_t* desc, const int32_t* cu_seqlens, int64_t num_seqs,
+                                const void* x, const float* dt, const float* A,
+                                const void* B, const void* C, const float* D,
+                                const float* init_states, void* y, float* final_states,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- the recurrent (decode) step ------------------------------------------ */
 
 /* One token of a batch of sequences through the recurrence, the state kept

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     decode_step,
     effective_chunk_size,
     forward,
+    forward_varlen,
     lib_path,
     load_library,
     make_desc,

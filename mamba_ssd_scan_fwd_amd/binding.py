@@ -29,6 +29,7 @@ __all__ = [
     "state_passing",
     "chunk_scan",
     "decode_step",
+    "forward_varlen",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -46,6 +47,8 @@ EXPORTED_SYMBOLS = (
     "ssd_state_passing",
     "ssd_chunk_scan",
     "ssd_decode_step",
+    "ssd_workspace_bytes_varlen",
+    "ssd_forward_varlen",
 )
 
 SSD_DTYPE_F32 = 0
@@ -121,6 +124,10 @@ def load_library():
         lib.ssd_chunk_scan.restype = ctypes.c_int
         lib.ssd_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.ssd_decode_step.restype = ctypes.c_int
+        lib.ssd_workspace_bytes_varlen.argtypes = [dp, ctypes.c_int64, ctypes.POINTER(sz)]
+        lib.ssd_workspace_bytes_varlen.restype = ctypes.c_int
+        lib.ssd_forward_varlen.argtypes = [dp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.ssd_forward_varlen.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -388,3 +395,46 @@ def decode_step(x, dt, A, B, C, D, state, *, y=None, dt_pre=None, stream=None):
                                           _ptr(D), _ptr(state), _ptr(y), _stream(stream, dev)),
            "ssd_decode_step")
     return y
+
+
+def forward_varlen(x, dt, A, B, C, D=None, *, cu_seqlens, init_states=None, chunk_size: int = 0,
+                   return_final_states: bool = True, y=None, final_states=None, workspace=None,
+                   dt_pre=None, stream=None):
+    """Packed variable-length sequences: x [1, T, H, P], dt [1, T, H],
+    B/C [1, T, G, N]; sequence s is tokens [cu_seqlens[s], cu_seqlens[s+1])
+    (cu_seqlens: int32 device tensor [S+1]). Returns (y, final_states [S, H, P, N]
+    or None)."""
+    dev = x.device
+    _need(x, "x", device=dev)
+    io = x.dtype
+    one, T, H, P = x.shape
+    if one != 1:
+        raise ValueError("packed sequences: x must be [1, T, H, P]")
+    _need(B, "B", io, dev)
+    G, N = B.shape[2], B.shape[3]
+    _need(C, "C", io, dev, B.shape)
+    _need(dt, "dt", torch.float32, dev, (1, T, H))
+    _need(A, "A", torch.float32, dev, (H,))
+    if D is not None:
+        _need(D, "D", torch.float32, dev, (H,))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    S = cu_seqlens.numel() - 1
+    if init_states is not None:
+        _need(init_states, "init_states", torch.float32, dev, (S, H, P, N))
+    desc = _desc_from(x, B, chunk_size, dt_pre)
+    if y is None:
+        y = torch.empty_like(x)
+    if final_states is None and return_final_states:
+        final_states = torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
+    n = ctypes.c_size_t()
+    lib = load_library()
+    _check(lib.ssd_workspace_bytes_varlen(ctypes.byref(desc), ctypes.c_int64(S), ctypes.byref(n)),
+           "ssd_workspace_bytes_varlen")
+    if workspace is None:
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    _check(lib.ssd_forward_varlen(ctypes.byref(desc), _ptr(cu_seqlens), ctypes.c_int64(S), _ptr(x), _ptr(dt),
+                                  _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_states), _ptr(y),
+                                  _ptr(final_states), _ptr(workspace),
+                                  ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                  _stream(stream, dev)), "ssd_forward_varlen")
+    return y, final_states

@@ -23,6 +23,10 @@ bool mfma_chunk_scan_supported(const Plan& p);
 hipError_t launch_chunk_state_mfma(const Plan& p, const void* x, const void* B,
                                    const float* dA_cs, const float* dtc, void* states,
                                    hipStream_t s);
+hipError_t launch_build_chunk_table(const int32_t* cu, int64_t S, int64_t T, int Q, int64_t nslots,
+                                    ChunkInfo* tab, hipStream_t s);
+hipError_t launch_empty_sequence_states(const int32_t* cu, int64_t S, int64_t T, int64_t HPN, const float* h0,
+                                        float* hT, hipStream_t s);
 // steps 1 and 2 in one launch (writes dA_cs and dtc as step 1 does)
 hipError_t launch_cumsum_chunk_state_mfma(const Plan& p, const void* x, const void* B, const float* dt,
                                           const float* A, float* dA_cs, float* dtc, void* states,
@@ -90,18 +94,36 @@ ssd_status_t make_plan(const ssd_desc_t* d, Plan* p) {
 }
 
 struct WsLayout {
-  size_t cs_off, dt_off, st_off, total;
+  size_t cs_off, dt_off, st_off, tab_off, total;
 };
 
-WsLayout ws_layout(const Plan& p) {
+// dA_cumsum, dt_chunked, states and (packed sequences) the chunk table, each
+// on a kWsAlign boundary. p.nc counts chunk slots.
+WsLayout ws_layout(const Plan& p, bool with_table = false) {
   WsLayout w;
   const size_t cs_bytes = size_t(p.batch * p.H * p.nc * p.Q) * sizeof(float);
   const size_t st_bytes = size_t(p.batch * p.H * p.nc * p.P * p.N) * p.io_bytes();
   w.cs_off = 0;
   w.dt_off = align_up(w.cs_off + cs_bytes, kWsAlign);
   w.st_off = align_up(w.dt_off + cs_bytes, kWsAlign);
-  w.total = align_up(w.st_off + st_bytes, kWsAlign);
+  w.tab_off = align_up(w.st_off + st_bytes, kWsAlign);
+  w.total = with_table ? align_up(w.tab_off + size_t(p.nc) * sizeof(ChunkInfo), kWsAlign) : w.tab_off;
   return w;
+}
+
+// Packed sequences: the descriptor's batch must be 1 and seqlen the total
+// token count T; the chunk slots are ceil(T/Q) + num_seqs (each sequence adds
+// at most one partial chunk).
+ssd_status_t make_varlen_plan(const ssd_desc_t* d, int64_t num_seqs, Plan* p) {
+  ssd_status_t st = make_plan(d, p);
+  if (st != SSD_OK) return st;
+  if (p->batch != 1 || num_seqs < 1 || num_seqs > (int64_t(1) << 31) - 1) return SSD_ERR_BAD_SHAPE;
+  if (p->L >= (int64_t(1) << 31)) return SSD_ERR_BAD_SHAPE;  // token offsets are 32-bit
+  const int64_t slots = (p->L + p->Q - 1) / p->Q + num_seqs;
+  if (p->H * slots > kMaxElems / (p->P * p->N)) return SSD_ERR_BAD_SHAPE;
+  if (p->H * slots * (p->Q / 16) >= (int64_t(1) << 31)) return SSD_ERR_BAD_SHAPE;
+  p->nc = slots;
+  return SSD_OK;
 }
 
 
@@ -246,6 +268,76 @@ ssd_status_t ssd_forward(const ssd_desc_t* desc, const void* x, const float* dt,
 
   hipError_t e = ssd::run_cumsum_chunk_state(p, x, B, dt, A, cs, dtc, states, s);
   if (e == hipSuccess) e = ssd::launch_state_passing(p, states, cs, init_state, final_state, s);
+  if (e == hipSuccess) e = ssd::run_chunk_scan(p, x, B, C, D, cs, dtc, states, y, s);
+  if (owned) {
+    const hipError_t fe = hipFreeAsync(wbase, s);
+    if (e == hipSuccess) e = fe;
+  }
+  return ssd::from_hip(e);
+}
+
+ssd_status_t ssd_workspace_bytes_varlen(const ssd_desc_t* desc, int64_t num_seqs, size_t* bytes) {
+  if (bytes == nullptr) return SSD_ERR_NULL_POINTER;
+  Plan p;
+  const ssd_status_t st = ssd::make_varlen_plan(desc, num_seqs, &p);
+  if (st != SSD_OK) return st;
+  *bytes = ssd::ws_layout(p, true).total;
+  return SSD_OK;
+}
+
+ssd_status_t ssd_forward_varlen(const ssd_desc_t* desc, const int32_t* cu_seqlens, int64_t num_seqs,
+                                const void* x, const float* dt, const float* A, const void* B, const void* C,
+                                const float* D, const float* init_states, void* y, float* final_states,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  ssd_status_t st = ssd::make_varlen_plan(desc, num_seqs, &p);
+  if (st != SSD_OK) return st;
+  if (!cu_seqlens || !x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL_POINTER;
+  if (!ssd::aligned(x, 16) || !ssd::aligned(B, 16) || !ssd::aligned(C, 16) || !ssd::aligned(y, 16) ||
+      !ssd::aligned(init_states, 16) || !ssd::aligned(final_states, 16) || !ssd::aligned(dt, 4) ||
+      !ssd::aligned(A, 4) || !ssd::aligned(D, 4) || !ssd::aligned(cu_seqlens, 4) ||
+      !ssd::aligned(workspace, ssd::kWsAlign))
+    return SSD_ERR_ALIGNMENT;
+  const ssd::WsLayout ws = ssd::ws_layout(p, true);
+  if (workspace != nullptr && workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
+
+  const size_t io = p.io_bytes();
+  const size_t xy_bytes = size_t(p.L * p.H * p.P) * io;
+  const size_t bc_bytes = size_t(p.L * p.G * p.N) * io;
+  const size_t st_bytes = size_t(num_seqs * p.H * p.P * p.N) * sizeof(float);
+  const ssd::Range in[] = {ssd::range_of(x, xy_bytes), ssd::range_of(dt, size_t(p.L * p.H) * sizeof(float)),
+                           ssd::range_of(A, size_t(p.H) * sizeof(float)), ssd::range_of(B, bc_bytes),
+                           ssd::range_of(C, bc_bytes), ssd::range_of(D, size_t(p.H) * sizeof(float)),
+                           ssd::range_of(init_states, st_bytes),
+                           ssd::range_of(cu_seqlens, size_t(num_seqs + 1) * sizeof(int32_t))};
+  const ssd::Range ry = ssd::range_of(y, xy_bytes);
+  const ssd::Range rf = ssd::range_of(final_states, st_bytes);
+  const ssd::Range rw = ssd::range_of(workspace, ws.total);
+  for (const ssd::Range& r : in) {
+    if (ssd::overlap(ry, r) || ssd::overlap(rw, r)) return SSD_ERR_ALIAS;
+    if (ssd::overlap(rf, r) && !(r.lo == reinterpret_cast<uintptr_t>(init_states) && rf.lo == r.lo))
+      return SSD_ERR_ALIAS;
+  }
+  if (ssd::overlap(ry, rf) || ssd::overlap(ry, rw) || ssd::overlap(rf, rw)) return SSD_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* wbase = workspace;
+  bool owned = false;
+  if (wbase == nullptr) {
+    if (hipMallocAsync(&wbase, ws.total, s) != hipSuccess) return SSD_ERR_HIP;
+    owned = true;
+  }
+  char* w = static_cast<char*>(wbase);
+  float* cs = reinterpret_cast<float*>(w + ws.cs_off);
+  float* dtc = reinterpret_cast<float*>(w + ws.dt_off);
+  void* states = w + ws.st_off;
+  ssd::ChunkInfo* tab = reinterpret_cast<ssd::ChunkInfo*>(w + ws.tab_off);
+  p.ctab = tab;
+  hipError_t e = ssd::launch_build_chunk_table(cu_seqlens, num_seqs, p.L, p.Q, p.nc, tab, s);
+  if (e == hipSuccess) e = ssd::run_cumsum_chunk_state(p, x, B, dt, A, cs, dtc, states, s);
+  if (e == hipSuccess) e = ssd::launch_state_passing(p, states, cs, init_states, final_states, s);
+  if (e == hipSuccess && final_states != nullptr)
+    e = ssd::launch_empty_sequence_states(cu_seqlens, num_seqs, p.L, p.H * p.P * p.N, init_states, final_states, s);
   if (e == hipSuccess) e = ssd::run_chunk_scan(p, x, B, C, D, cs, dtc, states, y, s);
   if (owned) {
     const hipError_t fe = hipFreeAsync(wbase, s);

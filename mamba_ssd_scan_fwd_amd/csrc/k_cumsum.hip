@@ -26,7 +26,7 @@ template <int Q>
 __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(
     const float* __restrict__ dt, const float* __restrict__ A,
     float* __restrict__ dA_cs, float* __restrict__ dtc,
-    int64_t L, int H, int64_t nc, DtOpts dto) {
+    int64_t L, int H, int64_t nc, DtOpts dto, const ChunkInfo* __restrict__ ctab) {
   constexpr int QPL = Q / 64;  // positions per lane
   __shared__ float tile[Q][kHB + 1];
   const int64_t c = blockIdx.x;
@@ -35,11 +35,13 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(
   const int hb = min(kHB, H - h0);
   const int tid = threadIdx.x;
 
+  int64_t row0;
+  int rows;
+  chunk_span(ctab, b, c, L, Q, row0, rows);
   for (int idx = tid; idx < Q * kHB; idx += kThreads) {
     const int i = idx / kHB, hh = idx % kHB;
-    const int64_t t = c * Q + i;
     float v = 0.f;
-    if (hh < hb && t < L) v = dt_pre(dt[(b * L + t) * H + h0 + hh], h0 + hh, dto);
+    if (hh < hb && i < rows) v = dt_pre(dt[(row0 + i) * H + h0 + hh], h0 + hh, dto);
     tile[i][hh] = v;
   }
   __syncthreads();
@@ -69,13 +71,13 @@ hipError_t launch_chunk_cumsum(const Plan& p, const float* dt, const float* A,
   dim3 grid((unsigned)p.nc, (unsigned)p.batch, (unsigned)((p.H + kHB - 1) / kHB));
   switch (p.Q) {
     case 64:
-      chunk_cumsum_kernel<64><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto);
+      chunk_cumsum_kernel<64><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab);
       break;
     case 128:
-      chunk_cumsum_kernel<128><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto);
+      chunk_cumsum_kernel<128><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab);
       break;
     case 256:
-      chunk_cumsum_kernel<256><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto);
+      chunk_cumsum_kernel<256><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab);
       break;
     default:
       return hipErrorInvalidValue;

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
     const uint16_t* __restrict__ Cm, const float* __restrict__ D,
     const float* __restrict__ dA_cs, const float* __restrict__ dtc,
     const uint16_t* __restrict__ states, uint16_t* __restrict__ y,
-    int64_t L, int H, int G, int64_t nc, int HB) {
+    int64_t L, int H, int G, int64_t nc, int HB, const ChunkInfo* __restrict__ ctab) {
   using C = ScanCfg<P, N, Q>;
   constexpr int R = C::R, NM = C::NM, RG = C::RG, NTP = C::NTP, NK = C::NK;
   __shared__ __align__(16) unsigned char lds[C::TOTAL];
@@ -112,8 +112,10 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int64_t t0 = c * Q;
-  const int rows = (int)(L - t0 < Q ? L - t0 : Q);
+  int64_t row0;  // first token row of this chunk in the [batch * L] arrays
+  int rows;      // valid positions in this chunk
+  chunk_span(ctab, b, c, L, Q, row0, rows);
+  if (rows <= 0) return;  // unused slot of a packed-sequence table (uniform)
 
   // row groups of this wavefront: w and R-1-w
   int rk[RG], ik[RG];
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   // Rows past the end re-read the last row (their outputs are never stored).
   bf16x8_t Cr[RG][NK];
   {
-    const uint16_t* cbase = Cm + ((b * L + t0) * G + g) * N;
+    const uint16_t* cbase = Cm + (row0 * G + g) * N;
 #pragma unroll
     for (int k = 0; k < RG; ++k) {
       const uint32_t coff = (uint32_t)((min(ik[k], rows - 1) * G * N + (8 * g4 < N ? 8 * g4 : 0)) * 2);
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
       if (ci < CH) {
         const int j = ci / (C::NSW / 8), n0 = 8 * (ci % (C::NSW / 8));
         st16(sB + j * C::BPITCH + n0,
-             ld16_keep(Bm + ((b * L + t0 + min(j, rows - 1)) * G + g) * N + sl * 128 + n0, j < rows));
+             ld16_keep(Bm + ((row0 + min(j, rows - 1)) * G + g) * N + sl * 128 + n0, j < rows));
       }
     }
     __syncthreads();
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   // operations lets each wait cover exactly the loads it needs.
   auto fetch_head = [&](int h) {
     const int tid = opaque(threadIdx.x);
-    const uint16_t* xh = x + ((b * L + t0) * H + h) * P;
+    const uint16_t* xh = x + (row0 * H + h) * P;
 #pragma unroll
     for (int k = 0; k < C::XPT; ++k) {
       const int bi = min(tid + k * C::THREADS, C::XBLK - 1);
@@ -447,7 +449,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
     // epilogue: store. Rows past the end of the sequence fall outside the
     // buffer range and are dropped, so the store sequence is the same for
     // every chunk.
-    uint16_t* ybase = y + ((b * L + t0) * H + h) * P;
+    uint16_t* ybase = y + (row0 * H + h) * P;
     const __amdgpu_buffer_rsrc_t yr = buffer_range(ybase, (uint32_t)(((rows - 1) * (int64_t)H + 1) * P * 2));
 #pragma unroll
     for (int k = 0; k < RG; ++k) {
@@ -487,7 +489,8 @@ hipError_t launch_pnq(const Plan& p, const void* x, const void* B, const void* C
   const int64_t grid = p.batch * p.nc * (p.H / hb);
   chunk_scan_mfma_kernel<P, N, Q><<<dim3((unsigned)grid), Cfg::THREADS, 0, s>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(Cm), D,
-      cs, dtc, static_cast<const uint16_t*>(st), static_cast<uint16_t*>(y), p.L, (int)p.H, (int)p.G, p.nc, hb);
+      cs, dtc, static_cast<const uint16_t*>(st), static_cast<uint16_t*>(y), p.L, (int)p.H, (int)p.G, p.nc, hb,
+      p.ctab);
   return hipGetLastError();
 }
 

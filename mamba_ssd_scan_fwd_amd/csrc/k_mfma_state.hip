@@ -68,7 +68,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const float* __restrict__ dt, const float* __restrict__ A,
     float* __restrict__ dA_cs, float* __restrict__ dtc,
-    uint16_t* __restrict__ states, int64_t L, int H, int G, int N, int64_t nc, int HB, DtOpts dto) {
+    uint16_t* __restrict__ states, int64_t L, int H, int G, int N, int64_t nc, int HB, DtOpts dto,
+    const ChunkInfo* __restrict__ ctab) {
   using C = StateCfg<P, NB, Q>;
   constexpr int KS = C::KS;
   constexpr int TAB_U4 = FUSED ? C::TAB_FLOATS / 4 : 0;
@@ -90,15 +91,17 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int64_t t0 = c * Q;
-  const int rows = (int)(L - t0 < Q ? L - t0 : Q);  // valid positions in this chunk
+  int64_t row0;  // first token row of this chunk in the [batch * L] arrays
+  int rows;      // valid positions in this chunk
+  chunk_span(ctab, b, c, L, Q, row0, rows);
+  if (rows <= 0) return;  // unused slot of a packed-sequence table (uniform)
   const int wn = wave % C::WN, wp = wave / C::WN;
 
   if constexpr (FUSED) {
     // ---- step 1 for this chunk and these heads: dt tile, then one
     // wavefront scan per head ----
     if (tid < Q) {
-      const float* drow = dt + (b * L + t0 + min(tid, rows - 1)) * H + h0;
+      const float* drow = dt + (row0 + min(tid, rows - 1)) * H + h0;
       for (int hh = 0; hh < HB; ++hh)
         tab[(2 * hh + 1) * Q + tid] = tid < rows ? dt_pre(drow[hh], h0 + hh, dto) : 0.f;
     }
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
         const int j = 8 * jb + rr;
-        r[rr] = ld16_keep(Bm + ((b * L + t0 + min(j, rows - 1)) * G + g) * N + nb * NB + 8 * cb, j < rows);
+        r[rr] = ld16_keep(Bm + ((row0 + min(j, rows - 1)) * G + g) * N + nb * NB + 8 * cb, j < rows);
       }
       transpose8x8(r, o);
       // column n = 8cb + s holds B[8jb .. 8jb+7][n]: one fragment slot
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
       for (int rr = 0; rr < 8; ++rr) {
         // clamped row, always in bounds; rows past the end are zeroed later
         const int j = 8 * jb + rr;
-        xr[k][rr] = ld16(x + ((b * L + t0 + min(j, rows - 1)) * H + h) * P + 8 * cb);
+        xr[k][rr] = ld16(x + ((row0 + min(j, rows - 1)) * H + h) * P + 8 * cb);
       }
     }
   };
@@ -296,7 +299,7 @@ hipError_t launch_pnq(const Plan& p, const void* x, const void* B, const float* 
   const int64_t grid = p.batch * p.nc * (p.H / hb) * nnb;
   chunk_state_mfma_kernel<P, NB, Q, FUSED><<<dim3((unsigned)grid), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), dt, A, cs, dtc,
-      static_cast<uint16_t*>(st), p.L, (int)p.H, (int)p.G, (int)p.N, p.nc, hb, p.dto);
+      static_cast<uint16_t*>(st), p.L, (int)p.H, (int)p.G, (int)p.N, p.nc, hb, p.dto, p.ctab);
   return hipGetLastError();
 }
 

@@ -24,7 +24,8 @@ template <typename TIO>
 __global__ __launch_bounds__(kThreads) void chunk_state_simt_kernel(
     const TIO* __restrict__ x, const TIO* __restrict__ Bm,
     const float* __restrict__ dA_cs, const float* __restrict__ dtc,
-    TIO* __restrict__ states, int64_t L, int H, int G, int P, int N, int Q, int64_t nc) {
+    TIO* __restrict__ states, int64_t L, int H, int G, int P, int N, int Q, int64_t nc,
+    const ChunkInfo* __restrict__ ctab) {
   __shared__ float w[256];
   __shared__ float xs[kJT][128 + 1];
   __shared__ float bs[kJT][256 + 1];
@@ -34,6 +35,10 @@ __global__ __launch_bounds__(kThreads) void chunk_state_simt_kernel(
   const int h = (int)(bh % H);
   const int g = h / (H / G);
   const int tid = threadIdx.x;
+  int64_t row0;
+  int rows;
+  chunk_span(ctab, b, c, L, Q, row0, rows);
+  if (rows <= 0) return;  // unused slot of a packed-sequence table (uniform)
   const float* lc = dA_cs + (bh * nc + c) * Q;
   const float* dc = dtc + (bh * nc + c) * Q;
   const float lam = lc[Q - 1];
@@ -49,13 +54,13 @@ __global__ __launch_bounds__(kThreads) void chunk_state_simt_kernel(
       __syncthreads();
       for (int idx = tid; idx < kJT * P; idx += kThreads) {
         const int j = idx / P, p = idx % P;
-        const int64_t t = c * Q + j0 + j;
-        xs[j][p] = t < L ? w[j0 + j] * to_f32(x[((b * L + t) * H + h) * P + p]) : 0.f;
+        const int tl = j0 + j;
+        xs[j][p] = tl < rows ? w[j0 + j] * to_f32(x[((row0 + tl) * H + h) * P + p]) : 0.f;
       }
       for (int idx = tid; idx < kJT * N; idx += kThreads) {
         const int j = idx / N, n = idx % N;
-        const int64_t t = c * Q + j0 + j;
-        bs[j][n] = t < L ? to_f32(Bm[((b * L + t) * G + g) * N + n]) : 0.f;
+        const int tl = j0 + j;
+        bs[j][n] = tl < rows ? to_f32(Bm[((row0 + tl) * G + g) * N + n]) : 0.f;
       }
       __syncthreads();
 #pragma unroll
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_simt_kernel(
     const TIO* __restrict__ x, const TIO* __restrict__ Bm, const TIO* __restrict__ Cm,
     const float* __restrict__ D, const float* __restrict__ dA_cs,
     const float* __restrict__ dtc, const TIO* __restrict__ states, TIO* __restrict__ y,
-    int64_t L, int H, int G, int P, int N, int Q, int64_t nc) {
+    int64_t L, int H, int G, int P, int N, int Q, int64_t nc, const ChunkInfo* __restrict__ ctab) {
   __shared__ float cs[kIB][256 + 1];
   __shared__ float bs[kJT2][256 + 1];
   __shared__ float xs[kJT2][128 + 1];
@@ -113,13 +118,15 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_simt_kernel(
   const float* lc = dA_cs + (bh * nc + c) * Q;
   const float* dc = dtc + (bh * nc + c) * Q;
   const TIO* hin = states + (bh * nc + c) * (int64_t)P * N;
-  const int64_t t0 = c * Q + i0;
-  if (t0 >= L) return;  // whole row block past the end (uniform per block)
+  int64_t row0;
+  int rows;
+  chunk_span(ctab, b, c, L, Q, row0, rows);
+  if (i0 >= rows) return;  // whole row block past the end (uniform per block)
 
   for (int idx = tid; idx < kIB * N; idx += kThreads) {
     const int r = idx / N, n = idx % N;
-    const int64_t t = t0 + r;
-    cs[r][n] = t < L ? to_f32(Cm[((b * L + t) * G + g) * N + n]) : 0.f;
+    const int tl = i0 + r;
+    cs[r][n] = tl < rows ? to_f32(Cm[((row0 + tl) * G + g) * N + n]) : 0.f;
   }
   for (int r = tid; r < kIB; r += kThreads) li[r] = lc[i0 + r];
   __syncthreads();
@@ -143,13 +150,13 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_simt_kernel(
     __syncthreads();
     for (int idx = tid; idx < kJT2 * N; idx += kThreads) {
       const int j = idx / N, n = idx % N;
-      const int64_t t = c * Q + j0 + j;
-      bs[j][n] = t < L ? to_f32(Bm[((b * L + t) * G + g) * N + n]) : 0.f;
+      const int tl = j0 + j;
+      bs[j][n] = tl < rows ? to_f32(Bm[((row0 + tl) * G + g) * N + n]) : 0.f;
     }
     for (int idx = tid; idx < kJT2 * P; idx += kThreads) {
       const int j = idx / P, p = idx % P;
-      const int64_t t = c * Q + j0 + j;
-      xs[j][p] = t < L ? to_f32(x[((b * L + t) * H + h) * P + p]) : 0.f;
+      const int tl = j0 + j;
+      xs[j][p] = tl < rows ? to_f32(x[((row0 + tl) * H + h) * P + p]) : 0.f;
     }
     for (int j = tid; j < kJT2; j += kThreads) {
       lj[j] = lc[j0 + j];
@@ -187,9 +194,9 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_simt_kernel(
     const int o = k * kThreads + tid;
     if (o < kIB * P) {
       const int r = o / P, p = o % P;
-      const int64_t t = t0 + r;
-      if (t < L) {
-        const int64_t off = ((b * L + t) * H + h) * P + p;
+      const int tl = i0 + r;
+      if (tl < rows) {
+        const int64_t off = ((row0 + tl) * H + h) * P + p;
         y[off] = from_f32<TIO>(acc[k] + dh * to_f32(x[off]));
       }
     }
@@ -206,11 +213,11 @@ hipError_t launch_chunk_state_simt(const Plan& p, const void* x, const void* B,
     using T = __hip_bfloat16;
     chunk_state_simt_kernel<T><<<grid, kThreads, 0, s>>>(
         static_cast<const T*>(x), static_cast<const T*>(B), dA_cs, dtc, static_cast<T*>(states),
-        p.L, (int)p.H, (int)p.G, (int)p.P, (int)p.N, p.Q, p.nc);
+        p.L, (int)p.H, (int)p.G, (int)p.P, (int)p.N, p.Q, p.nc, p.ctab);
   } else {
     chunk_state_simt_kernel<float><<<grid, kThreads, 0, s>>>(
         static_cast<const float*>(x), static_cast<const float*>(B), dA_cs, dtc,
-        static_cast<float*>(states), p.L, (int)p.H, (int)p.G, (int)p.P, (int)p.N, p.Q, p.nc);
+        static_cast<float*>(states), p.L, (int)p.H, (int)p.G, (int)p.P, (int)p.N, p.Q, p.nc, p.ctab);
   }
   return hipGetLastError();
 }
@@ -224,12 +231,12 @@ hipError_t launch_chunk_scan_simt(const Plan& p, const void* x, const void* B, c
     chunk_scan_simt_kernel<T><<<grid, kThreads, 0, s>>>(
         static_cast<const T*>(x), static_cast<const T*>(B), static_cast<const T*>(C), D, dA_cs,
         dtc, static_cast<const T*>(states), static_cast<T*>(y), p.L, (int)p.H, (int)p.G,
-        (int)p.P, (int)p.N, p.Q, p.nc);
+        (int)p.P, (int)p.N, p.Q, p.nc, p.ctab);
   } else {
     chunk_scan_simt_kernel<float><<<grid, kThreads, 0, s>>>(
         static_cast<const float*>(x), static_cast<const float*>(B), static_cast<const float*>(C),
         D, dA_cs, dtc, static_cast<const float*>(states), static_cast<float*>(y), p.L, (int)p.H,
-        (int)p.G, (int)p.P, (int)p.N, p.Q, p.nc);
+        (int)p.G, (int)p.P, (int)p.N, p.Q, p.nc, p.ctab);
   }
   return hipGetLastError();
 }

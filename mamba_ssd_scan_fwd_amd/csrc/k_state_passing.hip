@@ -69,18 +69,22 @@ template <> struct Vec8<__hip_bfloat16> {
   }
 };
 
+// With a packed-sequence table (ctab != nullptr, batch 1) the walk over the
+// chunk slots restarts the state at the first chunk of every sequence (from
+// h0[seq] or zero), writes hT[seq] after its last chunk, and skips unused
+// slots; h0 and hT are then [num_seqs, H, P, N].
 template <typename TS, int PF>
 __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     TS* __restrict__ states, const float* __restrict__ dA_cs,
     const float* h0, float* hT,  // may be the same buffer (in-place update)
-    int64_t nc, int Q, int PN) {
+    int64_t nc, int Q, int PN, int H, const ChunkInfo* __restrict__ ctab) {
   const int64_t bh = blockIdx.x;
   const int e0 = (blockIdx.y * kThreads + threadIdx.x) * kVec;
   const bool active = e0 < PN;
   const int lane = threadIdx.x & 63;
 
   float h[kVec];
-  if (active && h0 != nullptr) {
+  if (active && h0 != nullptr && ctab == nullptr) {
     Vec8<float> v;
     v.load(h0 + bh * PN + e0);
     v.to(h);
@@ -109,18 +113,34 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
         }
         const float d = __int_as_float(
             __builtin_amdgcn_readlane(__float_as_int(dec), (int)(c & 63)));
+        ChunkInfo ci{0, 1, 0, 0};
+        if (ctab != nullptr) ci = ctab[c];  // same slot for the whole workgroup
         if (active) {
           float sv[kVec];
           ring[k].to(sv);
           if (c + PF < nc) ring[k].load(s + (c + PF) * PN);
-          Vec8<TS>::store(s + c * PN, h);
+          if (ci.rows > 0) {
+            if (ci.flags & kFirstChunk) {  // a new sequence starts here
+              if (h0 != nullptr) {
+                Vec8<float> v;
+                v.load(h0 + ((int64_t)ci.seq * H + bh) * PN + e0);
+                v.to(h);
+              } else {
 #pragma unroll
-          for (int e = 0; e < kVec; ++e) h[e] = fmaf(d, h[e], sv[e]);
+                for (int e = 0; e < kVec; ++e) h[e] = 0.f;
+              }
+            }
+            Vec8<TS>::store(s + c * PN, h);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) h[e] = fmaf(d, h[e], sv[e]);
+            if ((ci.flags & kLastChunk) && hT != nullptr)
+              Vec8<float>::store(hT + ((int64_t)ci.seq * H + bh) * PN + e0, h);
+          }
         }
       }
     }
   }
-  if (active && hT != nullptr) Vec8<float>::store(hT + bh * PN + e0, h);
+  if (active && hT != nullptr && ctab == nullptr) Vec8<float>::store(hT + bh * PN + e0, h);
 }
 
 template <typename TS>
@@ -129,7 +149,7 @@ hipError_t launch_typed(const Plan& p, void* states, const float* dA_cs,
   const int PN = (int)(p.P * p.N);
   dim3 grid((unsigned)(p.batch * p.H), (unsigned)((PN + kThreads * kVec - 1) / (kThreads * kVec)));
   state_passing_kernel<TS, 8><<<grid, kThreads, 0, s>>>(
-      static_cast<TS*>(states), dA_cs, h0, hT, p.nc, p.Q, PN);
+      static_cast<TS*>(states), dA_cs, h0, hT, p.nc, p.Q, PN, (int)p.H, p.ctab);
   return hipGetLastError();
 }
 

@@ -17,9 +17,18 @@ struct DtOpts {
   float lo, hi;
 };
 
+// Where chunk c lies when sequences are packed (variable lengths): tokens
+// [t0, t0 + rows) of the packed [T, ...] arrays, sequence `seq`, and flags
+// kFirstChunk / kLastChunk of that sequence. rows == 0 marks an unused slot.
+struct ChunkInfo {
+  int32_t t0, rows, seq, flags;
+};
+constexpr int32_t kFirstChunk = 1, kLastChunk = 2;
+
 // A validated problem plus the chosen chunk length.
 struct Plan {
   DtOpts dto;
+  const ChunkInfo* ctab = nullptr;  // packed sequences: per-chunk table (device), else null
   int64_t batch, L, H, P, N, G;
   int io;       // IoType of x, B, C, y and of the chunk states
   int Q;        // chunk length
@@ -42,6 +51,20 @@ hipError_t launch_chunk_scan(const Plan& p, const void* x, const void* B, const 
 
 hipError_t launch_decode_step(const Plan& p, const void* x, const float* dt, const float* A, const void* B,
                               const void* C, const float* D, float* state, void* y, hipStream_t s);
+
+// First row (of the [batch * L, ...] token arrays) and valid length of chunk
+// c of batch b: fixed-size chunks of each sequence, or the packed table.
+__device__ __forceinline__ void chunk_span(const ChunkInfo* tab, int64_t b, int64_t c, int64_t L, int Q,
+                                           int64_t& row0, int& rows) {
+  if (tab != nullptr) {
+    const ChunkInfo ci = tab[c];
+    row0 = ci.t0;
+    rows = ci.rows;
+  } else {
+    row0 = b * L + c * Q;
+    rows = (int)(L - c * Q < Q ? L - c * Q : Q);
+  }
+}
 
 // Element conversion helpers used by every kernel file.
 __device__ __forceinline__ float to_f32(float v) { return v; }

@@ -244,3 +244,34 @@ def test_decode_step_validates():
     q[6] = p[3]  # state over B
     assert L.ssd_decode_step(ctypes.byref(d1), *q, None) == ALIAS
     assert L.ssd_decode_step(ctypes.byref(desc(seqlen=1, headdim=48)), *p, None) == UNSUP
+
+
+def test_varlen_validates():
+    L = lib()
+    n = ctypes.c_size_t()
+    assert L.ssd_workspace_bytes_varlen(ctypes.byref(desc(batch=2)), 3, ctypes.byref(n)) == SHAPE
+    assert L.ssd_workspace_bytes_varlen(ctypes.byref(desc(batch=1)), 0, ctypes.byref(n)) == SHAPE
+    assert L.ssd_workspace_bytes_varlen(ctypes.byref(desc(batch=1, seqlen=1 << 31)), 4, ctypes.byref(n)) == SHAPE
+    d = desc(batch=1, seqlen=10000)
+    assert L.ssd_workspace_bytes_varlen(ctypes.byref(d), 7, ctypes.byref(n)) == OK
+    # chunk slots ceil(T/Q) + S: ceil(10000 / 256) + 7 = 47
+    q = ctypes.c_int32()
+    assert L.ssd_effective_chunk_size(ctypes.byref(d), ctypes.byref(q)) == OK and q.value == 256
+    slots = -(-10000 // 256) + 7
+    expect = 0
+    for nbytes in (64 * slots * 256 * 4, 64 * slots * 256 * 4, 64 * slots * 64 * 128 * 2, slots * 16):
+        expect += -(-nbytes // 256) * 256
+    assert n.value == expect
+    p = [ctypes.c_void_p(BASE + k * (1 << 30)) for k in range(12)]
+    # cu x dt A B C D h0 y hT ws
+    args = lambda q: (ctypes.byref(d), q[0], ctypes.c_int64(7), *q[1:10], q[10], ctypes.c_size_t(n.value), None)
+    assert L.ssd_forward_varlen(*args([None] + p[1:11])) == NULLP
+    q2 = list(p)
+    q2[0] = ctypes.c_void_p(BASE + 2)
+    assert L.ssd_forward_varlen(*args(q2)) == ALIGN
+    q2 = list(p)
+    q2[8] = p[1]  # y over x
+    assert L.ssd_forward_varlen(*args(q2)) == ALIAS
+    q2 = list(p)
+    q2[9] = ctypes.c_void_p(p[7].value + 4096)  # final_states partly over init_states
+    assert L.ssd_forward_varlen(*args(q2)) == ALIAS

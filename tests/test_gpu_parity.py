@@ -527,3 +527,61 @@ def test_fused_steps_with_dt_preprocessing_bitwise():
     cs2, dtc2, st2 = ssd().cumsum_chunk_state(d["x"], d["B"], d["dt"], d["A"], dt_pre=pre)
     torch.cuda.synchronize()
     assert torch.equal(cs, cs2) and torch.equal(dtc, dtc2) and torch.equal(st, st2)
+
+
+# ---- packed variable-length sequences ---------------------------------------
+
+def _packed_case(lengths, cfg, seed, init):
+    """Seeded inputs for sum(lengths) packed tokens (the workload recipe on a
+    [1, T] batch) and the int32 offsets."""
+    T = int(sum(lengths))
+    inp = make_inputs(cfg.with_(batch=1, seqlen=max(T, 1), init_state=False), seed=seed)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    h0 = None
+    if init:
+        g = torch.Generator().manual_seed(2000 + seed)
+        h0 = 0.1 * torch.randn((len(lengths), cfg.nheads, cfg.headdim, cfg.dstate), generator=g)
+    return inp, cu, h0
+
+
+@pytest.mark.parametrize("io,Q,init", [("bf16", 256, True), ("bf16", 64, False), ("fp32", 128, True)])
+def test_varlen_matches_oracle_per_sequence(io, Q, init):
+    lengths = [1, 300, 0, 64, 255, 256, 257, 17, 0, 700, 3]
+    cfg = BASE.with_(io_dtype=io, nheads=4, ngroups=2)
+    inp, cu, h0 = _packed_case(lengths, cfg, seed=36, init=init)
+    d = to_dev(inp)
+    cu_d = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    note(f"[gpu] varlen {io} Q={Q} init={init} lengths={lengths}")
+    y, hT = ssd().forward_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], cu_seqlens=cu_d,
+                                 init_states=None if h0 is None else h0.to(DEV), chunk_size=Q)
+    torch.cuda.synchronize()
+    yg, hg = np64(y), np64(hT)
+    for s, n in enumerate(lengths):
+        a, e = int(cu[s]), int(cu[s + 1])
+        h0s = None if h0 is None else np64(h0[s:s + 1])
+        if n == 0:
+            ref_h = np.zeros_like(hg[s]) if h0 is None else h0s[0]
+            assert np.array_equal(hg[s], ref_h), f"empty sequence {s}: final state must be its initial state"
+            continue
+        yr, hr = ssd_recurrent(*(np64(inp[k][:, a:e]) for k in ("x", "dt")), np64(inp["A"]),
+                               *(np64(inp[k][:, a:e]) for k in ("B", "C")), np64(inp["D"]), h0s)
+        check_rel(yg[:, a:e], yr, TOL[io], f"varlen y seq {s} (len {n})")
+        check_rel(hg[s:s + 1], hr, TOL[io], f"varlen final state seq {s} (len {n})")
+
+
+@pytest.mark.parametrize("L,Q", [(700, 256), (256, 256), (300, 64)])
+def test_varlen_with_equal_lengths_equals_batched_bitwise(L, Q):
+    """Equal lengths: every sequence starts where the batched layout's does,
+    so the packed path must give the batched path's bits."""
+    S = 3
+    cfg = BASE.with_(batch=S, seqlen=L, nheads=4, ngroups=2, init_state=True)
+    inp = make_inputs(cfg, seed=37)
+    d = to_dev(inp)
+    note(f"[gpu] varlen vs batched bitwise L={L} Q={Q}")
+    y1, h1 = ssd().forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], chunk_size=Q)
+    pk = {k: d[k].reshape(1, S * L, *d[k].shape[2:]) for k in ("x", "dt", "B", "C")}
+    cu = torch.arange(0, S * L + 1, L, dtype=torch.int32, device=DEV)
+    y2, h2 = ssd().forward_varlen(pk["x"], pk["dt"], d["A"], pk["B"], pk["C"], d["D"], cu_seqlens=cu,
+                                  init_states=d["init_state"], chunk_size=Q)
+    torch.cuda.synchronize()
+    assert torch.equal(y2.reshape(y1.shape), y1) and torch.equal(h2, h1)
