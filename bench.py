@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--kernel-reps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step and packed-sequence measurements")
     ap.add_argument("--cpu-sample-seqs", type=int, default=8)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain fp32 elementwise copy (negation) of MIB MiB, "
@@ -178,6 +178,46 @@ def decode_measure(cfg, batch, steps, dev):
     return {"workload": f"decode step, {batch} sequences x {cfg.name} layer (H {H}, P {P}, N {N}, G {G})",
             "batch": batch, "avg_us": round(us, 2), "tokens_per_s": round(batch / (us * 1e-6), 1),
             "algo_bytes": nbytes, "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def varlen_measure(cfg, steps, dev):
+    """The workload's tokens as packed sequences of mixed lengths (seeded;
+    same total as batch x seqlen): time per forward pass and tokens/s."""
+    import numpy as np
+    import torch
+
+    import mamba_ssd_scan_fwd_amd as ssd
+    from ssd_inputs import make_inputs
+
+    T = cfg.batch * cfg.seqlen
+    rng = np.random.default_rng(7)
+    w = rng.uniform(0.1, 1.0, size=4 * cfg.batch)
+    lengths = np.floor(w / w.sum() * T).astype(np.int64)
+    lengths[-1] += T - lengths.sum()
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device=dev)
+    inp = make_inputs(cfg.with_(batch=1, seqlen=T), seed=102)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    S = len(lengths)
+    y = torch.empty_like(d["x"])
+    hT = torch.empty((S, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run():
+        ssd.forward_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], cu_seqlens=cu, y=y, final_states=hT)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1e3
+    return {"workload": f"{S} packed sequences, {T} tokens in all (lengths {int(lengths.min())}..{int(lengths.max())}), "
+                        f"{cfg.name} layer", "num_seqs": S, "avg_us": round(us, 2),
+            "tokens_per_s": round(T / (us * 1e-6), 1)}
 
 
 def main():
@@ -348,6 +388,7 @@ def main():
     decode = None
     if not args.no_decode:
         decode = [decode_measure(cfg, bsz, 50, dev) for bsz in (cfg.batch, 256)]
+    varlen = None if args.no_decode else varlen_measure(cfg, 20, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -376,6 +417,7 @@ def main():
         "kernels": per_kernel,
         "cpu_baseline": cpu,
         "decode_step": decode,
+        "varlen": varlen,
     }
     print(json.dumps(line), flush=True)
 

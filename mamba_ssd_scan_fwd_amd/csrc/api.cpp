@@ -24,9 +24,7 @@ hipError_t launch_chunk_state_mfma(const Plan& p, const void* x, const void* B,
                                    const float* dA_cs, const float* dtc, void* states,
                                    hipStream_t s);
 hipError_t launch_build_chunk_table(const int32_t* cu, int64_t S, int64_t T, int Q, int64_t nslots,
-                                    ChunkInfo* tab, hipStream_t s);
-hipError_t launch_empty_sequence_states(const int32_t* cu, int64_t S, int64_t T, int64_t HPN, const float* h0,
-                                        float* hT, hipStream_t s);
+                                    ChunkInfo* tab, int2* seqtab, hipStream_t s);
 // steps 1 and 2 in one launch (writes dA_cs and dtc as step 1 does)
 hipError_t launch_cumsum_chunk_state_mfma(const Plan& p, const void* x, const void* B, const float* dt,
                                           const float* A, float* dA_cs, float* dtc, void* states,
@@ -94,7 +92,7 @@ ssd_status_t make_plan(const ssd_desc_t* d, Plan* p) {
 }
 
 struct WsLayout {
-  size_t cs_off, dt_off, st_off, tab_off, total;
+  size_t cs_off, dt_off, st_off, tab_off, seq_off, total;
 };
 
 // dA_cumsum, dt_chunked, states and (packed sequences) the chunk table, each
@@ -107,7 +105,8 @@ WsLayout ws_layout(const Plan& p, bool with_table = false) {
   w.dt_off = align_up(w.cs_off + cs_bytes, kWsAlign);
   w.st_off = align_up(w.dt_off + cs_bytes, kWsAlign);
   w.tab_off = align_up(w.st_off + st_bytes, kWsAlign);
-  w.total = with_table ? align_up(w.tab_off + size_t(p.nc) * sizeof(ChunkInfo), kWsAlign) : w.tab_off;
+  w.seq_off = align_up(w.tab_off + size_t(p.nc) * sizeof(ChunkInfo), kWsAlign);
+  w.total = with_table ? align_up(w.seq_off + size_t(p.nseq) * sizeof(int2), kWsAlign) : w.tab_off;
   return w;
 }
 
@@ -117,12 +116,13 @@ WsLayout ws_layout(const Plan& p, bool with_table = false) {
 ssd_status_t make_varlen_plan(const ssd_desc_t* d, int64_t num_seqs, Plan* p) {
   ssd_status_t st = make_plan(d, p);
   if (st != SSD_OK) return st;
-  if (p->batch != 1 || num_seqs < 1 || num_seqs > (int64_t(1) << 31) - 1) return SSD_ERR_BAD_SHAPE;
+  if (p->batch != 1 || num_seqs < 1 || num_seqs * p->H >= (int64_t(1) << 31)) return SSD_ERR_BAD_SHAPE;
   if (p->L >= (int64_t(1) << 31)) return SSD_ERR_BAD_SHAPE;  // token offsets are 32-bit
   const int64_t slots = (p->L + p->Q - 1) / p->Q + num_seqs;
   if (p->H * slots > kMaxElems / (p->P * p->N)) return SSD_ERR_BAD_SHAPE;
   if (p->H * slots * (p->Q / 16) >= (int64_t(1) << 31)) return SSD_ERR_BAD_SHAPE;
   p->nc = slots;
+  p->nseq = num_seqs;
   return SSD_OK;
 }
 
@@ -332,12 +332,12 @@ ssd_status_t ssd_forward_varlen(const ssd_desc_t* desc, const int32_t* cu_seqlen
   float* dtc = reinterpret_cast<float*>(w + ws.dt_off);
   void* states = w + ws.st_off;
   ssd::ChunkInfo* tab = reinterpret_cast<ssd::ChunkInfo*>(w + ws.tab_off);
+  int2* seqtab = reinterpret_cast<int2*>(w + ws.seq_off);
   p.ctab = tab;
-  hipError_t e = ssd::launch_build_chunk_table(cu_seqlens, num_seqs, p.L, p.Q, p.nc, tab, s);
+  p.seqtab = seqtab;
+  hipError_t e = ssd::launch_build_chunk_table(cu_seqlens, num_seqs, p.L, p.Q, p.nc, tab, seqtab, s);
   if (e == hipSuccess) e = ssd::run_cumsum_chunk_state(p, x, B, dt, A, cs, dtc, states, s);
   if (e == hipSuccess) e = ssd::launch_state_passing(p, states, cs, init_states, final_states, s);
-  if (e == hipSuccess && final_states != nullptr)
-    e = ssd::launch_empty_sequence_states(cu_seqlens, num_seqs, p.L, p.H * p.P * p.N, init_states, final_states, s);
   if (e == hipSuccess) e = ssd::run_chunk_scan(p, x, B, C, D, cs, dtc, states, y, s);
   if (owned) {
     const hipError_t fe = hipFreeAsync(wbase, s);

@@ -69,22 +69,31 @@ template <> struct Vec8<__hip_bfloat16> {
   }
 };
 
-// With a packed-sequence table (ctab != nullptr, batch 1) the walk over the
-// chunk slots restarts the state at the first chunk of every sequence (from
-// h0[seq] or zero), writes hT[seq] after its last chunk, and skips unused
-// slots; h0 and hT are then [num_seqs, H, P, N].
+// One chain per block row: chain bh = b*H + h walks chunks [0, nc) of its
+// sequence; with packed sequences (seqtab != nullptr, batch 1) chain
+// bh = s*H + h walks the seqtab[s].y chunk slots from seqtab[s].x of head h,
+// so every sequence is a chain of its own. h0 and hT are indexed by the chain.
 template <typename TS, int PF>
 __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     TS* __restrict__ states, const float* __restrict__ dA_cs,
     const float* h0, float* hT,  // may be the same buffer (in-place update)
-    int64_t nc, int Q, int PN, int H, const ChunkInfo* __restrict__ ctab) {
+    int64_t nc, int Q, int PN, int H, const int2* __restrict__ seqtab) {
   const int64_t bh = blockIdx.x;
   const int e0 = (blockIdx.y * kThreads + threadIdx.x) * kVec;
   const bool active = e0 < PN;
   const int lane = threadIdx.x & 63;
 
+  // this chain's chunks: states / dA_cs rows of (b, h) = row, slots [c_beg, c_beg + cnt)
+  int64_t row = bh, c_beg = 0, cnt = nc;
+  if (seqtab != nullptr) {
+    const int2 st = seqtab[bh / H];
+    row = bh % H;
+    c_beg = st.x;
+    cnt = st.y;
+  }
+
   float h[kVec];
-  if (active && h0 != nullptr && ctab == nullptr) {
+  if (active && h0 != nullptr) {
     Vec8<float> v;
     v.load(h0 + bh * PN + e0);
     v.to(h);
@@ -93,63 +102,48 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     for (int k = 0; k < kVec; ++k) h[k] = 0.f;
   }
 
-  TS* s = states + bh * nc * (int64_t)PN + e0;
-  const float* lam = dA_cs + bh * nc * Q + (Q - 1);
+  TS* s = states + (row * nc + c_beg) * (int64_t)PN + e0;
+  const float* lam = dA_cs + (row * nc + c_beg) * Q + (Q - 1);
 
   Vec8<TS> ring[PF];
 #pragma unroll
   for (int k = 0; k < PF; ++k)
-    if (active && k < nc) ring[k].load(s + (int64_t)k * PN);
+    if (active && k < cnt) ring[k].load(s + (int64_t)k * PN);
 
   float dec = 0.f;
-  for (int64_t c0 = 0; c0 < nc; c0 += PF) {
+  for (int64_t c0 = 0; c0 < cnt; c0 += PF) {
 #pragma unroll
     for (int k = 0; k < PF; ++k) {
       const int64_t c = c0 + k;
-      if (c < nc) {
+      if (c < cnt) {
         if ((c & 63) == 0) {  // refresh: lane l holds exp(Lam_{c+l})
           const int64_t cl = c + lane;
-          dec = cl < nc ? __expf(lam[cl * Q]) : 0.f;
+          dec = cl < cnt ? __expf(lam[cl * Q]) : 0.f;
         }
         const float d = __int_as_float(
             __builtin_amdgcn_readlane(__float_as_int(dec), (int)(c & 63)));
-        ChunkInfo ci{0, 1, 0, 0};
-        if (ctab != nullptr) ci = ctab[c];  // same slot for the whole workgroup
         if (active) {
           float sv[kVec];
           ring[k].to(sv);
-          if (c + PF < nc) ring[k].load(s + (c + PF) * PN);
-          if (ci.rows > 0) {
-            if (ci.flags & kFirstChunk) {  // a new sequence starts here
-              if (h0 != nullptr) {
-                Vec8<float> v;
-                v.load(h0 + ((int64_t)ci.seq * H + bh) * PN + e0);
-                v.to(h);
-              } else {
+          if (c + PF < cnt) ring[k].load(s + (c + PF) * PN);
+          Vec8<TS>::store(s + c * PN, h);
 #pragma unroll
-                for (int e = 0; e < kVec; ++e) h[e] = 0.f;
-              }
-            }
-            Vec8<TS>::store(s + c * PN, h);
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) h[e] = fmaf(d, h[e], sv[e]);
-            if ((ci.flags & kLastChunk) && hT != nullptr)
-              Vec8<float>::store(hT + ((int64_t)ci.seq * H + bh) * PN + e0, h);
-          }
+          for (int e = 0; e < kVec; ++e) h[e] = fmaf(d, h[e], sv[e]);
         }
       }
     }
   }
-  if (active && hT != nullptr && ctab == nullptr) Vec8<float>::store(hT + bh * PN + e0, h);
+  if (active && hT != nullptr) Vec8<float>::store(hT + bh * PN + e0, h);
 }
 
 template <typename TS>
 hipError_t launch_typed(const Plan& p, void* states, const float* dA_cs,
                         const float* h0, float* hT, hipStream_t s) {
   const int PN = (int)(p.P * p.N);
-  dim3 grid((unsigned)(p.batch * p.H), (unsigned)((PN + kThreads * kVec - 1) / (kThreads * kVec)));
+  const int64_t chains = p.seqtab != nullptr ? p.nseq * p.H : p.batch * p.H;
+  dim3 grid((unsigned)chains, (unsigned)((PN + kThreads * kVec - 1) / (kThreads * kVec)));
   state_passing_kernel<TS, 8><<<grid, kThreads, 0, s>>>(
-      static_cast<TS*>(states), dA_cs, h0, hT, p.nc, p.Q, PN, (int)p.H, p.ctab);
+      static_cast<TS*>(states), dA_cs, h0, hT, p.nc, p.Q, PN, (int)p.H, p.seqtab);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // Packed variable-length sequences: the per-chunk table every step reads in
-// place of fixed-size chunks, and the final state of empty sequences.
+// place of fixed-size chunks, and the per-sequence (first slot, chunk count)
+// table that state passing walks, one chain per sequence and head.
 //
 // Sequence s holds tokens [cu[s], cu[s+1]) of the packed arrays. Its
 // ceil(len/Q) chunks take consecutive table slots starting at the exclusive
@@ -32,7 +33,7 @@ __device__ __forceinline__ void seq_span(const int32_t* cu, int64_t s, int64_t T
 // 1024 sequences at a time, then each thread writes its sequence's slots.
 __global__ __launch_bounds__(kTabThreads) void build_chunk_table_kernel(
     const int32_t* __restrict__ cu, int64_t S, int64_t T, int Q, int64_t nslots,
-    ChunkInfo* __restrict__ tab) {
+    ChunkInfo* __restrict__ tab, int2* __restrict__ seqtab) {
   __shared__ int64_t wsum[kTabThreads / 64];
   __shared__ int64_t carry_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -55,6 +56,11 @@ __global__ __launch_bounds__(kTabThreads) void build_chunk_table_kernel(
     int64_t before = carry_s;
     for (int w = 0; w < wave; ++w) before += wsum[w];
     const int64_t first = before + incl - n;
+    if (s < S) {
+      // slots past the table (only for invalid offsets) are dropped
+      const int64_t fit = first >= nslots ? 0 : (first + n > nslots ? nslots - first : n);
+      seqtab[s] = make_int2((int)(first < nslots ? first : 0), (int)fit);
+    }
     for (int64_t k = 0; k < n; ++k) {
       const int64_t slot = first + k;
       if (slot >= nslots) break;
@@ -70,29 +76,11 @@ __global__ __launch_bounds__(kTabThreads) void build_chunk_table_kernel(
     tab[slot] = ChunkInfo{0, 0, -1, 0};
 }
 
-// hT[s] = h0[s] (or zero) for sequences without tokens: no chunk of theirs
-// reaches the state-passing step.
-__global__ __launch_bounds__(256) void empty_sequence_state_kernel(
-    const int32_t* __restrict__ cu, int64_t T, int64_t HPN, const float* h0, float* hT) {
-  const int64_t s = blockIdx.x;
-  int64_t start, len;
-  seq_span(cu, s, T, start, len);
-  if (len > 0) return;
-  for (int64_t e = threadIdx.x; e < HPN; e += blockDim.x)
-    hT[s * HPN + e] = h0 != nullptr ? h0[s * HPN + e] : 0.f;
-}
-
 }  // namespace
 
 hipError_t launch_build_chunk_table(const int32_t* cu, int64_t S, int64_t T, int Q, int64_t nslots,
-                                    ChunkInfo* tab, hipStream_t s) {
-  build_chunk_table_kernel<<<1, kTabThreads, 0, s>>>(cu, S, T, Q, nslots, tab);
-  return hipGetLastError();
-}
-
-hipError_t launch_empty_sequence_states(const int32_t* cu, int64_t S, int64_t T, int64_t HPN, const float* h0,
-                                        float* hT, hipStream_t s) {
-  empty_sequence_state_kernel<<<dim3((unsigned)S), 256, 0, s>>>(cu, T, HPN, h0, hT);
+                                    ChunkInfo* tab, int2* seqtab, hipStream_t s) {
+  build_chunk_table_kernel<<<1, kTabThreads, 0, s>>>(cu, S, T, Q, nslots, tab, seqtab);
   return hipGetLastError();
 }
 

@@ -24,11 +24,15 @@ struct ChunkInfo {
   int32_t t0, rows, seq, flags;
 };
 constexpr int32_t kFirstChunk = 1, kLastChunk = 2;
+// The chunk count of a sequence is also kept per sequence (first slot, count)
+// so that state passing can run one chain per sequence.
 
 // A validated problem plus the chosen chunk length.
 struct Plan {
   DtOpts dto;
   const ChunkInfo* ctab = nullptr;  // packed sequences: per-chunk table (device), else null
+  const int2* seqtab = nullptr;     // packed sequences: (first slot, chunk count) per sequence
+  int64_t nseq = 0;                 // packed sequences: their number
   int64_t batch, L, H, P, N, G;
   int io;       // IoType of x, B, C, y and of the chunk states
   int Q;        // chunk length

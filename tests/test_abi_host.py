@@ -259,7 +259,7 @@ def test_varlen_validates():
     assert L.ssd_effective_chunk_size(ctypes.byref(d), ctypes.byref(q)) == OK and q.value == 256
     slots = -(-10000 // 256) + 7
     expect = 0
-    for nbytes in (64 * slots * 256 * 4, 64 * slots * 256 * 4, 64 * slots * 64 * 128 * 2, slots * 16):
+    for nbytes in (64 * slots * 256 * 4, 64 * slots * 256 * 4, 64 * slots * 64 * 128 * 2, slots * 16, 7 * 8):
         expect += -(-nbytes // 256) * 256
     assert n.value == expect
     p = [ctypes.c_void_p(BASE + k * (1 << 30)) for k in range(12)]
