@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--kernel-reps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step and packed-sequence measurements")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step, packed-sequence and convolution measurements")
     ap.add_argument("--cpu-sample-seqs", type=int, default=8)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain fp32 elementwise copy (negation) of MIB MiB, "
@@ -220,6 +220,39 @@ def varlen_measure(cfg, steps, dev):
             "tokens_per_s": round(T / (us * 1e-6), 1)}
 
 
+def conv_measure(cfg, steps, dev):
+    """The short causal convolution (width 4, SiLU) on the workload's packed
+    [x | B | C] channels, split into x, B, C: time per call and algorithmic
+    GB/s (every input and output once)."""
+    import torch
+
+    import mamba_ssd_scan_fwd_amd as ssd
+
+    CH = cfg.nheads * cfg.headdim + 2 * cfg.ngroups * cfg.dstate
+    g = torch.Generator().manual_seed(103)
+    dt_ = torch.bfloat16 if cfg.io_dtype == "bf16" else torch.float32
+    u = torch.randn((cfg.batch, cfg.seqlen, CH), generator=g).to(dt_).to(dev)
+    w = (torch.randn((CH, 4), generator=g) / 4).to(dev)
+    bias = torch.randn(CH, generator=g).to(dev)
+    kw = dict(nheads=cfg.nheads, headdim=cfg.headdim, ngroups=cfg.ngroups, dstate=cfg.dstate, silu=True)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(3):
+        ssd.conv1d_split(u, w, bias, **kw)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        ssd.conv1d_split(u, w, bias, **kw)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1e3
+    nbytes = 2 * cfg.batch * cfg.seqlen * CH * (2 if cfg.io_dtype == "bf16" else 4)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"causal conv width 4 + SiLU, [{cfg.batch}, {cfg.seqlen}, {CH}] channels split into x, B, C",
+            "avg_us": round(us, 2), "algo_bytes": nbytes, "GB_per_s": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -389,6 +422,7 @@ def main():
     if not args.no_decode:
         decode = [decode_measure(cfg, bsz, 50, dev) for bsz in (cfg.batch, 256)]
     varlen = None if args.no_decode else varlen_measure(cfg, 20, dev)
+    conv = None if args.no_decode else conv_measure(cfg, 20, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -418,6 +452,7 @@ def main():
         "cpu_baseline": cpu,
         "decode_step": decode,
         "varlen": varlen,
+        "conv1d_split": conv,
     }
     print(json.dumps(line), flush=True)
 

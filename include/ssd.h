@@ -213,6 +213,30 @@ SSD_API ssd_status_t ssd_forward_varlen(const ssd_desc_t* desc, const int32_t* c
                                 const float* init_states, void* y, float* final_states,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- the short causal convolution before the SSM --------------------------- */
+
+/* Depthwise causal convolution over time of the packed token vector
+ * [x (h, p) | B (g, n) | C (g, n)], width K = conv_width in 1..4, then split
+ * into the x, B and C tensors ssd_forward reads (Telegram post "Mamba3" and
+ * "Mamba-3 : SSM optimise inference", section "Architecture revisitee": the
+ * short causal convolution of Mamba-1/2). Per channel ch of CH = H*P + 2*G*N:
+ *   z[t] = bias[ch] + sum_{k<K} weight[ch][k] * in[t - (K-1) + k],
+ *   out[t] = silu ? z * sigmoid(z) : z,
+ * with in[t < 0] = conv_state_in[b][ch][K-1+t] (zeros when it is NULL).
+ *   xbc             [batch, L, CH]        io dtype, 16-byte aligned
+ *   weight          [CH, K]               fp32
+ *   bias            [CH]                  fp32, nullable, 16-byte aligned
+ *   conv_state_in   [batch, CH, K-1]      fp32, nullable
+ *   conv_state_out  [batch, CH, K-1]      fp32, nullable: the last K-1 inputs
+ *                                         (continues the sequence in a later
+ *                                         call); must not overlap conv_state_in
+ *   x [batch, L, H, P], B, C [batch, L, G, N]   io dtype outputs
+ * Outputs must not overlap inputs or each other. */
+SSD_API ssd_status_t ssd_conv1d_split(const ssd_desc_t* desc, int32_t conv_width, const void* xbc,
+                              const float* weight, const float* bias, int32_t silu,
+                              const float* conv_state_in, float* conv_state_out,
+                              void* x, void* B, void* C, void* stream);
+
 /* ---- the recurrent (decode) step ------------------------------------------ */
 
 /* One token of a batch of sequences through the recurrence, the state kept

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     chunk_cumsum,
     chunk_scan,
     chunk_state,
+    conv1d_split,
     cumsum_chunk_state,
     decode_step,
     effective_chunk_size,

@@ -30,6 +30,7 @@ __all__ = [
     "chunk_scan",
     "decode_step",
     "forward_varlen",
+    "conv1d_split",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -49,6 +50,7 @@ EXPORTED_SYMBOLS = (
     "ssd_decode_step",
     "ssd_workspace_bytes_varlen",
     "ssd_forward_varlen",
+    "ssd_conv1d_split",
 )
 
 SSD_DTYPE_F32 = 0
@@ -128,6 +130,8 @@ def load_library():
         lib.ssd_workspace_bytes_varlen.restype = ctypes.c_int
         lib.ssd_forward_varlen.argtypes = [dp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.ssd_forward_varlen.restype = ctypes.c_int
+        lib.ssd_conv1d_split.argtypes = [dp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+        lib.ssd_conv1d_split.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -438,3 +442,27 @@ def forward_varlen(x, dt, A, B, C, D=None, *, cu_seqlens, init_states=None, chun
                                   ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                                   _stream(stream, dev)), "ssd_forward_varlen")
     return y, final_states
+
+
+def conv1d_split(xbc, weight, bias=None, *, nheads, headdim, ngroups, dstate, silu=True, conv_state_in=None,
+                 conv_state_out=None, stream=None):
+    """Short causal depthwise convolution of the packed [x | B | C] channels,
+    split into x [b, L, H, P], B and C [b, L, G, N]. weight [CH, K] fp32."""
+    dev = xbc.device
+    _need(xbc, "xbc", device=dev)
+    bsz, L, CH = xbc.shape
+    if CH != nheads * headdim + 2 * ngroups * dstate:
+        raise ValueError("xbc channels must be H*P + 2*G*N")
+    _need(weight, "weight", torch.float32, dev)
+    K = weight.shape[1]
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dev, (CH,))
+    desc = make_desc(bsz, L, nheads, headdim, dstate, ngroups, xbc.dtype, 0)
+    x = torch.empty((bsz, L, nheads, headdim), dtype=xbc.dtype, device=dev)
+    B = torch.empty((bsz, L, ngroups, dstate), dtype=xbc.dtype, device=dev)
+    C = torch.empty_like(B)
+    _check(load_library().ssd_conv1d_split(ctypes.byref(desc), ctypes.c_int32(K), _ptr(xbc), _ptr(weight),
+                                           _ptr(bias), ctypes.c_int32(1 if silu else 0), _ptr(conv_state_in),
+                                           _ptr(conv_state_out), _ptr(x), _ptr(B), _ptr(C), _stream(stream, dev)),
+           "ssd_conv1d_split")
+    return x, B, C

@@ -446,4 +446,38 @@ ssd_status_t ssd_decode_step(const ssd_desc_t* desc, const void* x, const float*
   return ssd::from_hip(ssd::launch_decode_step(p, x, dt, A, B, C, D, state, y, static_cast<hipStream_t>(stream)));
 }
 
+ssd_status_t ssd_conv1d_split(const ssd_desc_t* desc, int32_t conv_width, const void* xbc, const float* weight,
+                              const float* bias, int32_t silu, const float* conv_state_in, float* conv_state_out,
+                              void* x, void* B, void* C, void* stream) {
+  Plan p;
+  ssd_status_t st = ssd::make_plan(desc, &p);
+  if (st != SSD_OK) return st;
+  if (conv_width < 1 || conv_width > 4) return SSD_ERR_UNSUPPORTED;
+  if ((p.L + 63) / 64 > 65535) return SSD_ERR_BAD_SHAPE;  // token tiles along grid.y
+  if (!xbc || !weight || !x || !B || !C) return SSD_ERR_NULL_POINTER;
+  if (!ssd::aligned(xbc, 16) || !ssd::aligned(weight, 4) || !ssd::aligned(bias, 16) ||
+      !ssd::aligned(conv_state_in, 4) || !ssd::aligned(conv_state_out, 4) || !ssd::aligned(x, 16) ||
+      !ssd::aligned(B, 16) || !ssd::aligned(C, 16))
+    return SSD_ERR_ALIGNMENT;
+  const size_t io = p.io_bytes();
+  const int64_t CH = p.H * p.P + 2 * p.G * p.N;
+  const size_t km1 = size_t(conv_width - 1);
+  const ssd::Range ins[] = {ssd::range_of(xbc, size_t(p.batch * p.L * CH) * io),
+                            ssd::range_of(weight, size_t(CH * conv_width) * sizeof(float)),
+                            ssd::range_of(bias, bias ? size_t(CH) * sizeof(float) : 0),
+                            ssd::range_of(conv_state_in, conv_state_in ? size_t(p.batch * CH) * km1 * 4 : 0)};
+  const ssd::Range outs[] = {ssd::range_of(x, size_t(p.batch * p.L * p.H * p.P) * io),
+                             ssd::range_of(B, size_t(p.batch * p.L * p.G * p.N) * io),
+                             ssd::range_of(C, size_t(p.batch * p.L * p.G * p.N) * io),
+                             ssd::range_of(conv_state_out, conv_state_out ? size_t(p.batch * CH) * km1 * 4 : 0)};
+  for (int i = 0; i < 4; ++i) {
+    for (const ssd::Range& r : ins)
+      if (ssd::overlap(outs[i], r)) return SSD_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (ssd::overlap(outs[i], outs[j])) return SSD_ERR_ALIAS;
+  }
+  return ssd::from_hip(ssd::launch_conv1d_split(p, conv_width, xbc, weight, bias, silu != 0, conv_state_in,
+                                                conv_state_out, x, B, C, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

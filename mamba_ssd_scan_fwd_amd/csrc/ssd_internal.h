@@ -53,6 +53,8 @@ hipError_t launch_chunk_scan(const Plan& p, const void* x, const void* B, const 
                              const float* D, const float* dA_cs, const float* dtc,
                              const void* states, void* y, hipStream_t s);
 
+hipError_t launch_conv1d_split(const Plan& p, int K, const void* xbc, const float* w, const float* bias, int act,
+                               const float* st_in, float* st_out, void* x, void* B, void* C, hipStream_t s);
 hipError_t launch_decode_step(const Plan& p, const void* x, const float* dt, const float* A, const void* B,
                               const void* C, const float* D, float* state, void* y, hipStream_t s);
 

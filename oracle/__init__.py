@@ -18,6 +18,7 @@ Contents (all in ``oracle.ssd_oracle``):
   from their plain definitions, for per-step parity.
 * ``dt_preprocess``    -- the optional dt transformation (bias, softplus,
   clamp) applied before the recurrence.
+* ``causal_conv1d``    -- the short causal convolution in front of the SSM.
 
 Every function is pinned by ``tests/test_oracle_pins.py``.
 """
@@ -32,4 +33,5 @@ from .ssd_oracle import (  # noqa: F401
     chunk_entry_states,
     group_of_head,
     dt_preprocess,
+    causal_conv1d,
 )

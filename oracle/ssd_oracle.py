@@ -55,6 +55,7 @@ __all__ = [
     "chunk_entry_states",
     "group_of_head",
     "dt_preprocess",
+    "causal_conv1d",
 ]
 
 
@@ -114,6 +115,32 @@ def dt_preprocess(dt, dt_bias=None, softplus=False, limit=None):
     if limit is not None:
         z = np.minimum(np.maximum(z, float(limit[0])), float(limit[1]))
     return z
+
+
+def causal_conv1d(u, weight, bias=None, silu=False, state=None):
+    """The short causal convolution in front of the SSM, fp64: per channel,
+    z[t] = bias + sum_k weight[k] * u[t - (K-1) + k], with u before t = 0 taken
+    from `state` (the K-1 previous inputs, oldest first; zeros when None);
+    then z * sigmoid(z) when `silu`. The pages name this convolution (present
+    in Mamba-1 and Mamba-2) but give neither width nor activation; both are
+    parameters here.
+
+    u [b, L, CH], weight [CH, K], bias [CH] or None, state [b, CH, K-1] or None.
+    Returns (out [b, L, CH], the last K-1 inputs [b, CH, K-1]).
+    """
+    u = _f64(u)
+    w = _f64(weight)
+    bsz, L, CH = u.shape
+    K = w.shape[1]
+    prev = np.zeros((bsz, K - 1, CH)) if state is None else np.transpose(_f64(state), (0, 2, 1))
+    full = np.concatenate([prev, u], axis=1)  # [b, K-1+L, CH]: position t at index t + K-1
+    z = np.zeros((bsz, L, CH)) if bias is None else np.broadcast_to(_f64(bias), (bsz, L, CH)).copy()
+    for k in range(K):
+        z += w[None, None, :, k] * full[:, k:k + L, :]
+    if silu:
+        z = z / (1.0 + np.exp(-z))
+    last = np.transpose(full[:, L:L + K - 1, :], (0, 2, 1)) if K > 1 else np.zeros((bsz, CH, 0))
+    return z, last
 
 
 def ssd_recurrent(x, dt, A, B, C, D=None, init_state=None):

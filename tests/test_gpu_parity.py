@@ -585,3 +585,49 @@ def test_varlen_with_equal_lengths_equals_batched_bitwise(L, Q):
                                   init_states=d["init_state"], chunk_size=Q)
     torch.cuda.synchronize()
     assert torch.equal(y2.reshape(y1.shape), y1) and torch.equal(h2, h1)
+
+
+# ---- the short causal convolution (split into x, B, C) ------------------------
+
+@pytest.mark.parametrize("io,K,silu,bias,state", [("bf16", 4, True, True, True), ("bf16", 1, False, False, False),
+                                                  ("bf16", 2, True, False, True), ("fp32", 3, True, True, False)])
+def test_conv1d_split_matches_oracle(io, K, silu, bias, state):
+    from oracle import causal_conv1d
+    b, L, H, P, G, N = 2, 150, 4, 32, 2, 16
+    CH = H * P + 2 * G * N
+    g = torch.Generator().manual_seed(60 + K)
+    dt_ = torch.bfloat16 if io == "bf16" else torch.float32
+    u = torch.randn((b, L, CH), generator=g).to(dt_)
+    w = (torch.randn((CH, K), generator=g) / K).float()
+    bv = torch.randn(CH, generator=g).float() if bias else None
+    s0 = torch.randn((b, CH, K - 1), generator=g).float() if state else None
+    s_out = torch.full((b, CH, max(K - 1, 1)), float("nan"), device=DEV) if K > 1 else None
+    note(f"[gpu] conv1d split {io} K={K} silu={silu} bias={bias} state={state}")
+    x, B, C = ssd().conv1d_split(u.to(DEV), w.to(DEV), None if bv is None else bv.to(DEV), nheads=H, headdim=P,
+                                 ngroups=G, dstate=N, silu=silu, conv_state_in=None if s0 is None else s0.to(DEV),
+                                 conv_state_out=s_out)
+    torch.cuda.synchronize()
+    ref, last = causal_conv1d(np64(u), np64(w), None if bv is None else np64(bv), silu,
+                              None if s0 is None else np64(s0))
+    got = np.concatenate([np64(x).reshape(b, L, H * P), np64(B).reshape(b, L, G * N),
+                          np64(C).reshape(b, L, G * N)], axis=2)
+    check_rel(got, ref, TOL[io], f"conv1d {io} K={K}")
+    if K > 1:
+        assert np.array_equal(np64(s_out)[:, :, :K - 1], last), "carried state = last K-1 inputs"
+
+
+def test_conv1d_split_continues_across_calls_bitwise():
+    b, L, H, P, G, N, K, cut = 1, 200, 2, 16, 1, 16, 4, 70
+    CH = H * P + 2 * G * N
+    g = torch.Generator().manual_seed(70)
+    u = torch.randn((b, L, CH), generator=g).to(torch.bfloat16).to(DEV)
+    w = torch.randn((CH, K), generator=g).float().to(DEV)
+    kw = dict(nheads=H, headdim=P, ngroups=G, dstate=N, silu=True)
+    note("[gpu] conv1d split continuation")
+    whole = ssd().conv1d_split(u, w, **kw)
+    s = torch.empty((b, CH, K - 1), device=DEV)
+    a = ssd().conv1d_split(u[:, :cut].contiguous(), w, conv_state_out=s, **kw)
+    c = ssd().conv1d_split(u[:, cut:].contiguous(), w, conv_state_in=s, **kw)
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert torch.equal(torch.cat([a[i], c[i]], dim=1), whole[i])

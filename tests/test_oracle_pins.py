@@ -31,6 +31,7 @@ import numpy as np
 import pytest
 
 from oracle import (
+    causal_conv1d,
     dt_preprocess,
     chunk_cumsum,
     chunk_entry_states,
@@ -359,3 +360,49 @@ def test_dt_bias_goes_inside_the_softplus_and_clamp_comes_last():
     # without softplus the bias is a plain per-head shift
     raw = np.zeros((1, 2, H))
     assert np.array_equal(dt_preprocess(raw, bias), np.broadcast_to(bias, raw.shape))
+
+
+# ---- the short causal convolution -----------------------------------------
+
+def test_conv_impulse_response_is_the_reversed_kernel():
+    K, CH, L = 4, 3, 9
+    w = np.random.default_rng(50).normal(size=(CH, K))
+    u = np.zeros((1, L, CH))
+    u[0, 2, :] = 1.0  # impulse at t = 2
+    out, _ = causal_conv1d(u, w)
+    for t in range(L):
+        k = 2 + (K - 1) - t  # out[t] = w[k] with t - (K-1) + k = 2: the kernel reversed in time
+        expect = w[:, k] if 0 <= k < K else np.zeros(CH)
+        assert np.array_equal(out[0, t], expect)
+
+
+def test_conv_equals_numpy_convolve_per_channel():
+    rng = np.random.default_rng(51)
+    K, CH, L = 3, 5, 40
+    w = rng.normal(size=(CH, K))
+    b = rng.normal(size=CH)
+    u = rng.normal(size=(2, L, CH))
+    out, last = causal_conv1d(u, w, b)
+    for bb in range(2):
+        for c in range(CH):
+            ref = np.convolve(u[bb, :, c], w[c, ::-1])[:L] + b[c]  # causal: first L terms
+            assert np.allclose(out[bb, :, c], ref, rtol=0, atol=1e-12)
+    assert np.array_equal(last, np.transpose(u[:, L - (K - 1):, :], (0, 2, 1)))
+
+
+def test_conv_state_carries_a_split_and_silu():
+    rng = np.random.default_rng(52)
+    K, CH, L, cut = 4, 6, 30, 11
+    w = rng.normal(size=(CH, K))
+    u = rng.normal(size=(1, L, CH))
+    s0 = rng.normal(size=(1, CH, K - 1))
+    whole, last = causal_conv1d(u, w, None, True, s0)
+    a, sa = causal_conv1d(u[:, :cut], w, None, True, s0)
+    b, sb = causal_conv1d(u[:, cut:], w, None, True, sa)
+    assert np.allclose(np.concatenate([a, b], axis=1), whole, rtol=0, atol=1e-13)
+    assert np.array_equal(sb, last)
+    # silu(z) = z * sigmoid(z): zero at zero, z for large z, tends to 0 for very negative z
+    z0, _ = causal_conv1d(np.zeros((1, 2, 1)), np.ones((1, K)), np.array([0.0]), True)
+    assert np.all(z0 == 0.0)
+    big, _ = causal_conv1d(np.zeros((1, 1, 2)), np.ones((2, 1)), np.array([40.0, -40.0]), True)
+    assert big[0, 0, 0] == pytest.approx(40.0, rel=1e-15) and abs(big[0, 0, 1]) < 1e-15
