@@ -20,9 +20,10 @@
 //  * LDS tiles are fragment-major (each lane's 16-byte fragment contiguous,
 //    so operand reads are conflict-free) with a lane-slot swizzle that spreads
 //    the staging writes over the banks.
-//  * The next head's x rows, l and dt are loaded into registers while the
-//    current head's products run; they are scaled by w_j, rounded to bf16 and
-//    written transposed into the other LDS buffer; one barrier per head.
+//  * The x rows (and l, dt) of head hh+2 are loaded into one of two register
+//    sets while head hh's products run; head hh+1's set is scaled by w_j,
+//    rounded to bf16 and written transposed into the other LDS buffer; one
+//    barrier per head.
 //  * Output tiles hold four consecutive n per lane: 8-byte stores into
 //    states[b,h,c][p][n].
 #include "chunk_cumsum.h"
@@ -97,13 +98,113 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   if (rows <= 0) return;  // unused slot of a packed-sequence table (uniform)
   const int wn = wave % C::WN, wp = wave / C::WN;
 
+  // ---- x of one head: raw rows into registers; scaled, transposed into LDS.
+  // Two register sets: the loads of head hh+2 are issued while head hh's
+  // products run, so about two heads of loads are in flight per workgroup. ----
+  struct XSet {
+    uint4 xr[C::XPT][8];
+    float4 lr[C::XPT][2], dr[C::XPT][2];
+    float lam;
+  };
+  auto fetch_x = [&](XSet& xs, int h) {
+    if constexpr (!FUSED) {
+      const float* lc = dA_cs + ((b * H + h) * nc + c) * Q;
+      const float* dc = dtc + ((b * H + h) * nc + c) * Q;
+      xs.lam = lc[Q - 1];
+#pragma unroll
+      for (int k = 0; k < C::XPT; ++k) {
+        const int jb = ((tid + k * kThreads) / (P / 8)) % (Q / 8);
+        xs.lr[k][0] = *reinterpret_cast<const float4*>(lc + 8 * jb);
+        xs.lr[k][1] = *reinterpret_cast<const float4*>(lc + 8 * jb + 4);
+        xs.dr[k][0] = *reinterpret_cast<const float4*>(dc + 8 * jb);
+        xs.dr[k][1] = *reinterpret_cast<const float4*>(dc + 8 * jb + 4);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < C::XPT; ++k) {
+      const int bi = tid + k * kThreads;
+      const int cb = bi % (P / 8), jb = (bi / (P / 8)) % (Q / 8);
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        // clamped row, always in bounds; rows past the end are zeroed later
+        const int j = 8 * jb + rr;
+        xs.xr[k][rr] = ld16(x + ((row0 + min(j, rows - 1)) * H + h) * P + 8 * cb);
+      }
+    }
+  };
+  auto stage_x = [&](XSet& xs, uint4* buf, int hh) {
+    if constexpr (FUSED) {  // l and dt of this head from the LDS table
+      const float* lt = tab + 2 * hh * Q;
+      xs.lam = lt[Q - 1];
+#pragma unroll
+      for (int k = 0; k < C::XPT; ++k) {
+        const int jb = ((tid + k * kThreads) / (P / 8)) % (Q / 8);
+        xs.lr[k][0] = *reinterpret_cast<const float4*>(lt + 8 * jb);
+        xs.lr[k][1] = *reinterpret_cast<const float4*>(lt + 8 * jb + 4);
+        xs.dr[k][0] = *reinterpret_cast<const float4*>(lt + Q + 8 * jb);
+        xs.dr[k][1] = *reinterpret_cast<const float4*>(lt + Q + 8 * jb + 4);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < C::XPT; ++k) {
+      const int bi = tid + k * kThreads;
+      if (bi < C::XBLK) {
+        const int cb = bi % (P / 8), jb = bi / (P / 8);
+        const float l8[8] = {xs.lr[k][0].x, xs.lr[k][0].y, xs.lr[k][0].z, xs.lr[k][0].w,
+                             xs.lr[k][1].x, xs.lr[k][1].y, xs.lr[k][1].z, xs.lr[k][1].w};
+        const float d8[8] = {xs.dr[k][0].x, xs.dr[k][0].y, xs.dr[k][0].z, xs.dr[k][0].w,
+                             xs.dr[k][1].x, xs.dr[k][1].y, xs.dr[k][1].z, xs.dr[k][1].w};
+        float w[8];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr)
+          w[rr] = 8 * jb + rr < rows ? __expf(xs.lam - l8[rr]) * d8[rr] : 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {  // column p = 8cb + s: eight scaled bf16 along j
+          uint32_t q[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            q[m] = pack_bf16x2(w[2 * m] * bf16_at(xs.xr[k][2 * m], s),
+                               w[2 * m + 1] * bf16_at(xs.xr[k][2 * m + 1], s));
+          const int p = 8 * cb + s, pt = p >> 4;
+          buf[(pt * KS + (jb >> 2)) * 64 + sslot(p & 15, jb & 3, pt)] = make_uint4(q[0], q[1], q[2], q[3]);
+        }
+      }
+    }
+  };
+
+  // ---- prologue. All its global loads are issued first, in the order they
+  // are consumed (dt, then B, then the x of the first two heads), so that each
+  // wait covers one group only and the three latencies overlap. ----
+  const int hlast = h0 + HB - 1;
+  float dtv[kMaxHB];
+  if constexpr (FUSED) {
+    // dt of this chunk and these heads: a fixed count of loads (clamped)
+    const float* drow = dt + (row0 + min(tid, rows - 1)) * H;
+#pragma unroll
+    for (int hh = 0; hh < kMaxHB; ++hh) dtv[hh] = drow[min(h0 + hh, hlast)];
+  }
+  uint4 braw[C::BPT][8];
+#pragma unroll
+  for (int k = 0; k < C::BPT; ++k) {
+    const int bi = min(tid + k * kThreads, C::BBLK - 1);
+    const int cb = bi % (NB / 8), jb = bi / (NB / 8);
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const int j = 8 * jb + rr;
+      braw[k][rr] = ld16(Bm + ((row0 + min(j, rows - 1)) * G + g) * N + nb * NB + 8 * cb);
+    }
+  }
+  XSet sa, sb;
+  fetch_x(sa, h0);
+  fetch_x(sb, min(h0 + 1, hlast));
+
   if constexpr (FUSED) {
     // ---- step 1 for this chunk and these heads: dt tile, then one
     // wavefront scan per head ----
     if (tid < Q) {
-      const float* drow = dt + (row0 + min(tid, rows - 1)) * H + h0;
-      for (int hh = 0; hh < HB; ++hh)
-        tab[(2 * hh + 1) * Q + tid] = tid < rows ? dt_pre(drow[hh], h0 + hh, dto) : 0.f;
+#pragma unroll
+      for (int hh = 0; hh < kMaxHB; ++hh)
+        if (hh < HB) tab[(2 * hh + 1) * Q + tid] = tid < rows ? dt_pre(dtv[hh], h0 + hh, dto) : 0.f;
     }
     __syncthreads();
     constexpr int QPL = Q / 64;
@@ -131,14 +232,12 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   for (int k = 0; k < C::BPT; ++k) {
     const int bi = tid + k * kThreads;
     if (bi < C::BBLK) {
-      const int cb = bi % (NB / 8), jb = bi / (NB / 8);
-      uint4 r[8], o[8];
+      const int jb = bi / (NB / 8), cb = bi % (NB / 8);
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int j = 8 * jb + rr;
-        r[rr] = ld16_keep(Bm + ((row0 + min(j, rows - 1)) * G + g) * N + nb * NB + 8 * cb, j < rows);
-      }
-      transpose8x8(r, o);
+      for (int rr = 0; rr < 8; ++rr)  // rows past the end are zero
+        if (8 * jb + rr >= rows) braw[k][rr] = make_uint4(0, 0, 0, 0);
+      uint4 o[8];
+      transpose8x8(braw[k], o);
       // column n = 8cb + s holds B[8jb .. 8jb+7][n]: one fragment slot
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -157,106 +256,40 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   }
   __syncthreads();  // the LDS becomes the x double buffer
 
-  // ---- x of one head: raw rows into registers; scaled, transposed into LDS ----
-  uint4 xr[C::XPT][8];
-  float4 lr[C::XPT][2], dr[C::XPT][2];
-  float lam = 0.f;
-  auto fetch_x = [&](int h) {
-    if constexpr (!FUSED) {
-      const float* lc = dA_cs + ((b * H + h) * nc + c) * Q;
-      const float* dc = dtc + ((b * H + h) * nc + c) * Q;
-      lam = lc[Q - 1];
-#pragma unroll
-      for (int k = 0; k < C::XPT; ++k) {
-        const int jb = ((tid + k * kThreads) / (P / 8)) % (Q / 8);
-        lr[k][0] = *reinterpret_cast<const float4*>(lc + 8 * jb);
-        lr[k][1] = *reinterpret_cast<const float4*>(lc + 8 * jb + 4);
-        dr[k][0] = *reinterpret_cast<const float4*>(dc + 8 * jb);
-        dr[k][1] = *reinterpret_cast<const float4*>(dc + 8 * jb + 4);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < C::XPT; ++k) {
-      const int bi = tid + k * kThreads;
-      const int cb = bi % (P / 8), jb = (bi / (P / 8)) % (Q / 8);
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        // clamped row, always in bounds; rows past the end are zeroed later
-        const int j = 8 * jb + rr;
-        xr[k][rr] = ld16(x + ((row0 + min(j, rows - 1)) * H + h) * P + 8 * cb);
-      }
-    }
-  };
-  auto stage_x = [&](uint4* buf, int hh) {
-    if constexpr (FUSED) {  // l and dt of this head from the LDS table
-      const float* lt = tab + 2 * hh * Q;
-      lam = lt[Q - 1];
-#pragma unroll
-      for (int k = 0; k < C::XPT; ++k) {
-        const int jb = ((tid + k * kThreads) / (P / 8)) % (Q / 8);
-        lr[k][0] = *reinterpret_cast<const float4*>(lt + 8 * jb);
-        lr[k][1] = *reinterpret_cast<const float4*>(lt + 8 * jb + 4);
-        dr[k][0] = *reinterpret_cast<const float4*>(lt + Q + 8 * jb);
-        dr[k][1] = *reinterpret_cast<const float4*>(lt + Q + 8 * jb + 4);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < C::XPT; ++k) {
-      const int bi = tid + k * kThreads;
-      if (bi < C::XBLK) {
-        const int cb = bi % (P / 8), jb = bi / (P / 8);
-        const float l8[8] = {lr[k][0].x, lr[k][0].y, lr[k][0].z, lr[k][0].w,
-                             lr[k][1].x, lr[k][1].y, lr[k][1].z, lr[k][1].w};
-        const float d8[8] = {dr[k][0].x, dr[k][0].y, dr[k][0].z, dr[k][0].w,
-                             dr[k][1].x, dr[k][1].y, dr[k][1].z, dr[k][1].w};
-        float w[8];
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr)
-          w[rr] = 8 * jb + rr < rows ? __expf(lam - l8[rr]) * d8[rr] : 0.f;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {  // column p = 8cb + s: eight scaled bf16 along j
-          uint32_t q[4];
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-            q[m] = pack_bf16x2(w[2 * m] * bf16_at(xr[k][2 * m], s), w[2 * m + 1] * bf16_at(xr[k][2 * m + 1], s));
-          const int p = 8 * cb + s, pt = p >> 4;
-          buf[(pt * KS + (jb >> 2)) * 64 + sslot(p & 15, jb & 3, pt)] = make_uint4(q[0], q[1], q[2], q[3]);
-        }
-      }
-    }
-  };
-
-  const int ksteps = (rows + 31) / 32;
-  fetch_x(h0);
-  stage_x(lds, 0);
+  stage_x(sa, lds, 0);
   __syncthreads();
-  for (int hh = 0; hh < HB; ++hh) {
+  // head hh: its inputs are in LDS buffer hh & 1 (staged from `mine`, which
+  // is refilled with head hh+2); `next` holds head hh+1, staged at the end.
+  // The loads are always issued (the last heads re-read the final one), so
+  // every head has the same memory-operation sequence.
+  auto head = [&](XSet& mine, XSet& next, int hh) {
     const int h = h0 + hh;
     uint4* cur = lds + (hh & 1) * C::X_FRAGS;
-    // in flight during this head's products (the last head re-reads itself,
-    // which keeps the memory-operation count the same on every iteration)
-    fetch_x(hh + 1 < HB ? h + 1 : h);
+    fetch_x(mine, min(h + 2, hlast));
 
     f32x4_t acc[C::TN][C::TP];
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn)
 #pragma unroll
       for (int tp = 0; tp < C::TP; ++tp) acc[tn][tp] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // all KS steps, also past the end of a ragged last chunk (its x rows are
+    // zero there): straight-line code for the common full chunk
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks < ksteps) {  // uniform: skip steps entirely past the end
-        bf16x8_t bb[C::TP];
+      bf16x8_t bb[C::TP];
 #pragma unroll
-        for (int tp = 0; tp < C::TP; ++tp) {
-          const int pt = wp * C::TP + tp;
-          bb[tp] = pt < C::NT_P ? as_bf16x8(cur[(pt * KS + ks) * 64 + sslot(r16, g4, pt)])
-                                : as_bf16x8(make_uint4(0, 0, 0, 0));
-        }
-#pragma unroll
-        for (int tn = 0; tn < C::TN; ++tn)
-#pragma unroll
-          for (int tp = 0; tp < C::TP; ++tp) acc[tn][tp] = mfma_16x16x32(bt[tn][ks], bb[tp], acc[tn][tp]);
+      for (int tp = 0; tp < C::TP; ++tp) {
+        const int pt = wp * C::TP + tp;
+        // every p tile exists when the wavefronts split the p tiles evenly
+        // (then this is no branch at all)
+        bb[tp] = (C::WP * C::TP == C::NT_P || pt < C::NT_P)
+                     ? as_bf16x8(cur[(pt * KS + ks) * 64 + sslot(r16, g4, pt)])
+                     : as_bf16x8(make_uint4(0, 0, 0, 0));
       }
+#pragma unroll
+      for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+        for (int tp = 0; tp < C::TP; ++tp) acc[tn][tp] = mfma_16x16x32(bt[tn][ks], bb[tp], acc[tn][tp]);
     }
 
     // lane holds S^T[n = 4*g4 + i][p = r16] of each tile: four consecutive n
@@ -264,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 #pragma unroll
     for (int tp = 0; tp < C::TP; ++tp) {
       const int pt = wp * C::TP + tp;
-      if (pt < C::NT_P) {
+      if (C::WP * C::TP == C::NT_P || pt < C::NT_P) {
         const int p = pt * 16 + r16;
 #pragma unroll
         for (int tn = 0; tn < C::TN; ++tn) {
@@ -275,8 +308,12 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         }
       }
     }
-    if (hh + 1 < HB) stage_x(lds + ((hh + 1) & 1) * C::X_FRAGS, hh + 1);  // the other buffer
+    if (hh + 1 < HB) stage_x(next, lds + ((hh + 1) & 1) * C::X_FRAGS, hh + 1);  // the other buffer
     __syncthreads();
+  };
+  for (int hh = 0; hh < HB; hh += 2) {
+    head(sa, sb, hh);
+    if (hh + 1 < HB) head(sb, sa, hh + 1);
   }
 }
 
