@@ -275,3 +275,10 @@ def test_varlen_validates():
     q2 = list(p)
     q2[9] = ctypes.c_void_p(p[7].value + 4096)  # final_states partly over init_states
     assert L.ssd_forward_varlen(*args(q2)) == ALIAS
+
+
+def test_default_chunk_rule():
+    lib()
+    assert ssd.effective_chunk_size(desc(dstate=256)) == 256
+    assert ssd.effective_chunk_size(desc(headdim=32, dstate=16)) == 256
+    assert ssd.effective_chunk_size(desc(headdim=128)) == 128
