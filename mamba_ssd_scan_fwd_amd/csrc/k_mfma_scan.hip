@@ -83,11 +83,19 @@ struct ScanCfg {
 template <int Q>
 constexpr int kScanThreads = 2 * Q;
 
-// Slot of lane (r16, g4) inside a 1 KB fragment block. Readers cover all 64
-// slots of a block, so any per-block permutation keeps their reads
-// conflict-free; these two spread the staging writes across the banks.
-__device__ __forceinline__ int xslot(int r16, int g4, int pt) { return 16 * g4 + ((r16 + g4 + 4 * pt) & 15); }
-__device__ __forceinline__ int hslot(int r16, int g4) { return 16 * g4 + ((r16 + 4 * g4) & 15); }
+// Slot of lane (r16, g4) inside a 1 KB fragment block: a permutation of the
+// 64 slots for every block, so the matrix-core operand reads stay
+// conflict-free (each group of eight lanes covers the eight 16-byte bank
+// positions); the permutations are chosen so that the staging writes of
+// eight consecutive lanes land on eight different bank positions too.
+//  x^T: eight consecutive staging lanes hold columns p = 8 * cb + s of four
+//  p tiles (cb = 0..7): bit 3 of r16 and the p tile pick the position.
+__device__ __forceinline__ int xslot(int r16, int g4, int pt) {
+  return 16 * g4 + ((r16 & 8) | ((r16 & 7) ^ ((((r16 >> 3) << 2) ^ pt) & 7)));
+}
+//  Hin: eight consecutive staging lanes hold the four 8-wide n groups of two
+//  consecutive 32-deep steps ks of one row p.
+__device__ __forceinline__ int hslot(int r16, int g4, int ks) { return 16 * g4 + ((r16 + 2 * g4 + (ks & 1)) & 15); }
 
 template <int P, int N, int Q>
 __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu(2))) void chunk_scan_mfma_kernel(
@@ -280,7 +288,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
       const int ci = tid + k * C::THREADS;
       if (ci < C::HCH) {
         const int p = ci / (N / 8), n0 = 8 * (ci % (N / 8));
-        sHf[((p >> 4) * NK + (n0 >> 5)) * 64 + hslot(p & 15, (n0 >> 3) & 3)] = hr[k];
+        sHf[((p >> 4) * NK + (n0 >> 5)) * 64 + hslot(p & 15, (n0 >> 3) & 3, n0 >> 5)] = hr[k];
       }
     }
     float* sL = reinterpret_cast<float*>(buf + C::OFF_L);
@@ -341,7 +349,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
     for (int ks = 0; ks < NK; ++ks) {
 #pragma unroll
       for (int pt = 0; pt < NTP; ++pt) {
-        const bf16x8_t a = as_bf16x8(sHf[(pt * NK + ks) * 64 + hslot(r16, g4)]);
+        const bf16x8_t a = as_bf16x8(sHf[(pt * NK + ks) * 64 + hslot(r16, g4, ks)]);
 #pragma unroll
         for (int k = 0; k < RG; ++k)
           acc[k][pt] = mfma_16x16x32(a, Cr[k][ks], ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[k][pt]);
