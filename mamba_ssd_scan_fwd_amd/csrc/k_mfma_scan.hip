@@ -32,13 +32,17 @@
 //    tile, every factor <= 1; the three factors are tabulated per head when
 //    its inputs are staged. Diagonal tiles are masked (j > i -> 0) before the
 //    exponential of l_i - l_j is taken.
-//  * Per head, x (transposed), Hin and the decay tables are staged in LDS,
-//    double-buffered: the inputs of head h+1 are loaded into registers while
-//    the products of head h run (from one buffer) and are then written to
-//    the other buffer. One barrier per head. Operand tiles are fragment-major: each lane's 16-byte operand
-//    fragment is contiguous, so a matrix-core operand is one conflict-free
-//    16-byte LDS read; a swizzle of the lane slot inside each 1 KB fragment
-//    block spreads the staging writes over the banks.
+//  * Per head, x and Hin are loaded straight from memory into the LDS in
+//    their natural row order (loads that write the LDS directly: no
+//    registers and no staging instructions), double-buffered: the loads of
+//    head h+1 are issued at the start of head h into the other buffer and
+//    waited for before the barrier that ends head h. One barrier per head.
+//    The matrix-core operands are read from the row-major tiles as they
+//    are: Hin fragments (k = n along a row) with 16-byte reads, x fragments
+//    (k = j down a column) with the transposing 8-byte LDS read. A per-row
+//    XOR of the 16-byte chunk positions keeps both reads free of bank
+//    conflicts. The decay tables are tabulated per head from values read
+//    into registers.
 //  * The skip term D_h x_i is one more product on the diagonal tiles' x
 //    operand, against D_h times the identity (D_h split into two bf16 parts,
 //    so the term is exact to 16 bits of D_h in the fp32 accumulator).
@@ -57,18 +61,22 @@ struct ScanCfg {
   static constexpr int NTP = P / 16;          // p tiles
   static constexpr int NK = (N + 31) / 32;    // 32-deep steps over n
   static constexpr int NGT = R - 1;           // off-diagonal G^T tiles per wavefront
-  static constexpr int XBLK = (Q / 4) * (P / 8);  // 4x8 blocks of the x tile
-  static constexpr int XPT = (XBLK + THREADS - 1) / THREADS;
-  static constexpr int HCH = P * N / 8;           // 16-byte chunks of Hin
-  static constexpr int HPT = (HCH + THREADS - 1) / THREADS;
+  // x: Q rows of P bf16, Hin: P rows of N bf16, each in its natural row
+  // order with the 16-byte chunks of a row permuted (xsw, hsw); both are
+  // filled in 1 KB blocks by loads that write the LDS directly
+  static constexpr int XRB = 2 * P, HRB = 2 * N, HCPR = N / 8;
+  static constexpr int XBLK = Q * P * 2 / 1024;
+  static constexpr int HBLK = (P * N * 2 + 1023) / 1024;
+  static constexpr int XBPW = XBLK / WAVES;  // = P / 16
+  static constexpr int HBPW = (HBLK + WAVES - 1) / WAVES;
   static constexpr int NSL = (N + 127) / 128;     // n slices when staging B
   static constexpr int NSW = N < 128 ? N : 128;   // width of one slice
   static constexpr int BPITCH = NSW + 8;          // staged B row pitch (bf16)
   // one staging buffer (bytes): x^T fragments, Hin fragments, then per
   // position l, dt, (row factor, exp(l)), column factor, and the R x R
   // table of tile-boundary factors
-  static constexpr int X_BYTES = NTP * NM * 64 * 16;
-  static constexpr int H_BYTES = NTP * NK * 64 * 16;
+  static constexpr int X_BYTES = XBLK * 1024;
+  static constexpr int H_BYTES = HBLK * 1024;
   static constexpr int OFF_X = 0, OFF_H = X_BYTES, OFF_L = OFF_H + H_BYTES;
   static constexpr int OFF_DT = OFF_L + Q * 4, OFF_RE = OFF_DT + Q * 4;
   static constexpr int OFF_COL = OFF_RE + Q * 8, OFF_T = OFF_COL + Q * 4;
@@ -77,25 +85,83 @@ struct ScanCfg {
   // two buffers when they fit the LDS, else one (and a second barrier per head)
   static constexpr bool DB = 2 * BUF <= 160 * 1024;
   static constexpr int NBUF = DB ? 2 : 1;
-  static constexpr int TOTAL = NBUF * BUF > BST_BYTES ? NBUF * BUF : BST_BYTES;
+  // the B staging area of the G^T set-up lies over buffer 1 when buffer 0
+  // and it fit together: then the first head's loads into buffer 0 are
+  // issued before the set-up
+  static constexpr bool EARLY = DB && BUF + BST_BYTES <= 160 * 1024;
+  static constexpr int OFF_SB = EARLY ? BUF : 0;
+  static constexpr int TOTAL = NBUF * BUF > OFF_SB + BST_BYTES ? NBUF * BUF : OFF_SB + BST_BYTES;
+  // read the next pair's operands during the current pair's products where
+  // the registers allow it (two operand sets live at once)
+  static constexpr bool PIPE = N <= 128 && P <= 64;
 };
 
 template <int Q>
 constexpr int kScanThreads = 2 * Q;
 
-// Slot of lane (r16, g4) inside a 1 KB fragment block: a permutation of the
-// 64 slots for every block, so the matrix-core operand reads stay
-// conflict-free (each group of eight lanes covers the eight 16-byte bank
-// positions); the permutations are chosen so that the staging writes of
-// eight consecutive lanes land on eight different bank positions too.
-//  x^T: eight consecutive staging lanes hold columns p = 8 * cb + s of four
-//  p tiles (cb = 0..7): bit 3 of r16 and the p tile pick the position.
-__device__ __forceinline__ int xslot(int r16, int g4, int pt) {
-  return 16 * g4 + ((r16 & 8) | ((r16 & 7) ^ ((((r16 >> 3) << 2) ^ pt) & 7)));
+// Chunk permutations of the staged rows: row r's 16-byte chunk c is stored
+// at chunk position c ^ sw(r), sw(r) the XOR of one constant per set bit of
+// r mod 16. The constants make the operand reads conflict-free whether the
+// LDS serves 128 or 256 bytes (32 or 64 four-byte banks) per cycle: the
+// transposing 8-byte x read of 16 (32) lanes covers four (eight)
+// consecutive rows and two adjacent chunks, the 16-byte Hin read of 8 (16)
+// lanes eight (sixteen) consecutive rows at one chunk.
+__device__ __forceinline__ constexpr int row_xor(int r, int m0, int m1, int m2, int m3) {
+  return ((r & 1) ? m0 : 0) ^ ((r & 2) ? m1 : 0) ^ ((r & 4) ? m2 : 0) ^ ((r & 8) ? m3 : 0);
 }
-//  Hin: eight consecutive staging lanes hold the four 8-wide n groups of two
-//  consecutive 32-deep steps ks of one row p.
-__device__ __forceinline__ int hslot(int r16, int g4, int ks) { return 16 * g4 + ((r16 + 2 * g4 + (ks & 1)) & 15); }
+template <int P>
+__device__ __forceinline__ int xsw(int j) {  // x rows: P bf16
+  return P == 32 ? row_xor(j, 0, 2, 2, 0) : P == 64 ? row_xor(j, 2, 4, 2, 0) : P == 128 ? row_xor(j, 2, 4, 8, 0) : 0;
+}
+template <int N>
+__device__ __forceinline__ int hsw(int p) {  // Hin rows: N bf16
+  return N == 16 ? row_xor(p, 0, 0, 1, 1) : N == 32 ? row_xor(p, 0, 1, 2, 1) : N == 64 ? row_xor(p, 1, 2, 4, 1)
+                                                                                       : row_xor(p, 1, 2, 4, 8);
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// A raw buffer descriptor over [base, base + bytes) as four scalar words
+// (base and bytes wavefront-uniform).
+typedef int v4i32_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i32_t buffer_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return v4i32_t{(int)__builtin_amdgcn_readfirstlane((uint32_t)a), (int)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)),
+                 (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
+// 16 bytes per lane from a buffer straight into the LDS: lane l's bytes land
+// at LDS address lds_dst + 16 l (lds_dst wavefront-uniform); offsets past the
+// buffer's range read zeros. Written as inline assembly so that the compiler
+// does not treat it as a write to every LDS buffer (it would then wait for
+// the load before the next LDS read of the other buffer): completion is
+// waited for explicitly (vm_wait) before the barrier that publishes the
+// buffer. No result registers; the address register is read at issue.
+__device__ __forceinline__ void dma16(const v4i32_t& r, uint32_t lds_dst, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_dst), "v"(voff), "s"(__builtin_bit_cast(__int128, r))
+               : "memory", "m0");
+}
+
+// Transposing 8-byte LDS read (16-bit elements): within each group of 16
+// lanes, lane i receives element i % 4 of the 8-byte pieces addressed by
+// lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4, in that order. With lane
+// s addressing row s / 4 (of four consecutive rows) at column 4 (s % 4), lane
+// i receives column i of the four rows: a matrix-core operand fragment whose
+// k runs along the rows.
+__device__ __forceinline__ uint2 lds_tr8(const unsigned char* p) {
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Wait until at most n vector memory operations of this wavefront are in
+// flight (loads into the LDS included); other counters are not waited for.
+template <int n>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 template <int P, int N, int Q>
 __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu(2))) void chunk_scan_mfma_kernel(
@@ -139,6 +205,64 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
     return sidx < 0 ? 0 : (sidx > C::NGT - 1 ? C::NGT - 1 : sidx);
   };
 
+  // ---- per-head inputs. x and Hin go straight from memory into the LDS (no
+  // registers, no staging work): lane l of a 1 KB block fetches the 16-byte
+  // chunk that belongs at byte 16 l of the block. Rows of x past the end of
+  // the chunk fall outside the buffer range and arrive as zeros. The decay
+  // inputs are read into registers and tabulated in the LDS afterwards.
+  uint32_t xgo[C::XBPW], hgo[C::HBPW];
+#pragma unroll
+  for (int k = 0; k < C::XBPW; ++k) {
+    const int pos = (wave * C::XBPW + k) * 1024 + 16 * lane;
+    const int j = pos / C::XRB, cp = (pos % C::XRB) / 16;
+    xgo[k] = (uint32_t)(j * H * P * 2 + 16 * (cp ^ xsw<P>(j)));
+  }
+#pragma unroll
+  for (int k = 0; k < C::HBPW; ++k) {
+    const int pos = (wave * C::HBPW + k) * 1024 + 16 * lane;  // past P*N*2: padding, reads zeros
+    const int p = pos / C::HRB, cp = (pos % C::HRB) / 16;
+    hgo[k] = (uint32_t)(p * C::HRB + 16 * (cp ^ hsw<N>(p)));
+  }
+  float lpre = 0.f, dpre = 0.f, tl1 = 0.f, tl2 = 0.f;
+  // thread e < R*R tabulates exp(l_{16 r} - l_{16 t + 15}), r = e / R, t = e % R.
+  // LDS address of the workgroup's buffer area
+  const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)lds);
+  auto fetch_head = [&](int h, int bufoff) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + bufoff);
+    const v4i32_t xrs = buffer_words(x + (row0 * H + h) * P, (uint32_t)(((rows - 1) * (int64_t)H + 1) * P * 2));
+#pragma unroll
+    for (int k = 0; k < C::XBPW; ++k) dma16(xrs, dst + C::OFF_X + (wave * C::XBPW + k) * 1024, xgo[k]);
+    const v4i32_t hrs = buffer_words(states + ((b * H + h) * nc + c) * (int64_t)P * N, (uint32_t)(P * N * 2));
+#pragma unroll
+    for (int k = 0; k < C::HBPW; ++k)
+      if (wave * C::HBPW + k < C::HBLK) dma16(hrs, dst + C::OFF_H + (wave * C::HBPW + k) * 1024, hgo[k]);
+    const float* lc = dA_cs + ((b * H + h) * nc + c) * Q;
+    const float* dc = dtc + ((b * H + h) * nc + c) * Q;
+    const int tq = min(tid, Q - 1), te = min(tid, R * R - 1);
+    lpre = ld4f_at(lc, 4 * tq);
+    dpre = ld4f_at(dc, 4 * tq);
+    tl1 = ld4f_at(lc, 64 * (te / R));
+    tl2 = ld4f_at(lc, 64 * (te % R) + 60);
+  };
+  auto stage_tables = [&](unsigned char* buf) {
+    const int tr = tid / R, tt = tid % R;
+    float* sL = reinterpret_cast<float*>(buf + C::OFF_L);
+    float* sDt = reinterpret_cast<float*>(buf + C::OFF_DT);
+    float2* sRE = reinterpret_cast<float2*>(buf + C::OFF_RE);
+    float* sCol = reinterpret_cast<float*>(buf + C::OFF_COL);
+    float* sT = reinterpret_cast<float*>(buf + C::OFF_T);
+    if (tid < Q) {  // Q is a multiple of 64: whole wavefronts take this branch
+      const float lbeg = __shfl(lpre, lane & ~15, 64);  // l at the start of the 16-row tile
+      const float lend = __shfl(lpre, lane | 15, 64);   // l at its end
+      sL[tid] = lpre;
+      sDt[tid] = dpre;
+      sRE[tid] = make_float2(__expf(lpre - lbeg), __expf(lpre));
+      sCol[tid] = __expf(lend - lpre) * dpre;
+    }
+    if (tid < R * R) sT[tid] = tt < tr ? __expf(tl1 - tl2) : 0.f;
+  };
+  if constexpr (C::EARLY) fetch_head(h0, 0);
+
   // ---- C fragments of the row groups (B operand: column i, 8 consecutive n),
   // kept in registers: they also feed the chunk-output product of every head.
   // Rows past the end re-read the last row (their outputs are never stored).
@@ -159,7 +283,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   // ---- G^T = B C^T for every tile a row group needs, B staged through LDS.
   // Slot e < NGT holds an off-diagonal tile, slot NGT + k the diagonal tile
   // of row group k; the loop over slots is static and branch-free. ----
-  uint16_t* sB = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* sB = reinterpret_cast<uint16_t*>(lds + C::OFF_SB);
   f32x4_t Gacc[C::NGT + RG];
 #pragma unroll
   for (int e = 0; e < C::NGT + RG; ++e) Gacc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -215,115 +339,39 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   for (int k = 0; k < RG; ++k)
     Gd[k] = make_uint2(pack_bf16x2(Gacc[C::NGT + k][0], Gacc[C::NGT + k][1]),
                        pack_bf16x2(Gacc[C::NGT + k][2], Gacc[C::NGT + k][3]));
-  __syncthreads();  // the B staging area becomes the two head buffers
-
-  // ---- per-head inputs: global -> registers (two heads ahead) -> LDS ----
-  uint4 xr[C::XPT][4];
-  uint4 hr[C::HPT];
-  float lpre = 0.f, dpre = 0.f, tl1 = 0.f, tl2 = 0.f;
-  // thread e < R*R tabulates exp(l_{16 r} - l_{16 t + 15}), r = e / R, t = e % R.
-  // Staging and fetching use an opaque copy of the thread index, so their
-  // per-thread addresses are not kept live through the products.
-  // Every load is issued unconditionally, from a clamped (always valid)
-  // index where a thread has nothing to fetch: a fixed count of memory
-  // operations lets each wait cover exactly the loads it needs.
-  auto fetch_head = [&](int h) {
-    const int tid = opaque(threadIdx.x);
-    const uint16_t* xh = x + (row0 * H + h) * P;
-#pragma unroll
-    for (int k = 0; k < C::XPT; ++k) {
-      const int bi = min(tid + k * C::THREADS, C::XBLK - 1);
-      const int cb = bi % (P / 8), jb = bi / (P / 8);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        // raw load (clamped row, always in bounds); rows past the end are
-        // zeroed when staged, so nothing here waits for the data
-        const int j = 4 * jb + rr;
-        xr[k][rr] = ld16_at(xh, (uint32_t)((min(j, rows - 1) * H * P + 8 * cb) * 2));
-      }
-    }
-    const uint16_t* hin = states + ((b * H + h) * nc + c) * (int64_t)P * N;
-#pragma unroll
-    for (int k = 0; k < C::HPT; ++k) hr[k] = ld16_at(hin, (uint32_t)(16 * min(tid + k * C::THREADS, C::HCH - 1)));
-    const float* lc = dA_cs + ((b * H + h) * nc + c) * Q;
-    const float* dc = dtc + ((b * H + h) * nc + c) * Q;
-    const int tq = min(tid, Q - 1), te = min(tid, R * R - 1);
-    lpre = ld4f_at(lc, 4 * tq);
-    dpre = ld4f_at(dc, 4 * tq);
-    tl1 = ld4f_at(lc, 64 * (te / R));
-    tl2 = ld4f_at(lc, 64 * (te % R) + 60);
-  };
-  auto stage_head = [&](unsigned char* buf) {
-    const int tid = opaque(threadIdx.x);
-    const int lane = tid & 63;
-    const int tr = tid / R, tt = tid % R;
-    uint4* sXf = reinterpret_cast<uint4*>(buf + C::OFF_X);
-    uint4* sHf = reinterpret_cast<uint4*>(buf + C::OFF_H);
-#pragma unroll
-    for (int k = 0; k < C::XPT; ++k) {
-      const int bi = tid + k * C::THREADS;
-      if (bi < C::XBLK) {
-        const int cb = bi % (P / 8), jb = bi / (P / 8);
-        const int j0 = 4 * jb;
-        const int m = j0 >> 5, half = (j0 >> 4) & 1, jg = (j0 >> 2) & 3;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          if (j0 + rr >= rows) xr[k][rr] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {  // column p = 8cb + s: four bf16 along j
-          const uint32_t sel = (s & 1) ? 0x07060302u : 0x05040100u;
-          const int mw = s >> 1;
-          auto word = [&](const uint4& v) { return mw == 0 ? v.x : mw == 1 ? v.y : mw == 2 ? v.z : v.w; };
-          const uint32_t w0 = __builtin_amdgcn_perm(word(xr[k][1]), word(xr[k][0]), sel);
-          const uint32_t w1 = __builtin_amdgcn_perm(word(xr[k][3]), word(xr[k][2]), sel);
-          const int p = 8 * cb + s;
-          const int pt = p >> 4;
-          uint4* blk = sXf + (pt * NM + m) * 64;
-          reinterpret_cast<uint2*>(blk + xslot(p & 15, jg, pt))[half] = make_uint2(w0, w1);
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < C::HPT; ++k) {
-      const int ci = tid + k * C::THREADS;
-      if (ci < C::HCH) {
-        const int p = ci / (N / 8), n0 = 8 * (ci % (N / 8));
-        sHf[((p >> 4) * NK + (n0 >> 5)) * 64 + hslot(p & 15, (n0 >> 3) & 3, n0 >> 5)] = hr[k];
-      }
-    }
-    float* sL = reinterpret_cast<float*>(buf + C::OFF_L);
-    float* sDt = reinterpret_cast<float*>(buf + C::OFF_DT);
-    float2* sRE = reinterpret_cast<float2*>(buf + C::OFF_RE);
-    float* sCol = reinterpret_cast<float*>(buf + C::OFF_COL);
-    float* sT = reinterpret_cast<float*>(buf + C::OFF_T);
-    if (tid < Q) {  // Q is a multiple of 64: whole wavefronts take this branch
-      const float lbeg = __shfl(lpre, lane & ~15, 64);  // l at the start of the 16-row tile
-      const float lend = __shfl(lpre, lane | 15, 64);   // l at its end
-      sL[tid] = lpre;
-      sDt[tid] = dpre;
-      sRE[tid] = make_float2(__expf(lpre - lbeg), __expf(lpre));
-      sCol[tid] = __expf(lend - lpre) * dpre;
-    }
-    if (tid < R * R) sT[tid] = tt < tr ? __expf(tl1 - tl2) : 0.f;
-  };
-
-  if (N < 32) {  // fragment slots past N stay zero for the whole workgroup
-    for (int e = tid; e < NTP * NK * 64; e += C::THREADS) {
-#pragma unroll
-      for (int nb = 0; nb < C::NBUF; ++nb)
-        reinterpret_cast<uint4*>(lds + nb * C::BUF + C::OFF_H)[e] = make_uint4(0, 0, 0, 0);
-    }
+  if constexpr (!C::EARLY) {
+    __syncthreads();  // the B staging area becomes the head buffers
+    fetch_head(h0, 0);
   }
-  const int hlast = h0 + HB - 1;
-  fetch_head(h0);
-  stage_head(lds);
+  stage_tables(lds);
+
+  // per-lane LDS byte offsets of the operand reads inside a buffer:
+  //  x (A operand X^T, k = j): two transposing reads per fragment, lane
+  //  (s, q) = (l % 16, l / 16) addressing row 4q + s / 4 (then 16 rows on),
+  //  columns 16 pt + 4 (s % 4) .. +3; the fragment's k order, rows 4q..4q+3
+  //  of both 16-row tiles of a 32-row step, is that of the weights below.
+  //  Hin (A operand, k = n): row 16 pt + r16, the 16-byte chunk of n = 32 ks + 8 g4.
+  int xoff[NTP], hoff[NK];
+  {
+    const int s = lane & 15, q = lane >> 4;
+    const int j = 4 * q + (s >> 2);
+#pragma unroll
+    for (int pt = 0; pt < NTP; ++pt)
+      xoff[pt] = C::OFF_X + j * C::XRB + 16 * ((2 * pt + ((s & 3) >> 1)) ^ xsw<P>(j)) + 8 * (s & 1);
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+      hoff[ks] = C::OFF_H + r16 * C::HRB + 16 * (((4 * ks + g4) % C::HCPR) ^ hsw<N>(r16));
+  }
+  vm_wait<0>();
   __syncthreads();
 
   for (int hh = 0; hh < HB; ++hh) {
     const int h = h0 + hh;
     const unsigned char* buf = lds + (C::DB ? (hh & 1) * C::BUF : 0);
-    const uint4* sXf = reinterpret_cast<const uint4*>(buf + C::OFF_X);
-    const uint4* sHf = reinterpret_cast<const uint4*>(buf + C::OFF_H);
+    unsigned char* nbuf = lds + (C::DB ? ((hh + 1) & 1) * C::BUF : 0);
+    // loads of the next head into the other buffer, in flight during this
+    // head (nobody has read that buffer since the last barrier)
+    if (C::DB && hh + 1 < HB) fetch_head(h + 1, ((hh + 1) & 1) * C::BUF);
     const float* sL = reinterpret_cast<const float*>(buf + C::OFF_L);
     const float* sDt = reinterpret_cast<const float*>(buf + C::OFF_DT);
     const float2* sRE = reinterpret_cast<const float2*>(buf + C::OFF_RE);
@@ -344,34 +392,57 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
     auto lanef = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tv), l)); };
 
     f32x4_t acc[RG][NTP];
-    // chunk output: Y^T[p][i] = sum_n Hin[p][n] C_i[n], scaled by exp(l_i)
+    auto xfrag = [&](int m, int pt) {
+      const unsigned char* a = buf + xoff[pt] + m * 32 * C::XRB;
+      const uint2 lo = lds_tr8(a), hi = lds_tr8(a + 16 * C::XRB);
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    };
+    auto colf = [&](int t) { return *reinterpret_cast<const float4*>(sCol + 16 * t + 4 * g4); };
+    // operands of one pair of column tiles (2kp, 2kp + 1): x fragments and
+    // the column factors
+    struct PairOps {
+      uint4 a[NTP];
+      float4 ca, cb;
+    };
+    auto load_pair = [&](int kp, PairOps& o) {
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
+      for (int pt = 0; pt < NTP; ++pt) o.a[pt] = xfrag(kp, pt);
+      o.ca = colf(2 * kp);
+      o.cb = colf(2 * kp + 1);
+    };
+
+    // chunk output: Y^T[p][i] = sum_n Hin[p][n] C_i[n], scaled by exp(l_i).
+    // The fragments of step ks + 1 are read while the products of step ks run.
+    {
+      uint4 hf[2][NTP];
 #pragma unroll
-      for (int pt = 0; pt < NTP; ++pt) {
-        const bf16x8_t a = as_bf16x8(sHf[(pt * NK + ks) * 64 + hslot(r16, g4, ks)]);
+      for (int pt = 0; pt < NTP; ++pt) hf[0][pt] = ld16(buf + hoff[0] + pt * 16 * C::HRB);
 #pragma unroll
-        for (int k = 0; k < RG; ++k)
-          acc[k][pt] = mfma_16x16x32(a, Cr[k][ks], ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[k][pt]);
+      for (int ks = 0; ks < NK; ++ks) {
+        if (ks + 1 < NK) {
+#pragma unroll
+          for (int pt = 0; pt < NTP; ++pt) hf[(ks + 1) & 1][pt] = ld16(buf + hoff[ks + 1] + pt * 16 * C::HRB);
+        }
+#pragma unroll
+        for (int pt = 0; pt < NTP; ++pt)
+#pragma unroll
+          for (int k = 0; k < RG; ++k)
+            acc[k][pt] = mfma_16x16x32(as_bf16x8(hf[ks & 1][pt]), Cr[k][ks],
+                                       ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[k][pt]);
       }
     }
+    // the first pair's operands are read while those products drain
+    PairOps ops[2];
+    load_pair(0, ops[0]);
 #pragma unroll
     for (int k = 0; k < RG; ++k)
 #pragma unroll
       for (int pt = 0; pt < NTP; ++pt) acc[k][pt] *= el[k];
 
-    // loads for the next head, in flight during this head's products (the
-    // last head re-reads itself, so every iteration has the same sequence of
-    // memory operations and the wait before staging covers exactly these
-    // loads); issued here rather than at the barrier, where every wavefront
-    // would queue its loads at once
-    fetch_head(min(h + 1, hlast));
-
     // intra-chunk, off-diagonal tiles: both row groups walk the same pairs of
-    // column tiles (2kp, 2kp+1), so one x fragment feeds both.
+    // column tiles (2kp, 2kp+1), so one x fragment feeds both; the operands
+    // of pair kp + 1 are read while pair kp is weighted and multiplied.
     // All factors are <= 1: exp(l_i - l_r0) * exp(l_r0 - l_te) * c_j.
-    auto xfrag = [&](int m, int pt) { return sXf[(pt * NM + m) * 64 + xslot(r16, g4, pt)]; };
-    auto colf = [&](int t) { return *reinterpret_cast<const float4*>(sCol + 16 * t + 4 * g4); };
     auto wpair = [&](uint2 ga, float sa, float4 ca, uint2 gb, float sb, float4 cb) {
       const float w0 = bf16_lo(ga.x) * sa * ca.x, w1 = bf16_hi(ga.x) * sa * ca.y;
       const float w2 = bf16_lo(ga.y) * sa * ca.z, w3 = bf16_hi(ga.y) * sa * ca.w;
@@ -384,24 +455,27 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
     for (int kp = 0; kp < NM; ++kp) {
       const int ta = 2 * kp, tb = 2 * kp + 1;
       if (ta >= rk[1]) break;  // wavefront-uniform: row group 1 has the most tiles
-      // keep each pair's loads next to its products (no hoisting of every
-      // pair's operands, which would exhaust the registers)
+      // one pair's products and the next pair's loads per step (no hoisting
+      // of every pair's operands, which would exhaust the registers)
       __builtin_amdgcn_sched_barrier(0);
-      uint4 a[NTP];
-#pragma unroll
-      for (int pt = 0; pt < NTP; ++pt) a[pt] = xfrag(kp, pt);
-      const float4 ca = colf(ta), cb = colf(tb);
+      if constexpr (C::PIPE) {
+        if (kp + 1 < NM) load_pair(kp + 1, ops[(kp + 1) & 1]);
+      } else if (kp > 0) {
+        load_pair(kp, ops[kp & 1]);
+      }
+      const PairOps& o = ops[kp & 1];
 #pragma unroll
       for (int k = 0; k < RG; ++k) {
         if (ta < rk[k]) {  // tile tb == r_k is the diagonal: excluded here
           const float sa = rf[k] * lanef(16 * k + ta);
           const float sb = tb < rk[k] ? rf[k] * lanef(16 * k + tb) : 0.f;
-          const bf16x8_t w = wpair(Gt[gslot(k, ta)], sa, ca, Gt[gslot(k, tb)], sb, cb);
+          const bf16x8_t w = wpair(Gt[gslot(k, ta)], sa, o.ca, Gt[gslot(k, tb)], sb, o.cb);
 #pragma unroll
-          for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(as_bf16x8(a[pt]), w, acc[k][pt]);
+          for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(as_bf16x8(o.a[pt]), w, acc[k][pt]);
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     // The skip term D_h x_i rides on the diagonal tiles' x operand: an extra
     // product with D_h times the identity, D_h split into two bf16 parts
@@ -454,6 +528,10 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
       for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(a[pt], dop_lo, acc[k][pt]);
     }
 
+    // this wavefront's loads of the next head have landed (waited for before
+    // the stores are issued, so the wait does not include them)
+    vm_wait<0>();
+
     // epilogue: store. Rows past the end of the sequence fall outside the
     // buffer range and are dropped, so the store sequence is the same for
     // every chunk.
@@ -470,10 +548,14 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
       }
     }
 
-    // inputs of the next head into the other buffer (nobody reads it during
-    // this head)
-    if constexpr (!C::DB) __syncthreads();  // one buffer: everyone is done with it
-    if (hh + 1 < HB) stage_head(lds + (C::DB ? ((hh + 1) & 1) * C::BUF : 0));
+    if (hh + 1 < HB) {
+      if constexpr (!C::DB) {  // one buffer: refill it once everyone is done with it
+        __syncthreads();
+        fetch_head(h + 1, 0);
+        vm_wait<0>();
+      }
+      stage_tables(nbuf);
+    }
     __syncthreads();
   }
 }
