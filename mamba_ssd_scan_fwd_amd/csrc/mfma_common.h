@@ -78,6 +78,59 @@ __device__ __forceinline__ void buffer_st8(const uint2& v, __amdgpu_buffer_rsrc_
   __builtin_amdgcn_raw_buffer_store_b64(v2i{(int)v.x, (int)v.y}, r, (int)off, 0, 0);
 }
 
+// XOR of one constant per set bit of r mod 16 (m0 for bit 0, ...): the
+// row-dependent chunk permutation of tiles staged in the LDS.
+__device__ __forceinline__ constexpr int row_xor(int r, int m0, int m1, int m2, int m3) {
+  return ((r & 1) ? m0 : 0) ^ ((r & 2) ? m1 : 0) ^ ((r & 4) ? m2 : 0) ^ ((r & 8) ? m3 : 0);
+}
+
+// A raw buffer descriptor over [base, base + bytes) as four scalar words
+// (base and bytes wavefront-uniform).
+typedef int v4i32_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i32_t buffer_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return v4i32_t{(int)__builtin_amdgcn_readfirstlane((uint32_t)a), (int)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)),
+                 (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
+// 16 bytes per lane from a buffer straight into the LDS: lane l's bytes land
+// at LDS address lds_dst + 16 l (lds_dst wavefront-uniform); offsets past the
+// buffer's range read zeros. Written as inline assembly so that the compiler
+// does not treat it as a write to every LDS buffer (it would then wait for
+// the load before the next LDS read of the other buffer): completion is
+// waited for explicitly (vm_wait) before the barrier that publishes the
+// buffer. No result registers; the address register is read at issue.
+// The load takes its LDS address from m0, which the compiler reserves but
+// does not otherwise use in these kernels (no other LDS-DMA, interpolation or
+// indexed-register instructions), so nothing it holds there is lost.
+__device__ __forceinline__ void dma16(const v4i32_t& r, uint32_t lds_dst, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_dst), "v"(voff), "s"(__builtin_bit_cast(__int128, r))
+               : "memory", "m0");
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// Transposing 8-byte LDS read (16-bit elements): within each group of 16
+// lanes, lane i receives element i % 4 of the 8-byte pieces addressed by
+// lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4, in that order. With lane
+// s addressing row s / 4 (of four consecutive rows) at column 4 (s % 4), lane
+// i receives column i of the four rows: a matrix-core operand fragment whose
+// k runs along the rows.
+__device__ __forceinline__ uint2 lds_tr8(const unsigned char* p) {
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Wait until at most n vector memory operations of this wavefront are in
+// flight (loads into the LDS included); other counters are not waited for.
+template <int n>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Transpose an 8x8 block of bf16 held as eight rows of 16 bytes: out[s] holds
 // column s (rows 0..7, row 0 in the low half of word 0).
 __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
