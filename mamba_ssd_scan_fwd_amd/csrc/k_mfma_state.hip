@@ -8,22 +8,24 @@
 // As a matrix product per (b, c, h): S^T[N x P] = B_c^T[N x Q] * Xs[Q x P],
 // with Xs = diag(w) x_c. The contraction runs over the chunk positions j and
 // both operands are stored position-major in HBM (row j holds a contiguous P
-// or N vector), so every 16-byte operand fragment of eight consecutive j is
-// gathered from eight rows: tiles are transposed in registers (an 8x8 block
-// per thread, eight coalesced 16-byte row reads) on their way into LDS.
+// or N vector), so every operand fragment of eight consecutive j is a column
+// piece of a row-major tile.
 //
 // Work split: one workgroup (4 wavefronts) per (b, c, group of HB heads that
 // share a B/C group, block of up to 128 state columns).
-//  * B_c^T is staged through LDS once; each wavefront then keeps the
-//    fragments of its own n tiles in registers for all HB heads, and the LDS
-//    is reused as a double buffer for the scaled x of successive heads.
-//  * LDS tiles are fragment-major (each lane's 16-byte fragment contiguous,
-//    so operand reads are conflict-free) with a lane-slot swizzle that spreads
-//    the staging writes over the banks.
-//  * The x rows (and l, dt) of head hh+2 are loaded into one of two register
-//    sets while head hh's products run; head hh+1's set is scaled by w_j,
-//    rounded to bf16 and written transposed into the other LDS buffer; one
-//    barrier per head.
+//  * The B tile goes straight from memory into the LDS in its natural row
+//    order (loads that write the LDS directly; rows past the end of the chunk
+//    read as zeros), and each wavefront reads the B_c^T fragments of its own
+//    n tiles with the transposing LDS read, once, into registers kept for all
+//    HB heads. The LDS is then reused as a double buffer for the scaled x of
+//    successive heads.
+//  * x has to be scaled by w_j before it is rounded to bf16, so it passes
+//    through registers: the x rows (and l, dt) of head hh+2 are loaded into
+//    one of two register sets while head hh's products run; head hh+1's set
+//    is scaled, rounded and written transposed (8x8 blocks) into the other
+//    LDS buffer, fragment-major; one barrier per head. The slot permutation
+//    inside each fragment block keeps both the staging writes and the
+//    operand reads free of bank conflicts.
 //  * Output tiles hold four consecutive n per lane: 8-byte stores into
 //    states[b,h,c][p][n].
 #include "chunk_cumsum.h"
@@ -44,9 +46,12 @@ struct StateCfg {
   static constexpr int TP = (NT_P + WP - 1) / WP;  // p tiles per wavefront
   static constexpr int KS = Q / 32;                // 32-deep steps over the chunk
   static constexpr int XBLK = (Q / 8) * (P / 8);   // 8x8 blocks of the x tile
-  static constexpr int BBLK = (Q / 8) * (NB / 8);  // 8x8 blocks of the B tile
   static constexpr int XPT = (XBLK + kThreads - 1) / kThreads;
-  static constexpr int BPT = (BBLK + kThreads - 1) / kThreads;
+  // B tile: Q rows of NB bf16 in natural order (chunks swizzled per row),
+  // loaded straight into the LDS in 1 KB blocks
+  static constexpr int BRB = 2 * NB;
+  static constexpr int BNBLK = Q * NB * 2 / 1024;
+  static constexpr int BBPW = (BNBLK + kThreads / 64 - 1) / (kThreads / 64);
   static constexpr int X_FRAGS = NT_P * KS * 64;   // 16-byte fragments of one x buffer
   static constexpr int B_FRAGS = NT_N * KS * 64;
   static constexpr int LDS_FRAGS = (2 * X_FRAGS > B_FRAGS ? 2 * X_FRAGS : B_FRAGS);
@@ -54,10 +59,33 @@ struct StateCfg {
   static constexpr int TAB_FLOATS = kMaxHB * 2 * Q;
 };
 
-// slot of lane (r16, g4) inside a 1 KB fragment block (a bijection, so the
-// matrix-core reads stay conflict-free; it spreads the transposed writes)
-__device__ __forceinline__ int sslot(int r16, int g4, int tile) {
-  return 16 * g4 + ((r16 + 2 * g4 + (tile & 1)) & 15);
+// Slot of lane (r, g) inside the 1 KB fragment block (pt, ks) of the scaled
+// x tile: 16 g + (v & 15), v = r ^ (bit 3 of r) ^ (one constant per set bit
+// of g and pt); a bijection per block. Measured on gfx950 (64 banks of 4
+// bytes): a 16-byte read serves the eight-lane groups of a wavefront in the
+// pairs (0-7, 24-31), (8-15, 16-23), (32-39, 56-63), (40-47, 48-55), each
+// pair free of conflicts when its 16 lanes cover 256 bytes of distinct
+// banks; a 16-byte write serves eight consecutive lanes over 128 bytes. Bit
+// 3 of v follows bit 3 of r, which keeps every read pair on distinct banks;
+// the other constants spread the eight threads of a staging write (eight
+// columns p of 8x8 blocks: r = p % 16 with bit 3 from the column block,
+// and the p tile) over the eight 16-byte positions.
+template <int P>
+__device__ __forceinline__ int xslot(int r, int g, int pt, int ks) {
+  (void)ks;
+  constexpr int mg0 = P == 16 || P == 32 ? 4 : 0;
+  constexpr int mg1 = P == 16 ? 2 : 0;
+  constexpr int mp0 = P == 16 ? 0 : 2;
+  constexpr int mp1 = P >= 64 ? 4 : 0;
+  const int v = r ^ ((r >> 3) & 1) ^ ((g & 1) ? mg0 : 0) ^ ((g & 2) ? mg1 : 0) ^ ((pt & 1) ? mp0 : 0) ^
+                ((pt & 2) ? mp1 : 0);
+  return 16 * g + (v & 15);
+}
+// Chunk permutation of B row j (NB bf16): the transposing 8-byte read of 16
+// (32) lanes covers four (eight) rows at two adjacent chunks.
+template <int NB>
+__device__ __forceinline__ int bsw(int j) {
+  return NB == 32 ? row_xor(j, 0, 2, 0, 2) : NB == 64 ? row_xor(j, 2, 4, 0, 2) : NB == 128 ? row_xor(j, 2, 4, 0, 8) : 0;
 }
 
 // FUSED: the workgroup also computes the chunk's dA_cumsum and dt_chunked
@@ -166,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
             q[m] = pack_bf16x2(w[2 * m] * bf16_at(xs.xr[k][2 * m], s),
                                w[2 * m + 1] * bf16_at(xs.xr[k][2 * m + 1], s));
           const int p = 8 * cb + s, pt = p >> 4;
-          buf[(pt * KS + (jb >> 2)) * 64 + sslot(p & 15, jb & 3, pt)] = make_uint4(q[0], q[1], q[2], q[3]);
+          buf[(pt * KS + (jb >> 2)) * 64 + xslot<P>(p & 15, jb & 3, pt, jb >> 2)] = make_uint4(q[0], q[1], q[2], q[3]);
         }
       }
     }
@@ -176,23 +204,28 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   // are consumed (dt, then B, then the x of the first two heads), so that each
   // wait covers one group only and the three latencies overlap. ----
   const int hlast = h0 + HB - 1;
+  // B tile of the chunk straight into the LDS (rows past the end fall
+  // outside the buffer range and arrive as zeros)
+  {
+    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint4*)lds);
+    const v4i32_t brs =
+        buffer_words(Bm + (row0 * G + g) * N + nb * NB, (uint32_t)(((rows - 1) * (int64_t)G * N + NB) * 2));
+#pragma unroll
+    for (int k = 0; k < C::BBPW; ++k) {
+      const int blk = wave * C::BBPW + k;
+      if (blk < C::BNBLK) {
+        const int pos = blk * 1024 + 16 * lane;
+        const int j = pos / C::BRB, cp = (pos % C::BRB) / 16;
+        dma16(brs, lds_base + blk * 1024, (uint32_t)(j * G * N * 2 + 16 * (cp ^ bsw<NB>(j))));
+      }
+    }
+  }
   float dtv[kMaxHB];
   if constexpr (FUSED) {
     // dt of this chunk and these heads: a fixed count of loads (clamped)
     const float* drow = dt + (row0 + min(tid, rows - 1)) * H;
 #pragma unroll
     for (int hh = 0; hh < kMaxHB; ++hh) dtv[hh] = drow[min(h0 + hh, hlast)];
-  }
-  uint4 braw[C::BPT][8];
-#pragma unroll
-  for (int k = 0; k < C::BPT; ++k) {
-    const int bi = min(tid + k * kThreads, C::BBLK - 1);
-    const int cb = bi % (NB / 8), jb = bi / (NB / 8);
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const int j = 8 * jb + rr;
-      braw[k][rr] = ld16(Bm + ((row0 + min(j, rows - 1)) * G + g) * N + nb * NB + 8 * cb);
-    }
   }
   XSet sa, sb;
   fetch_x(sa, h0);
@@ -224,35 +257,30 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         }
       }
     }
-    // the barrier after the B^T staging below also orders these LDS writes
+    // the barrier before the B^T reads below also orders these LDS writes
   }
 
-  // ---- B_c^T -> LDS fragments [nt][ks][slot] (once), then into registers ----
-#pragma unroll
-  for (int k = 0; k < C::BPT; ++k) {
-    const int bi = tid + k * kThreads;
-    if (bi < C::BBLK) {
-      const int jb = bi / (NB / 8), cb = bi % (NB / 8);
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr)  // rows past the end are zero
-        if (8 * jb + rr >= rows) braw[k][rr] = make_uint4(0, 0, 0, 0);
-      uint4 o[8];
-      transpose8x8(braw[k], o);
-      // column n = 8cb + s holds B[8jb .. 8jb+7][n]: one fragment slot
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int n = 8 * cb + s, nt = n >> 4;
-        lds[(nt * KS + (jb >> 2)) * 64 + sslot(n & 15, jb & 3, nt)] = o[s];
-      }
-    }
-  }
+  // ---- B_c^T fragments into registers (A operand, m = n, k = j): two
+  // transposing reads each, lane (s, q) = (l % 16, l / 16) addressing row
+  // 32 ks + 8 q + s / 4 (then 4 rows on), columns 16 nt + 4 (s % 4) .. +3,
+  // so k runs over the eight consecutive j of the x fragments ----
+  vm_wait<0>();
   __syncthreads();
   bf16x8_t bt[C::TN][KS];
+  {
+    const unsigned char* bl = reinterpret_cast<const unsigned char*>(lds);
+    const int s = lane & 15, q = lane >> 4;
 #pragma unroll
-  for (int tn = 0; tn < C::TN; ++tn) {
-    const int nt = wn * C::TN + tn;
+    for (int tn = 0; tn < C::TN; ++tn) {
+      const int c2 = 2 * (wn * C::TN + tn) + ((s & 3) >> 1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bt[tn][ks] = as_bf16x8(lds[(nt * KS + ks) * 64 + sslot(r16, g4, nt)]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int j = 32 * ks + 8 * q + (s >> 2);
+        const uint2 lo = lds_tr8(bl + j * C::BRB + 16 * (c2 ^ bsw<NB>(j)) + 8 * (s & 1));
+        const uint2 hi = lds_tr8(bl + (j + 4) * C::BRB + 16 * (c2 ^ bsw<NB>(j + 4)) + 8 * (s & 1));
+        bt[tn][ks] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      }
+    }
   }
   __syncthreads();  // the LDS becomes the x double buffer
 
@@ -283,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         // every p tile exists when the wavefronts split the p tiles evenly
         // (then this is no branch at all)
         bb[tp] = (C::WP * C::TP == C::NT_P || pt < C::NT_P)
-                     ? as_bf16x8(cur[(pt * KS + ks) * 64 + sslot(r16, g4, pt)])
+                     ? as_bf16x8(cur[(pt * KS + ks) * 64 + xslot<P>(r16, g4, pt, ks)])
                      : as_bf16x8(make_uint4(0, 0, 0, 0));
       }
 #pragma unroll
