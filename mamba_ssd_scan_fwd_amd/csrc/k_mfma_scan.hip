@@ -101,19 +101,19 @@ constexpr int kScanThreads = 2 * Q;
 
 // Chunk permutations of the staged rows: row r's 16-byte chunk c is stored
 // at chunk position c ^ sw(r), sw(r) the XOR of one constant per set bit of
-// r mod 16. The constants make the operand reads conflict-free whether the
-// LDS serves 128 or 256 bytes (32 or 64 four-byte banks) per cycle: the
-// transposing 8-byte x read of 16 (32) lanes covers four (eight)
-// consecutive rows and two adjacent chunks, the 16-byte Hin read of 8 (16)
-// lanes eight (sixteen) consecutive rows at one chunk.
+// r mod 16 (row_xor). The constants keep the operand reads free of bank
+// conflicts on gfx950 (64 banks of 4 bytes): the transposing 8-byte x read
+// covers four consecutive rows and two adjacent chunks per 16 lanes; the
+// 16-byte Hin read serves its eight-lane groups in the pairs (0-7, 24-31),
+// (8-15, 16-23), ... (as measured), each pair reading eight consecutive rows
+// p at the chunk of one g4 and eight rows at the next chunk.
 template <int P>
 __device__ __forceinline__ int xsw(int j) {  // x rows: P bf16
   return P == 32 ? row_xor(j, 0, 2, 2, 0) : P == 64 ? row_xor(j, 2, 4, 2, 0) : P == 128 ? row_xor(j, 2, 4, 8, 0) : 0;
 }
 template <int N>
 __device__ __forceinline__ int hsw(int p) {  // Hin rows: N bf16
-  return N == 16 ? row_xor(p, 0, 0, 1, 1) : N == 32 ? row_xor(p, 0, 1, 2, 1) : N == 64 ? row_xor(p, 1, 2, 4, 1)
-                                                                                       : row_xor(p, 1, 2, 4, 8);
+  return N == 16 ? 0 : N == 32 ? row_xor(p, 0, 0, 1, 2) : N == 64 ? row_xor(p, 0, 1, 2, 4) : row_xor(p, 1, 2, 4, 8);
 }
 
 template <int P, int N, int Q>
