@@ -493,11 +493,21 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int k = 0; k < RG; ++k) {
       const uint32_t rowoff = (uint32_t)(ik[k] * (int64_t)H * P * 2);
+      if constexpr (NTP % 2 == 0) {
+        // p tiles in pairs: each lane stores eight consecutive p (16 bytes),
+        // one store writing 64 contiguous bytes of 16 rows
 #pragma unroll
-      for (int pt = 0; pt < NTP; ++pt) {
-        const int p = 16 * pt + 4 * g4;
-        const f32x4_t v = acc[k][pt];
-        buffer_st8(make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])), yr, rowoff + p * 2);
+        for (int pt = 0; pt < NTP; pt += 2) {
+          const int p = 16 * pt + 16 * (g4 & 1) + 8 * (g4 >> 1);
+          buffer_st16(pair_rows16(acc[k][pt], acc[k][pt + 1]), yr, rowoff + p * 2);
+        }
+      } else {
+#pragma unroll
+        for (int pt = 0; pt < NTP; ++pt) {
+          const int p = 16 * pt + 4 * g4;
+          const f32x4_t v = acc[k][pt];
+          buffer_st8(make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])), yr, rowoff + p * 2);
+        }
       }
     }
 

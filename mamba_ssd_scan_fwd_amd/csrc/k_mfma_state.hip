@@ -328,20 +328,13 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
       if (C::WP * C::TP == C::NT_P || pt < C::NT_P) {
         const int p = pt * 16 + r16;
         if constexpr (C::TN % 2 == 0) {
-          // two n tiles at a time: lane rows (16 lanes each) 1 and 3 of the
-          // first tile trade places with rows 0 and 2 of the second, after
-          // which each lane holds eight consecutive n of one row p, so one
-          // 16-byte store per lane writes 64 contiguous bytes of 16 rows
+          // two n tiles at a time: each lane stores eight consecutive n of
+          // one row p (16 bytes), one store writing 64 contiguous bytes of
+          // 16 rows
 #pragma unroll
           for (int tn = 0; tn < C::TN; tn += 2) {
-            const f32x4_t v0 = acc[tn][tp], v1 = acc[tn + 1][tp];
-            const auto s0 = __builtin_amdgcn_permlane16_swap(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v1[0], v1[1]),
-                                                             false, false);
-            const auto s1 = __builtin_amdgcn_permlane16_swap(pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[2], v1[3]),
-                                                             false, false);
-            // lane row g4 now holds n = 16 (g4 & 1) + 8 (g4 >> 1) .. +7 of the tile pair
             const int n = nb * NB + (wn * C::TN + tn) * 16 + 16 * (g4 & 1) + 8 * (g4 >> 1);
-            *reinterpret_cast<uint4*>(out + (int64_t)p * N + n) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+            *reinterpret_cast<uint4*>(out + (int64_t)p * N + n) = pair_rows16(acc[tn][tp], acc[tn + 1][tp]);
           }
         } else {
 #pragma unroll

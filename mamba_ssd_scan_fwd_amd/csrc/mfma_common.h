@@ -77,6 +77,22 @@ __device__ __forceinline__ void buffer_st8(const uint2& v, __amdgpu_buffer_rsrc_
   typedef int v2i __attribute__((ext_vector_type(2)));
   __builtin_amdgcn_raw_buffer_store_b64(v2i{(int)v.x, (int)v.y}, r, (int)off, 0, 0);
 }
+__device__ __forceinline__ void buffer_st16(const uint4& v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, r, (int)off, 0, 0);
+}
+
+// Two accumulator tiles of a 16x16 product (lane row g = l / 16 holding rows
+// 4g..4g+3 of column l % 16 in each) as bf16, rearranged so that each lane
+// holds eight consecutive rows of one tile pair: rows 1 and 3 of lanes (16
+// lanes each) of the first tile trade places with rows 0 and 2 of the
+// second. Lane row g then holds rows 16 (g & 1) + 8 (g >> 1) .. +7 of the
+// 32 rows of the pair (first tile rows 0..15, second 16..31), in order.
+__device__ __forceinline__ uint4 pair_rows16(const f32x4_t& t0, const f32x4_t& t1) {
+  const auto s0 = __builtin_amdgcn_permlane16_swap(pack_bf16x2(t0[0], t0[1]), pack_bf16x2(t1[0], t1[1]), false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(pack_bf16x2(t0[2], t0[3]), pack_bf16x2(t1[2], t1[3]), false, false);
+  return make_uint4(s0[0], s1[0], s0[1], s1[1]);
+}
 
 // XOR of one constant per set bit of r mod 16 (m0 for bit 0, ...): the
 // row-dependent chunk permutation of tiles staged in the LDS.
