@@ -180,11 +180,15 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   // thread e < R*R tabulates exp(l_{16 r} - l_{16 t + 15}), r = e / R, t = e % R.
   // LDS address of the workgroup's buffer area
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)lds);
-  auto fetch_head = [&](int h, int bufoff) {
+  // x block k of this wavefront
+  auto fetch_x_block = [&](int h, int bufoff, int k) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + bufoff);
     const v4i32_t xrs = buffer_words(x + (row0 * H + h) * P, (uint32_t)(((rows - 1) * (int64_t)H + 1) * P * 2));
-#pragma unroll
-    for (int k = 0; k < C::XBPW; ++k) dma16(xrs, dst + C::OFF_X + (wave * C::XBPW + k) * 1024, xgo[k]);
+    dma16(xrs, dst + C::OFF_X + (wave * C::XBPW + k) * 1024, xgo[k]);
+  };
+  // Hin blocks of this wavefront and the decay inputs
+  auto fetch_rest = [&](int h, int bufoff) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + bufoff);
     const v4i32_t hrs = buffer_words(states + ((b * H + h) * nc + c) * (int64_t)P * N, (uint32_t)(P * N * 2));
 #pragma unroll
     for (int k = 0; k < C::HBPW; ++k)
@@ -196,6 +200,11 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
     dpre = ld4f_at(dc, 4 * tq);
     tl1 = ld4f_at(lc, 64 * (te / R));
     tl2 = ld4f_at(lc, 64 * (te % R) + 60);
+  };
+  auto fetch_head = [&](int h, int bufoff) {
+    fetch_rest(h, bufoff);
+#pragma unroll
+    for (int k = 0; k < C::XBPW; ++k) fetch_x_block(h, bufoff, k);
   };
   auto stage_tables = [&](unsigned char* buf) {
     const int tr = tid / R, tt = tid % R;
@@ -323,8 +332,14 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
     const unsigned char* buf = lds + (C::DB ? (hh & 1) * C::BUF : 0);
     unsigned char* nbuf = lds + (C::DB ? ((hh + 1) & 1) * C::BUF : 0);
     // loads of the next head into the other buffer, in flight during this
-    // head (nobody has read that buffer since the last barrier)
-    if (C::DB && hh + 1 < HB) fetch_head(h + 1, ((hh + 1) & 1) * C::BUF);
+    // head (nobody has read that buffer since the last barrier). They are
+    // spread over the head: Hin and the decay inputs now, one x block per
+    // step of the off-diagonal loop below. Issued all at once, right after
+    // the barrier, the loads of eight wavefronts fill the vector-memory queue
+    // and stall every wavefront at the issue.
+    const bool pre = C::DB && hh + 1 < HB;
+    const int nbo = ((hh + 1) & 1) * C::BUF;
+    if (pre) fetch_rest(h + 1, nbo);
     const float* sL = reinterpret_cast<const float*>(buf + C::OFF_L);
     const float* sDt = reinterpret_cast<const float*>(buf + C::OFF_DT);
     const float2* sRE = reinterpret_cast<const float2*>(buf + C::OFF_RE);
@@ -411,6 +426,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
       // one pair's products and the next pair's loads per step (no hoisting
       // of every pair's operands, which would exhaust the registers)
       __builtin_amdgcn_sched_barrier(0);
+      if (pre && kp < C::XBPW) fetch_x_block(h + 1, nbo, kp);
       if constexpr (C::PIPE) {
         if (kp + 1 < NM) load_pair(kp + 1, ops[(kp + 1) & 1]);
       } else if (kp > 0) {
@@ -429,6 +445,13 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    // x blocks not issued by a wavefront with fewer steps than blocks
+    if (pre) {
+      const int steps = (rk[1] + 1) / 2;
+#pragma unroll
+      for (int k = 0; k < C::XBPW; ++k)
+        if (k >= steps) fetch_x_block(h + 1, nbo, k);
+    }
 
     // The skip term D_h x_i rides on the diagonal tiles' x operand: an extra
     // product with D_h times the identity, D_h split into two bf16 parts

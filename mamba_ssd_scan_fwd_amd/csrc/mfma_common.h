@@ -122,7 +122,7 @@ __device__ __forceinline__ v4i32_t buffer_words(const void* base, uint32_t bytes
 __device__ __forceinline__ void dma16(const v4i32_t& r, uint32_t lds_dst, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(lds_dst), "v"(voff), "s"(__builtin_bit_cast(__int128, r))
+               : "s"(__builtin_amdgcn_readfirstlane(lds_dst)), "v"(voff), "s"(__builtin_bit_cast(__int128, r))
                : "memory", "m0");
 }
 
