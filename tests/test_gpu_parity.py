@@ -138,6 +138,14 @@ EDGE = [
     (300, 64, 32, 4, 1, "bf16", 0, True),
     (300, 64, 256, 4, 2, "bf16", 0, True),
     (300, 128, 256, 2, 1, "bf16", 128, True),
+    # Hin smaller than one 1 KB load block; B tile with fewer load blocks
+    # than wavefronts; one LDS buffer per head (P = 128 at Q = 256)
+    (300, 16, 16, 4, 1, "bf16", 0, True),
+    (200, 32, 16, 4, 1, "bf16", 64, True),
+    (200, 32, 32, 4, 2, "bf16", 64, False),
+    (300, 16, 64, 4, 1, "bf16", 128, True),
+    (300, 128, 128, 2, 1, "bf16", 256, True),
+    (300, 128, 256, 2, 1, "bf16", 256, False),
     (1, 16, 16, 4, 1, "fp32", 0, True),
     (300, 16, 16, 4, 1, "fp32", 0, True),
     (300, 64, 128, 4, 2, "fp32", 0, True),
