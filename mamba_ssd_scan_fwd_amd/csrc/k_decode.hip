@@ -36,7 +36,7 @@ template <typename TIO, int N>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const TIO* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A,
     const TIO* __restrict__ Bm, const TIO* __restrict__ Cm, const float* __restrict__ D,
-    float* __restrict__ state, TIO* __restrict__ y, int64_t rows, int H, int P, int G, DtOpts dto) {
+    float* __restrict__ state, TIO* __restrict__ y, int64_t rows, int H, int pshift, int hpg, DtOpts dto) {
   constexpr int TPR = N / 4;                        // threads per state row
   constexpr int RPW = kThreads / TPR;               // rows per workgroup and pass
   const int tid = threadIdx.x;
@@ -55,16 +55,16 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
 #pragma unroll
   for (int k = 0; k < kRPT; ++k) {
     const int64_t r = rr[k] < rows ? rr[k] : rows - 1;
-    const int p = (int)(r % P);
-    const int64_t bh = r / P;
-    const int h = (int)(bh % H);
-    const int64_t b = bh / H;
-    const int g = h / (H / G);
+    // row r = (b * H + h) * P + p; P is a power of two and b * H < 2^31
+    const int bh = (int)(r >> pshift);
+    const int b = bh / H, h = bh - b * H;
+    const int g = h / hpg;
+    const int G = H / hpg;
     const float d = dt_pre(dt[bh], h, dto);
     const float alpha = __expf(d * A[h]);
     const float xp = to_f32(x[r]);
-    const float4 bv = IO4<TIO>::load(Bm + (b * G + g) * N + 4 * sub);
-    const float4 cv = IO4<TIO>::load(Cm + (b * G + g) * N + 4 * sub);
+    const float4 bv = IO4<TIO>::load(Bm + ((int64_t)b * G + g) * N + 4 * sub);
+    const float4 cv = IO4<TIO>::load(Cm + ((int64_t)b * G + g) * N + 4 * sub);
     const float u = d * xp;
     float4 hn;
     hn.x = fmaf(alpha, hs[k].x, u * bv.x);
@@ -93,7 +93,7 @@ hipError_t launch_io(const Plan& p, const void* x, const float* dt, const float*
     const int64_t grid = (rows + per_wg - 1) / per_wg;
     kern<<<dim3((unsigned)grid), kThreads, 0, s>>>(
         static_cast<const TIO*>(x), dt, A, static_cast<const TIO*>(B), static_cast<const TIO*>(C), D, state,
-        static_cast<TIO*>(y), rows, (int)p.H, (int)p.P, (int)p.G, p.dto);
+        static_cast<TIO*>(y), rows, (int)p.H, __builtin_ctzll((unsigned long long)p.P), (int)(p.H / p.G), p.dto);
     return hipGetLastError();
   };
   switch (p.N) {
