@@ -546,22 +546,40 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   }
 }
 
-// Heads per workgroup: a divisor of the heads in one B/C group, at most 8,
-// as large as keeps enough workgroups to fill the chip (the G^T set-up is
-// amortised over more heads).
-int pick_heads_per_wg(const Plan& p) {
+// Heads per workgroup: a power-of-two divisor of the heads in one B/C group,
+// at most 16, chosen by a small cost model: the workgroups run in rounds of
+// `resident` per compute unit, and each costs its heads plus about two heads'
+// worth of set-up (the G^T product). More heads per workgroup amortise the
+// set-up; fewer avoid a last round that leaves most compute units idle.
+// Packed sequences: of the ceil(T/Q) + nseq table slots, about
+// ceil(T/Q) + nseq/2 hold tokens (the rest exit at once).
+int pick_heads_per_wg(const Plan& p, int resident) {
   const int64_t hpg = p.H / p.G;
-  const int64_t base = p.batch * p.nc * p.H;
-  int hb = 1;
-  while (hb < 16 && hpg % (hb * 2) == 0 && base / (hb * 2) >= 256) hb *= 2;
-  return hb;
+  const int64_t used = p.seqtab != nullptr ? p.nc - p.nseq / 2 : p.nc;
+  const int64_t units = p.batch * used * p.H;  // (chunk, head) pairs with tokens
+  const int64_t slots = (int64_t)device_cu_count() * resident;
+  int best = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int hb = 1; hb <= 16 && hpg % hb == 0; hb *= 2) {
+    const int64_t wgs = (units + hb - 1) / hb;
+    const int64_t cost = (wgs + slots - 1) / slots * (hb + 2);
+    if (cost <= best_cost) {  // ties: the larger count (fewer set-ups)
+      best_cost = cost;
+      best = hb;
+    }
+  }
+  return best;
 }
 
 template <int P, int N, int Q>
 hipError_t launch_pnq(const Plan& p, const void* x, const void* B, const void* Cm, const float* D,
                       const float* cs, const float* dtc, const void* st, void* y, hipStream_t s) {
   using Cfg = ScanCfg<P, N, Q>;
-  const int hb = pick_heads_per_wg(p);
+  // workgroups resident per compute unit: two wavefronts per SIMD (the
+  // register budget), and the LDS
+  const int by_waves = 8 / Cfg::WAVES;
+  const int by_lds = 160 * 1024 / Cfg::TOTAL;
+  const int hb = pick_heads_per_wg(p, by_waves < by_lds ? by_waves : by_lds);
   const int64_t grid = p.batch * p.nc * (p.H / hb);
   chunk_scan_mfma_kernel<P, N, Q><<<dim3((unsigned)grid), Cfg::THREADS, 0, s>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(Cm), D,

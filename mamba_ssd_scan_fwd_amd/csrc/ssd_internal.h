@@ -58,6 +58,9 @@ hipError_t launch_conv1d_split(const Plan& p, int K, const void* xbc, const floa
 hipError_t launch_decode_step(const Plan& p, const void* x, const float* dt, const float* A, const void* B,
                               const void* C, const float* D, float* state, void* y, hipStream_t s);
 
+// Compute units of the current device (queried once per device).
+int device_cu_count();
+
 // First row (of the [batch * L, ...] token arrays) and valid length of chunk
 // c of batch b: fixed-size chunks of each sequence, or the packed table.
 __device__ __forceinline__ void chunk_span(const ChunkInfo* tab, int64_t b, int64_t c, int64_t L, int Q,
