@@ -52,9 +52,6 @@ __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cas
 __device__ __forceinline__ uint4 ld16_at(const void* base, uint32_t byte_off) {
   return *reinterpret_cast<const uint4*>(reinterpret_cast<const unsigned char*>(base) + byte_off);
 }
-__device__ __forceinline__ uint2 ld8_at(const void* base, uint32_t byte_off) {
-  return *reinterpret_cast<const uint2*>(reinterpret_cast<const unsigned char*>(base) + byte_off);
-}
 __device__ __forceinline__ float ld4f_at(const void* base, uint32_t byte_off) {
   return *reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(base) + byte_off);
 }
@@ -147,26 +144,6 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Transpose an 8x8 block of bf16 held as eight rows of 16 bytes: out[s] holds
-// column s (rows 0..7, row 0 in the low half of word 0).
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const uint32_t sel = (s & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4& r0 = in[2 * q];
-      const uint4& r1 = in[2 * q + 1];
-      const int m = s >> 1;
-      const uint32_t a = m == 0 ? r0.x : m == 1 ? r0.y : m == 2 ? r0.z : r0.w;
-      const uint32_t b = m == 0 ? r1.x : m == 1 ? r1.y : m == 2 ? r1.z : r1.w;
-      w[q] = __builtin_amdgcn_perm(b, a, sel);
-    }
-    out[s] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
 // Workgroups are handed to the eight XCDs (each with its own L2) round-robin
 // by workgroup id. This renumbering gives each XCD one contiguous run of
 // logical ids, so workgroups that share operands (neighbouring logical ids:
@@ -175,14 +152,6 @@ __device__ __forceinline__ int64_t xcd_local_order(int64_t bid, int64_t grid) {
   constexpr int kXcds = 8;
   if (grid % kXcds != 0) return bid;
   return (bid % kXcds) * (grid / kXcds) + bid / kXcds;
-}
-
-// The same value, but opaque to the optimiser: addresses derived from it are
-// recomputed where they are used instead of being hoisted out of a loop and
-// kept live in registers for its whole length.
-__device__ __forceinline__ int opaque(int v) {
-  asm volatile("" : "+v"(v));
-  return v;
 }
 
 // Element e (0..7) of a row of eight bf16 held in a uint4, as fp32.
