@@ -118,7 +118,9 @@ SSD_API ssd_status_t ssd_effective_chunk_size(const ssd_desc_t* desc, int32_t* c
 
 /* Bytes of device workspace ssd_forward needs for `desc`: dA_cumsum,
  * dt_chunked and states, each starting on a 256-byte boundary, in that order.
- * Pure host computation; no HIP call. */
+ * Where the one-pass kernel supports the shape (see ssd_forward_fused), the
+ * states region is at least the size of its state hand-over area. Pure host
+ * computation; no HIP call. */
 SSD_API ssd_status_t ssd_workspace_bytes(const ssd_desc_t* desc, size_t* bytes);
 
 /* The whole forward pass: y and (when final_state != NULL) the final state.
@@ -133,7 +135,9 @@ SSD_API ssd_status_t ssd_workspace_bytes(const ssd_desc_t* desc, size_t* bytes);
  *               least ssd_workspace_bytes() bytes, 256-byte aligned, not
  *               overlapping any other argument.
  *   y must not overlap any input.
- * Runs the five steps below on `stream`, in order. */
+ * Runs the five steps below on `stream`, in order, or, where the one-pass
+ * kernel of ssd_forward_fused supports the shape and is the faster choice for
+ * it, that path. */
 SSD_API ssd_status_t ssd_forward(const ssd_desc_t* desc,
                          const void* x, const float* dt, const float* A,
                          const void* B, const void* C, const float* D,
@@ -141,6 +145,30 @@ SSD_API ssd_status_t ssd_forward(const ssd_desc_t* desc,
                          void* y, float* final_state,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* The same forward pass in one pass over x ("Mamba-2 vs Transformers",
+ * section "Mamba-2 and the SSD paper: what changed in practice": the chunk
+ * states are combined by a scan over the chunks, here a chain of hand-overs
+ * between the workgroups of consecutive chunks inside one kernel). Two
+ * launches: the dt cumsum, then one kernel that computes every chunk's state,
+ * takes the state entering the chunk from the chunk before, passes its own
+ * on, and writes y. x is read once and no chunk state goes through the
+ * workspace's states array.
+ * Arguments, ownership and errors as for ssd_forward, with the same
+ * workspace size (ssd_workspace_bytes); the workspace must not be in use by
+ * another call that may run at the same time. Supported: bf16 io, chunk
+ * length 256, headdim 32 or 64, dstate 32, 64 or 128 (not headdim 32 with
+ * dstate 32); anything else returns SSD_ERR_UNSUPPORTED.
+ * Results agree with ssd_forward to rounding: the chunk states stay in fp32
+ * (ssd_forward rounds them to bf16 between its kernels), and the chunk-state
+ * weights are applied to B instead of x before the bf16 rounding. */
+SSD_API ssd_status_t ssd_forward_fused(const ssd_desc_t* desc,
+                               const void* x, const float* dt, const float* A,
+                               const void* B, const void* C, const float* D,
+                               const float* init_state,
+                               void* y, float* final_state,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /* ---- the steps of the chunked path, each callable on its own ------------ */
 

@@ -108,17 +108,33 @@ ssd_status_t make_plan(const ssd_desc_t* d, Plan* p) {
 
 struct WsLayout {
   size_t cs_off, dt_off, st_off, tab_off, seq_off, total;
+  // one-pass path, inside the states region: the state hand-over ring, then
+  // the per-head counters, the ticket and the status word (32-bit each)
+  size_t ring_off, sync_off;
+  int64_t nsync;
 };
 
 // dA_cumsum, dt_chunked, states and (packed sequences) the chunk table, each
-// on a kWsAlign boundary. p.nc counts chunk slots.
+// on a kWsAlign boundary. p.nc counts chunk slots. Where the one-pass path
+// applies, the states region is large enough for its ring and counters too.
 WsLayout ws_layout(const Plan& p, bool with_table = false) {
   WsLayout w;
   const size_t cs_bytes = size_t(p.batch * p.H * p.nc * p.Q) * sizeof(float);
-  const size_t st_bytes = size_t(p.batch * p.H * p.nc * p.P * p.N) * p.io_bytes();
+  size_t st_bytes = size_t(p.batch * p.H * p.nc * p.P * p.N) * p.io_bytes();
+  w.nsync = p.batch * p.H + 2;
+  w.ring_off = 0;
+  w.sync_off = 0;
+  if (!with_table && fused_forward_supported(p)) {
+    const size_t ring = align_up(fused_ring_bytes(p), kWsAlign);
+    const size_t need = ring + align_up(size_t(w.nsync) * sizeof(uint32_t), kWsAlign);
+    if (need > st_bytes) st_bytes = need;
+    w.sync_off = ring;
+  }
   w.cs_off = 0;
   w.dt_off = align_up(w.cs_off + cs_bytes, kWsAlign);
   w.st_off = align_up(w.dt_off + cs_bytes, kWsAlign);
+  w.ring_off += w.st_off;
+  w.sync_off += w.st_off;
   w.tab_off = align_up(w.st_off + st_bytes, kWsAlign);
   w.seq_off = align_up(w.tab_off + size_t(p.nc) * sizeof(ChunkInfo), kWsAlign);
   w.total = with_table ? align_up(w.seq_off + size_t(p.nseq) * sizeof(int2), kWsAlign) : w.tab_off;
@@ -187,6 +203,97 @@ hipError_t run_chunk_scan(const Plan& p, const void* x, const void* B, const voi
   return launch_chunk_scan_simt(p, x, B, C, D, cs, dtc, st, y, s);
 }
 
+// Which path ssd_forward takes. The one-pass kernel hands states from chunk
+// to chunk through a chain per head, so it is chosen only where it is
+// supported and the chains are short; SSD_FORWARD_PATH=split|fused overrides
+// the choice (fused only where supported).
+constexpr int64_t kFusedMaxChunks = 0;
+bool use_fused(const Plan& p) {
+  if (!fused_forward_supported(p)) return false;
+  static const int force = [] {
+    const char* v = std::getenv("SSD_FORWARD_PATH");
+    if (v == nullptr) return 0;
+    if (std::strcmp(v, "split") == 0) return 1;
+    if (std::strcmp(v, "fused") == 0) return 2;
+    return 0;
+  }();
+  if (force != 0) return force == 2;
+  return p.nc <= kFusedMaxChunks;
+}
+
+// Argument checks shared by the whole-forward entry points (batched layout).
+ssd_status_t check_forward(const Plan& p, const void* x, const float* dt, const float* A, const void* B,
+                           const void* C, const float* D, const float* init_state, const void* y,
+                           const float* final_state, const void* workspace, size_t workspace_bytes,
+                           const WsLayout& ws) {
+  if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL_POINTER;
+  if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(init_state, 16) ||
+      !aligned(final_state, 16) || !aligned(dt, 4) || !aligned(A, 4) || !aligned(D, 4) ||
+      !aligned(workspace, kWsAlign))
+    return SSD_ERR_ALIGNMENT;
+  if (workspace != nullptr && workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
+
+  const size_t io = p.io_bytes();
+  const size_t xy_bytes = size_t(p.batch * p.L * p.H * p.P) * io;
+  const size_t bc_bytes = size_t(p.batch * p.L * p.G * p.N) * io;
+  const size_t dt_bytes = size_t(p.batch * p.L * p.H) * sizeof(float);
+  const size_t hd_bytes = size_t(p.H) * sizeof(float);
+  const size_t st_bytes = size_t(p.batch * p.H * p.P * p.N) * sizeof(float);
+  const Range in[] = {range_of(x, xy_bytes), range_of(dt, dt_bytes), range_of(A, hd_bytes),
+                      range_of(B, bc_bytes), range_of(C, bc_bytes),   range_of(D, hd_bytes),
+                      range_of(init_state, st_bytes)};
+  const Range ry = range_of(y, xy_bytes);
+  const Range rf = range_of(final_state, st_bytes);
+  const Range rw = range_of(workspace, ws.total);
+  for (const Range& r : in) {
+    if (overlap(ry, r)) return SSD_ERR_ALIAS;
+    if (overlap(rw, r)) return SSD_ERR_ALIAS;
+    // final_state may be exactly init_state (in-place); any other overlap is an error
+    if (overlap(rf, r) && !(r.lo == reinterpret_cast<uintptr_t>(init_state) && rf.lo == r.lo)) return SSD_ERR_ALIAS;
+  }
+  if (overlap(ry, rf) || overlap(ry, rw) || overlap(rf, rw)) return SSD_ERR_ALIAS;
+  return SSD_OK;
+}
+
+// Enqueue the whole forward on `s` (the workspace allocated in stream order
+// when the caller passes none).
+ssd_status_t enqueue_forward(const Plan& p, bool fused, const void* x, const float* dt, const float* A,
+                             const void* B, const void* C, const float* D, const float* init_state, void* y,
+                             float* final_state, void* workspace, const WsLayout& ws, hipStream_t s) {
+  void* wbase = workspace;
+  bool owned = false;
+  if (wbase == nullptr) {
+    if (hipMallocAsync(&wbase, ws.total, s) != hipSuccess) return SSD_ERR_HIP;
+    owned = true;
+  }
+  char* w = static_cast<char*>(wbase);
+  float* cs = reinterpret_cast<float*>(w + ws.cs_off);
+  float* dtc = reinterpret_cast<float*>(w + ws.dt_off);
+  void* states = w + ws.st_off;
+  if (debug_enabled())
+    std::fprintf(stderr, "[ssd] B=%lld L=%lld H=%lld P=%lld N=%lld G=%lld io=%s Q=%d nc=%lld ws=%zu path=%s\n",
+                 (long long)p.batch, (long long)p.L, (long long)p.H, (long long)p.P, (long long)p.N,
+                 (long long)p.G, p.io == kBF16 ? "bf16" : "fp32", p.Q, (long long)p.nc, ws.total,
+                 fused ? "fused" : (mfma_chunk_scan_supported(p) ? "split-mfma" : "split-simt"));
+  hipError_t e;
+  if (fused) {
+    uint32_t* sync = reinterpret_cast<uint32_t*>(w + ws.sync_off);
+    FusedArgs a{x,    B,       C,  D,   cs, dtc, init_state, y, final_state, reinterpret_cast<float*>(w + ws.ring_off),
+                sync, sync + p.batch * p.H, sync + p.batch * p.H + 1};
+    e = launch_chunk_cumsum_clear(p, dt, A, cs, dtc, sync, ws.nsync, s);
+    if (e == hipSuccess) e = launch_fused_forward(p, a, s);
+  } else {
+    e = run_cumsum_chunk_state(p, x, B, dt, A, cs, dtc, states, s);
+    if (e == hipSuccess) e = launch_state_passing(p, states, cs, init_state, final_state, s);
+    if (e == hipSuccess) e = run_chunk_scan(p, x, B, C, D, cs, dtc, states, y, s);
+  }
+  if (owned) {
+    const hipError_t fe = hipFreeAsync(wbase, s);
+    if (e == hipSuccess) e = fe;
+  }
+  return from_hip(e);
+}
+
 }  // namespace
 }  // namespace ssd
 
@@ -233,62 +340,26 @@ ssd_status_t ssd_forward(const ssd_desc_t* desc, const void* x, const float* dt,
   Plan p;
   ssd_status_t st = ssd::make_plan(desc, &p);
   if (st != SSD_OK) return st;
-  if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL_POINTER;
-  if (!ssd::aligned(x, 16) || !ssd::aligned(B, 16) || !ssd::aligned(C, 16) || !ssd::aligned(y, 16) ||
-      !ssd::aligned(init_state, 16) || !ssd::aligned(final_state, 16) || !ssd::aligned(dt, 4) ||
-      !ssd::aligned(A, 4) || !ssd::aligned(D, 4) || !ssd::aligned(workspace, ssd::kWsAlign))
-    return SSD_ERR_ALIGNMENT;
   const ssd::WsLayout ws = ssd::ws_layout(p);
-  if (workspace != nullptr && workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
+  st = ssd::check_forward(p, x, dt, A, B, C, D, init_state, y, final_state, workspace, workspace_bytes, ws);
+  if (st != SSD_OK) return st;
+  return ssd::enqueue_forward(p, ssd::use_fused(p), x, dt, A, B, C, D, init_state, y, final_state, workspace, ws,
+                              static_cast<hipStream_t>(stream));
+}
 
-  const size_t io = p.io_bytes();
-  const size_t xy_bytes = size_t(p.batch * p.L * p.H * p.P) * io;
-  const size_t bc_bytes = size_t(p.batch * p.L * p.G * p.N) * io;
-  const size_t dt_bytes = size_t(p.batch * p.L * p.H) * sizeof(float);
-  const size_t hd_bytes = size_t(p.H) * sizeof(float);
-  const size_t st_bytes = size_t(p.batch * p.H * p.P * p.N) * sizeof(float);
-  const ssd::Range in[] = {ssd::range_of(x, xy_bytes),   ssd::range_of(dt, dt_bytes),
-                           ssd::range_of(A, hd_bytes),   ssd::range_of(B, bc_bytes),
-                           ssd::range_of(C, bc_bytes),   ssd::range_of(D, hd_bytes),
-                           ssd::range_of(init_state, st_bytes)};
-  const ssd::Range ry = ssd::range_of(y, xy_bytes);
-  const ssd::Range rf = ssd::range_of(final_state, st_bytes);
-  const ssd::Range rw = ssd::range_of(workspace, ws.total);
-  for (const ssd::Range& r : in) {
-    if (ssd::overlap(ry, r)) return SSD_ERR_ALIAS;
-    if (ssd::overlap(rw, r)) return SSD_ERR_ALIAS;
-    // final_state may be exactly init_state (in-place); any other overlap is an error
-    if (ssd::overlap(rf, r) && !(r.lo == reinterpret_cast<uintptr_t>(init_state) && rf.lo == r.lo))
-      return SSD_ERR_ALIAS;
-  }
-  if (ssd::overlap(ry, rf) || ssd::overlap(ry, rw) || ssd::overlap(rf, rw)) return SSD_ERR_ALIAS;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  void* wbase = workspace;
-  bool owned = false;
-  if (wbase == nullptr) {
-    if (hipMallocAsync(&wbase, ws.total, s) != hipSuccess) return SSD_ERR_HIP;
-    owned = true;
-  }
-  char* w = static_cast<char*>(wbase);
-  float* cs = reinterpret_cast<float*>(w + ws.cs_off);
-  float* dtc = reinterpret_cast<float*>(w + ws.dt_off);
-  void* states = w + ws.st_off;
-  if (ssd::debug_enabled())
-    std::fprintf(stderr, "[ssd] B=%lld L=%lld H=%lld P=%lld N=%lld G=%lld io=%s Q=%d nc=%lld ws=%zu state=%s scan=%s\n",
-                 (long long)p.batch, (long long)p.L, (long long)p.H, (long long)p.P, (long long)p.N,
-                 (long long)p.G, p.io == ssd::kBF16 ? "bf16" : "fp32", p.Q, (long long)p.nc, ws.total,
-                 ssd::mfma_chunk_state_supported(p) ? "mfma" : "simt",
-                 ssd::mfma_chunk_scan_supported(p) ? "mfma" : "simt");
-
-  hipError_t e = ssd::run_cumsum_chunk_state(p, x, B, dt, A, cs, dtc, states, s);
-  if (e == hipSuccess) e = ssd::launch_state_passing(p, states, cs, init_state, final_state, s);
-  if (e == hipSuccess) e = ssd::run_chunk_scan(p, x, B, C, D, cs, dtc, states, y, s);
-  if (owned) {
-    const hipError_t fe = hipFreeAsync(wbase, s);
-    if (e == hipSuccess) e = fe;
-  }
-  return ssd::from_hip(e);
+ssd_status_t ssd_forward_fused(const ssd_desc_t* desc, const void* x, const float* dt, const float* A,
+                               const void* B, const void* C, const float* D, const float* init_state,
+                               void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  Plan p;
+  ssd_status_t st = ssd::make_plan(desc, &p);
+  if (st != SSD_OK) return st;
+  if (!ssd::fused_forward_supported(p)) return SSD_ERR_UNSUPPORTED;
+  const ssd::WsLayout ws = ssd::ws_layout(p);
+  st = ssd::check_forward(p, x, dt, A, B, C, D, init_state, y, final_state, workspace, workspace_bytes, ws);
+  if (st != SSD_OK) return st;
+  return ssd::enqueue_forward(p, true, x, dt, A, B, C, D, init_state, y, final_state, workspace, ws,
+                              static_cast<hipStream_t>(stream));
 }
 
 ssd_status_t ssd_workspace_bytes_varlen(const ssd_desc_t* desc, int64_t num_seqs, size_t* bytes) {

@@ -14,6 +14,8 @@
 // axis) into LDS; then one wavefront per head scans the Q positions: each lane
 // owns Q/64 consecutive positions, scans them serially, and the lane totals
 // are combined with a log-step wavefront scan (__shfl_up).
+// Optionally the launch also sets a run of 32-bit words to zero (the
+// counters the one-pass kernel that follows synchronises on).
 #include "chunk_cumsum.h"
 
 namespace ssd {
@@ -26,7 +28,8 @@ template <int Q>
 __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(
     const float* __restrict__ dt, const float* __restrict__ A,
     float* __restrict__ dA_cs, float* __restrict__ dtc,
-    int64_t L, int H, int64_t nc, DtOpts dto, const ChunkInfo* __restrict__ ctab) {
+    int64_t L, int H, int64_t nc, DtOpts dto, const ChunkInfo* __restrict__ ctab,
+    uint32_t* __restrict__ clear, int64_t nclear) {
   constexpr int QPL = Q / 64;  // positions per lane
   __shared__ float tile[Q][kHB + 1];
   const int64_t c = blockIdx.x;
@@ -34,6 +37,11 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(
   const int h0 = blockIdx.z * kHB;
   const int hb = min(kHB, H - h0);
   const int tid = threadIdx.x;
+  if (clear != nullptr) {
+    const int64_t nthreads = int64_t(gridDim.x) * gridDim.y * gridDim.z * kThreads;
+    const int64_t gid = ((int64_t(blockIdx.z) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * kThreads + tid;
+    for (int64_t i = gid; i < nclear; i += nthreads) clear[i] = 0u;
+  }
 
   int64_t row0;
   int rows;
@@ -66,23 +74,31 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(
 
 }  // namespace
 
-hipError_t launch_chunk_cumsum(const Plan& p, const float* dt, const float* A,
-                               float* dA_cs, float* dtc, hipStream_t s) {
+hipError_t launch_chunk_cumsum_clear(const Plan& p, const float* dt, const float* A, float* dA_cs, float* dtc,
+                                     uint32_t* clear, int64_t nclear, hipStream_t s) {
   dim3 grid((unsigned)p.nc, (unsigned)p.batch, (unsigned)((p.H + kHB - 1) / kHB));
   switch (p.Q) {
     case 64:
-      chunk_cumsum_kernel<64><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab);
+      chunk_cumsum_kernel<64><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab, clear,
+                                                        nclear);
       break;
     case 128:
-      chunk_cumsum_kernel<128><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab);
+      chunk_cumsum_kernel<128><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab, clear,
+                                                         nclear);
       break;
     case 256:
-      chunk_cumsum_kernel<256><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab);
+      chunk_cumsum_kernel<256><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab, clear,
+                                                         nclear);
       break;
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_chunk_cumsum(const Plan& p, const float* dt, const float* A,
+                               float* dA_cs, float* dtc, hipStream_t s) {
+  return launch_chunk_cumsum_clear(p, dt, A, dA_cs, dtc, nullptr, 0, s);
 }
 
 }  // namespace ssd

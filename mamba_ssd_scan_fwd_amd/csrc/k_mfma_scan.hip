@@ -62,7 +62,7 @@ struct ScanCfg {
   static constexpr int NK = (N + 31) / 32;    // 32-deep steps over n
   static constexpr int NGT = R - 1;           // off-diagonal G^T tiles per wavefront
   // x: Q rows of P bf16, Hin: P rows of N bf16, each in its natural row
-  // order with the 16-byte chunks of a row permuted (xsw, hsw); both are
+  // order with the 16-byte chunks of a row permuted (scan_xsw, scan_hsw); both are
   // filled in 1 KB blocks by loads that write the LDS directly
   static constexpr int XRB = 2 * P, HRB = 2 * N, HCPR = N / 8;
   static constexpr int XBLK = Q * P * 2 / 1024;
@@ -98,23 +98,6 @@ struct ScanCfg {
 
 template <int Q>
 constexpr int kScanThreads = 2 * Q;
-
-// Chunk permutations of the staged rows: row r's 16-byte chunk c is stored
-// at chunk position c ^ sw(r), sw(r) the XOR of one constant per set bit of
-// r mod 16 (row_xor). The constants keep the operand reads free of bank
-// conflicts on gfx950 (64 banks of 4 bytes): the transposing 8-byte x read
-// covers four consecutive rows and two adjacent chunks per 16 lanes; the
-// 16-byte Hin read serves its eight-lane groups in the pairs (0-7, 24-31),
-// (8-15, 16-23), ... (as measured), each pair reading eight consecutive rows
-// p at the chunk of one g4 and eight rows at the next chunk.
-template <int P>
-__device__ __forceinline__ int xsw(int j) {  // x rows: P bf16
-  return P == 32 ? row_xor(j, 0, 2, 2, 0) : P == 64 ? row_xor(j, 2, 4, 2, 0) : P == 128 ? row_xor(j, 2, 4, 8, 0) : 0;
-}
-template <int N>
-__device__ __forceinline__ int hsw(int p) {  // Hin rows: N bf16
-  return N == 16 ? 0 : N == 32 ? row_xor(p, 0, 0, 1, 2) : N == 64 ? row_xor(p, 0, 1, 2, 4) : row_xor(p, 1, 2, 4, 8);
-}
 
 template <int P, int N, int Q>
 __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu(2))) void chunk_scan_mfma_kernel(
@@ -168,13 +151,13 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   for (int k = 0; k < C::XBPW; ++k) {
     const int pos = (wave * C::XBPW + k) * 1024 + 16 * lane;
     const int j = pos / C::XRB, cp = (pos % C::XRB) / 16;
-    xgo[k] = (uint32_t)(j * H * P * 2 + 16 * (cp ^ xsw<P>(j)));
+    xgo[k] = (uint32_t)(j * H * P * 2 + 16 * (cp ^ scan_xsw<P>(j)));
   }
 #pragma unroll
   for (int k = 0; k < C::HBPW; ++k) {
     const int pos = (wave * C::HBPW + k) * 1024 + 16 * lane;  // past P*N*2: padding, reads zeros
     const int p = pos / C::HRB, cp = (pos % C::HRB) / 16;
-    hgo[k] = (uint32_t)(p * C::HRB + 16 * (cp ^ hsw<N>(p)));
+    hgo[k] = (uint32_t)(p * C::HRB + 16 * (cp ^ scan_hsw<N>(p)));
   }
   float lpre = 0.f, dpre = 0.f, tl1 = 0.f, tl2 = 0.f;
   // thread e < R*R tabulates exp(l_{16 r} - l_{16 t + 15}), r = e / R, t = e % R.
@@ -319,10 +302,10 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
     const int j = 4 * q + (s >> 2);
 #pragma unroll
     for (int pt = 0; pt < NTP; ++pt)
-      xoff[pt] = C::OFF_X + j * C::XRB + 16 * ((2 * pt + ((s & 3) >> 1)) ^ xsw<P>(j)) + 8 * (s & 1);
+      xoff[pt] = C::OFF_X + j * C::XRB + 16 * ((2 * pt + ((s & 3) >> 1)) ^ scan_xsw<P>(j)) + 8 * (s & 1);
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks)
-      hoff[ks] = C::OFF_H + r16 * C::HRB + 16 * (((4 * ks + g4) % C::HCPR) ^ hsw<N>(r16));
+      hoff[ks] = C::OFF_H + r16 * C::HRB + 16 * (((4 * ks + g4) % C::HCPR) ^ scan_hsw<N>(r16));
   }
   vm_wait<0>();
   __syncthreads();

@@ -97,6 +97,25 @@ __device__ __forceinline__ constexpr int row_xor(int r, int m0, int m1, int m2, 
   return ((r & 1) ? m0 : 0) ^ ((r & 2) ? m1 : 0) ^ ((r & 4) ? m2 : 0) ^ ((r & 8) ? m3 : 0);
 }
 
+// Chunk permutations of tiles staged row by row in the LDS for the chunk
+// output kernels: row r's 16-byte chunk c is stored at chunk position
+// c ^ sw(r), sw(r) the XOR of one constant per set bit of r mod 16
+// (row_xor). The constants keep the operand reads free of bank conflicts on
+// gfx950 (64 banks of 4 bytes): the transposing 8-byte read of x rows covers
+// four consecutive rows and two adjacent chunks per 16 lanes; the 16-byte
+// read of rows of N bf16 (the entering state, B) serves its eight-lane groups
+// in the pairs (0-7, 24-31), (8-15, 16-23), ... (as measured), each pair
+// reading eight consecutive rows at the chunk of one lane group and eight
+// rows at the next chunk.
+template <int P>
+__device__ __forceinline__ int scan_xsw(int j) {  // rows of P bf16 (x)
+  return P == 32 ? row_xor(j, 0, 2, 2, 0) : P == 64 ? row_xor(j, 2, 4, 2, 0) : P == 128 ? row_xor(j, 2, 4, 8, 0) : 0;
+}
+template <int N>
+__device__ __forceinline__ int scan_hsw(int p) {  // rows of N bf16 (Hin, B)
+  return N == 16 ? 0 : N == 32 ? row_xor(p, 0, 0, 1, 2) : N == 64 ? row_xor(p, 0, 1, 2, 4) : row_xor(p, 1, 2, 4, 8);
+}
+
 // A raw buffer descriptor over [base, base + bytes) as four scalar words
 // (base and bytes wavefront-uniform).
 typedef int v4i32_t __attribute__((ext_vector_type(4)));

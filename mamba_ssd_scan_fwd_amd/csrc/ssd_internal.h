@@ -53,6 +53,29 @@ hipError_t launch_chunk_scan(const Plan& p, const void* x, const void* B, const 
                              const float* D, const float* dA_cs, const float* dtc,
                              const void* states, void* y, hipStream_t s);
 
+// Steps 1 to 5 on the one-pass path: the cumsum launch (which also clears
+// the words the chain synchronises on) and the fused state/output kernel.
+struct FusedArgs {
+  const void* x;
+  const void* B;
+  const void* C;
+  const float* D;
+  const float* dA_cs;
+  const float* dtc;
+  const float* h_init;  // [batch, H, P, N] fp32 or nullptr (zeros)
+  void* y;
+  float* h_final;       // [batch, H, P, N] fp32 or nullptr
+  float* ring;          // [batch, H, 2, P * N] fp32 hand-over slots
+  uint32_t* flags;      // [batch * H] per-head chunk counters, zero at launch
+  uint32_t* ticket;     // workgroup ticket counter, zero at launch
+  uint32_t* status;     // bit 0: a wait for a state was cut off, zero at launch
+};
+bool fused_forward_supported(const Plan& p);
+size_t fused_ring_bytes(const Plan& p);
+hipError_t launch_chunk_cumsum_clear(const Plan& p, const float* dt, const float* A, float* dA_cs, float* dtc,
+                                     uint32_t* clear, int64_t nclear, hipStream_t s);
+hipError_t launch_fused_forward(const Plan& p, const FusedArgs& a, hipStream_t s);
+
 hipError_t launch_conv1d_split(const Plan& p, int K, const void* xbc, const float* w, const float* bias, int act,
                                const float* st_in, float* st_out, void* x, void* B, void* C, hipStream_t s);
 hipError_t launch_decode_step(const Plan& p, const void* x, const float* dt, const float* A, const void* B,

@@ -141,12 +141,12 @@ def fwd_args(d, **over):
     return ptrs, sizes
 
 
-def call_fwd(d, p, ws_bytes=None):
+def call_fwd(d, p, ws_bytes=None, entry="ssd_forward"):
     L = lib()
     v = lambda k: None if p[k] is None else ctypes.c_void_p(p[k])  # noqa: E731
     wsb = ssd.workspace_bytes(d) if ws_bytes is None else ws_bytes
-    return L.ssd_forward(ctypes.byref(d), v("x"), v("dt"), v("A"), v("B"), v("C"), v("D"), v("h0"),
-                         v("y"), v("hT"), v("ws"), ctypes.c_size_t(wsb), None)
+    return getattr(L, entry)(ctypes.byref(d), v("x"), v("dt"), v("A"), v("B"), v("C"), v("D"), v("h0"),
+                             v("y"), v("hT"), v("ws"), ctypes.c_size_t(wsb), None)
 
 
 @pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "y"])
@@ -282,3 +282,47 @@ def test_default_chunk_rule():
     assert ssd.effective_chunk_size(desc(dstate=256)) == 256
     assert ssd.effective_chunk_size(desc(headdim=32, dstate=16)) == 256
     assert ssd.effective_chunk_size(desc(headdim=128)) == 128
+
+
+# ---- the one-pass entry point --------------------------------------------
+
+@pytest.mark.parametrize("kw", [dict(io_dtype="fp32"), dict(chunk_size=128), dict(chunk_size=64),
+                                dict(headdim=128), dict(headdim=16), dict(dstate=256), dict(dstate=16),
+                                dict(headdim=32, dstate=32)])
+def test_fused_entry_rejects_unsupported_shapes(kw):
+    d = desc(**kw)
+    p, _ = fwd_args(d)
+    assert call_fwd(d, p, entry="ssd_forward_fused") == UNSUP
+
+
+def test_fused_entry_validates_like_forward():
+    d = desc()
+    p, s = fwd_args(d, x=None)
+    assert call_fwd(d, p, entry="ssd_forward_fused") == NULLP
+    p, s = fwd_args(d)
+    p["B"] += 8
+    assert call_fwd(d, p, entry="ssd_forward_fused") == ALIGN
+    p, s = fwd_args(d)
+    assert call_fwd(d, p, ws_bytes=ssd.workspace_bytes(d) - 256, entry="ssd_forward_fused") == WS
+    p, s = fwd_args(d)
+    p["y"] = p["B"] + s["B"] - 1024
+    assert call_fwd(d, p, entry="ssd_forward_fused") == ALIAS
+
+
+@pytest.mark.parametrize("L", [1, 256, 700, 2048])
+def test_workspace_covers_the_one_pass_hand_over_area(L):
+    """Where the one-pass kernel applies, the states region holds its fp32
+    hand-over ring (two slots per head) and the per-head counters, even when
+    there are fewer chunks than the ring has slots' worth of bf16 states."""
+    lib()
+    d = desc(seqlen=L)
+    nc = -(-L // 256)
+
+    def up(v):
+        return -(-v // 256) * 256
+
+    cs = 8 * 64 * nc * 256 * 4
+    st = 8 * 64 * nc * 64 * 128 * 2
+    ring = 8 * 64 * 2 * 64 * 128 * 4
+    sync = up((8 * 64 + 2) * 4)
+    assert ssd.workspace_bytes(d) == up(up(up(cs) + cs) + max(st, up(ring) + sync))
