@@ -80,6 +80,10 @@ struct FusedCfg {
   // the ticket is passed to the workgroup through the Hin area, which is
   // first written several barriers later
   static constexpr int OFF_TK = OFF_HIN;
+  // read the next pair's operands during the current pair's products where
+  // the registers allow it (two operand sets live at once)
+  static constexpr bool PIPE = N <= 64;
+  static constexpr int YST = RG * NTP / 2;  // y stores per lane and head
   static_assert(N >= 32 && P >= 32, "tile shapes");
   static_assert(TOTAL <= 160 * 1024, "LDS");
   static_assert(fused_shape_ok(P, N, Q), "shape");
@@ -339,7 +343,11 @@ __global__ __launch_bounds__(2 * Q) __attribute__((amdgpu_waves_per_eu(2))) void
       if (ta >= rk[1]) break;  // wavefront-uniform
       __builtin_amdgcn_sched_barrier(0);
       if (pre && kp < C::XBPW) fetch_x_block(h + 1, nbo, kp);
-      if (kp + 1 < NM) load_pair(kp + 1, ops[(kp + 1) & 1]);
+      if constexpr (C::PIPE) {
+        if (kp + 1 < NM) load_pair(kp + 1, ops[(kp + 1) & 1]);
+      } else if (kp > 0) {
+        load_pair(kp, ops[kp & 1]);
+      }
       const PairOps& o = ops[kp & 1];
 #pragma unroll
       for (int k = 0; k < RG; ++k) {
@@ -405,36 +413,11 @@ __global__ __launch_bounds__(2 * Q) __attribute__((amdgpu_waves_per_eu(2))) void
       for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(a[pt], dop_lo, acc[k][pt]);
     }
 
-    // ---- chunk state S_c^T[n][p] = sum_j w_j B[j][n] x[j][p]: A operand the
-    // weighted B^T fragments (row n, k = j), B operand the x fragments
-    // (column p, k = j), both in the k order of the transposing read ----
-    f32x4_t sacc[C::SA][C::SB];
-#pragma unroll
-    for (int ni = 0; ni < C::SA; ++ni)
-#pragma unroll
-      for (int pi = 0; pi < C::SB; ++pi) sacc[ni][pi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const float4 wa = *reinterpret_cast<const float4*>(sW + 32 * m + 4 * g4);
-      const float4 wb = *reinterpret_cast<const float4*>(sW + 32 * m + 16 + 4 * g4);
-      uint4 xa[C::SB];
-#pragma unroll
-      for (int pi = 0; pi < C::SB; ++pi) xa[pi] = xfrag(m, pt0 + pi);
-#pragma unroll
-      for (int ni = 0; ni < C::SA; ++ni) {
-        const unsigned char* a = lds + boff[ni] + m * 32 * C::HRB;
-        const uint2 lo = lds_tr8(a), hi = lds_tr8(a + 16 * C::HRB);
-        const bf16x8_t bt = as_bf16x8(make_uint4(
-            pack_bf16x2(bf16_lo(lo.x) * wa.x, bf16_hi(lo.x) * wa.y), pack_bf16x2(bf16_lo(lo.y) * wa.z, bf16_hi(lo.y) * wa.w),
-            pack_bf16x2(bf16_lo(hi.x) * wb.x, bf16_hi(hi.x) * wb.y), pack_bf16x2(bf16_lo(hi.y) * wb.z, bf16_hi(hi.y) * wb.w)));
-#pragma unroll
-        for (int pi = 0; pi < C::SB; ++pi) sacc[ni][pi] = mfma_16x16x32(bt, as_bf16x8(xa[pi]), sacc[ni][pi]);
-      }
-    }
-
-    // ---- the state chain: Hin = H_{c-1} (the initial state for c = 0), then
-    // H_c = exp(Lam_c) Hin + S_c. Lane holds Hin[p][n .. n+3] of each of its
-    // tiles, p = 16 (pt0 + pi) + r16, n = 16 (nt0 + ni) + 4 g4. ----
+    // ---- the state chain: Hin = H_{c-1} (the initial state for c = 0), then,
+    // once the chunk state below is done, H_c = exp(Lam_c) Hin + S_c. Lane
+    // holds Hin[p][n .. n+3] of each of its tiles, p = 16 (pt0 + pi) + r16,
+    // n = 16 (nt0 + ni) + 4 g4. The loads are issued before the chunk-state
+    // product so that it runs while they are in flight. ----
     f32x4_t hin[C::SA][C::SB];
     // slot tile (ni, pi) of this wavefront: 256 floats, lane l at 4 l
     auto slot_off = [&](int ni, int pi) { return (uint32_t)(((wave * C::SA + ni) * C::SB + pi) * 1024 + 16 * lane); };
@@ -477,6 +460,33 @@ __global__ __launch_bounds__(2 * Q) __attribute__((amdgpu_waves_per_eu(2))) void
           hin[ni][pi] = __builtin_bit_cast(f32x4_t, v);
         }
     }
+    // ---- chunk state S_c^T[n][p] = sum_j w_j B[j][n] x[j][p]: A operand the
+    // weighted B^T fragments (row n, k = j), B operand the x fragments
+    // (column p, k = j), both in the k order of the transposing read ----
+    f32x4_t sacc[C::SA][C::SB];
+#pragma unroll
+    for (int ni = 0; ni < C::SA; ++ni)
+#pragma unroll
+      for (int pi = 0; pi < C::SB; ++pi) sacc[ni][pi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const float4 wa = *reinterpret_cast<const float4*>(sW + 32 * m + 4 * g4);
+      const float4 wb = *reinterpret_cast<const float4*>(sW + 32 * m + 16 + 4 * g4);
+      uint4 xa[C::SB];
+#pragma unroll
+      for (int pi = 0; pi < C::SB; ++pi) xa[pi] = xfrag(m, pt0 + pi);
+#pragma unroll
+      for (int ni = 0; ni < C::SA; ++ni) {
+        const unsigned char* a = lds + boff[ni] + m * 32 * C::HRB;
+        const uint2 lo = lds_tr8(a), hi = lds_tr8(a + 16 * C::HRB);
+        const bf16x8_t bt = as_bf16x8(make_uint4(
+            pack_bf16x2(bf16_lo(lo.x) * wa.x, bf16_hi(lo.x) * wa.y), pack_bf16x2(bf16_lo(lo.y) * wa.z, bf16_hi(lo.y) * wa.w),
+            pack_bf16x2(bf16_lo(hi.x) * wb.x, bf16_hi(hi.x) * wb.y), pack_bf16x2(bf16_lo(hi.y) * wb.z, bf16_hi(hi.y) * wb.w)));
+#pragma unroll
+        for (int pi = 0; pi < C::SB; ++pi) sacc[ni][pi] = mfma_16x16x32(bt, as_bf16x8(xa[pi]), sacc[ni][pi]);
+      }
+    }
+
     {
       const float eL = __expf(sL[Q - 1]);
       if (!last) {
@@ -511,13 +521,7 @@ __global__ __launch_bounds__(2 * Q) __attribute__((amdgpu_waves_per_eu(2))) void
               make_uint2(pack_bf16x2(hin[ni][pi][0], hin[ni][pi][1]), pack_bf16x2(hin[ni][pi][2], hin[ni][pi][3]));
         }
     }
-    // every wavefront's state stores (and its loads of the next head) have
-    // completed; after the barrier the head's flag is raised
-    asm volatile("" ::: "memory");
-    vm_wait<0>();
-    __syncthreads();
-    if (tid == 0 && !last)
-      __hip_atomic_store(flags + bh, (uint32_t)(c + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();  // Hin in the LDS
 
     // ---- chunk output: Y^T[p][i] += exp(l_i) sum_n Hin[p][n] C_i[n] ----
     {
@@ -557,7 +561,15 @@ __global__ __launch_bounds__(2 * Q) __attribute__((amdgpu_waves_per_eu(2))) void
       }
     }
     if (pre) stage_tables(nbuf);
+    // Everything but the y stores just issued has completed: the state
+    // stores (vector memory operations complete in issue order) and the
+    // loads of the next head. After the barrier every wavefront's part of
+    // H_c is in memory and the head's flag is raised.
+    asm volatile("" ::: "memory");
+    vm_wait<C::YST>();
     __syncthreads();
+    if (tid == 0 && !last)
+      __hip_atomic_store(flags + bh, (uint32_t)(c + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -34,6 +34,7 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const bf16x8_t& a, const bf16x8
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
+__device__ __forceinline__ bf16x8_t as_bf16x8(const bf16x8_t& v) { return v; }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
