@@ -10,7 +10,14 @@ Besides the headline tokens/s, it times every kernel on its own with HIP
 events recorded on the stream the kernels run on, and reports the dominant
 kernel against its roofline (algorithmic bytes or flops per launch divided
 by its average duration), next to the fp64 CPU oracle timed on a bounded
-sample of the same workload.
+sample of the same workload. It also times the one-pass path
+(ssd_forward_fused) next to the split path on the headline workload and on a
+larger-batch workload, where ssd_forward takes the one-pass path.
+
+Before the W warm-up steps the GPU runs forward passes for --device-warm-ms
+(untimed): from idle, its clocks take a few hundred milliseconds of load to
+reach their steady state, and a timed region that starts earlier measures
+the ramp (about 10% slower on the headline workload).
 """
 
 from __future__ import annotations
@@ -41,6 +48,9 @@ def parse():
     ap.add_argument("--config", type=int, default=1, help="workload index (1 = the headline workload)")
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--kernel-reps", type=int, default=None)
+    ap.add_argument("--device-warm-ms", type=float, default=500.0,
+                    help="untimed forward passes before the warm-up steps, to reach steady clocks")
+    ap.add_argument("--no-one-pass", action="store_true", help="skip the one-pass path measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step, packed-sequence and convolution measurements")
     ap.add_argument("--cpu-sample-seqs", type=int, default=8)
@@ -253,6 +263,70 @@ def conv_measure(cfg, steps, dev):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def one_pass_measure(cfg, steps, dev, bufs=None):
+    """The one-pass path (ssd_forward_fused: the dt cumsum, then one kernel
+    for chunk states, state hand-over and chunk output) next to the split
+    path, on the same buffers: time per forward pass each, which one
+    ssd_forward takes, and the one-pass kernel's algorithmic bytes (x and y,
+    B and C, dA_cumsum and dt_chunked once, each hand-over state written and
+    read once in fp32, the final state). `bufs` = (inputs, y, final state,
+    workspace) already allocated for `cfg`, else fresh ones (the two paths are
+    always compared on the same buffers: where in HBM the buffers lie changes
+    both paths' times)."""
+    import torch
+
+    import mamba_ssd_scan_fwd_amd as ssd
+    from ssd_inputs import make_inputs
+
+    desc = ssd.make_desc(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.io_dtype)
+    if bufs is None:
+        inp = make_inputs(cfg, seed=104)
+        d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+        y = torch.empty_like(d["x"])
+        hT = torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device=dev)
+        ws = torch.empty(ssd.workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    else:
+        d, y, hT, ws = bufs
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(**kw):
+        def run():
+            ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], y=y, final_state=hT,
+                        workspace=ws, **kw)
+        for _ in range(5):
+            run()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e3
+
+    split_us = timed(fused=False) if os.environ.get("SSD_FORWARD_PATH") is None else None
+    try:
+        fused_us = timed(fused=True)
+    except ssd.SSDError:
+        return {"workload": cfg.name, "supported": False}
+    # which path ssd_forward takes here: the one its own time matches
+    auto_us = timed()
+    T = cfg.tokens
+    Q = ssd.effective_chunk_size(desc)
+    nc = -(-cfg.seqlen // Q)
+    s = 2
+    H, P, N, G = cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
+    nbytes = (2 * T * H * P * s + 2 * T * G * N * s + 2 * cfg.batch * H * nc * Q * 4
+              + 2 * cfg.batch * H * (nc - 1) * P * N * 4 + cfg.batch * H * P * N * 4 * (2 if cfg.init_state else 1))
+    out = {"workload": f"{cfg.name}: B {cfg.batch}, L {cfg.seqlen}, H {H}, P {P}, N {N}, G {G}",
+           "supported": True, "one_pass_us": round(fused_us, 2), "one_pass_tokens_per_s": round(T / (fused_us * 1e-6), 1),
+           "one_pass_algo_bytes": nbytes}
+    if split_us is not None:
+        out.update({"split_us": round(split_us, 2), "split_tokens_per_s": round(T / (split_us * 1e-6), 1),
+                    "ssd_forward_takes": "one-pass" if abs(auto_us - fused_us) < abs(auto_us - split_us) else "split"})
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -294,6 +368,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < args.device_warm_ms / 1e3:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -418,6 +497,11 @@ def main():
         "mfma_frac_useful": round(m["flops"] / (durations[dom] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
     }
 
+    one_pass = None
+    if not args.no_one_pass and cfg.io_dtype == "bf16":
+        one_pass = [one_pass_measure(cfg, 30, dev, (d, y, hT, ws)),
+                    one_pass_measure(cfg.with_(name=f"{cfg.name} x4 batch", batch=4 * cfg.batch), 30, dev)]
+
     decode = None
     if not args.no_decode:
         decode = [decode_measure(cfg, bsz, 50, dev) for bsz in (cfg.batch, 256)]
@@ -453,6 +537,8 @@ def main():
         "decode_step": decode,
         "varlen": varlen,
         "conv1d_split": conv,
+        "one_pass": one_pass,
+        "device_warm_ms": args.device_warm_ms,
     }
     print(json.dumps(line), flush=True)
 

@@ -203,11 +203,10 @@ hipError_t run_chunk_scan(const Plan& p, const void* x, const void* B, const voi
   return launch_chunk_scan_simt(p, x, B, C, D, cs, dtc, st, y, s);
 }
 
-// Which path ssd_forward takes. The one-pass kernel hands states from chunk
-// to chunk through a chain per head, so it is chosen only where it is
-// supported and the chains are short; SSD_FORWARD_PATH=split|fused overrides
-// the choice (fused only where supported).
-constexpr int64_t kFusedMaxChunks = 0;
+// Which path ssd_forward takes: the one-pass kernel where it supports the
+// shape and is the faster one for it (fused_forward_preferred), else the
+// split path. SSD_FORWARD_PATH=split|fused overrides the choice (fused only
+// where supported).
 bool use_fused(const Plan& p) {
   if (!fused_forward_supported(p)) return false;
   static const int force = [] {
@@ -218,7 +217,7 @@ bool use_fused(const Plan& p) {
     return 0;
   }();
   if (force != 0) return force == 2;
-  return p.nc <= kFusedMaxChunks;
+  return fused_forward_preferred(p);
 }
 
 // Argument checks shared by the whole-forward entry points (batched layout).

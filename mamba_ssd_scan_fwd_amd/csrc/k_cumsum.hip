@@ -9,11 +9,12 @@
 // contiguous, so the contraction kernels read one contiguous run per
 // (b, h, c). Positions past the sequence end get dt = 0, so l stays flat.
 //
-// Mapping: one workgroup per (chunk, batch, block of HB heads). The dt tile
-// [Q][HB] is read with the head index fastest (coalesced along dt's innermost
-// axis) into LDS; then one wavefront per head scans the Q positions: each lane
-// owns Q/64 consecutive positions, scans them serially, and the lane totals
-// are combined with a log-step wavefront scan (__shfl_up).
+// Mapping: one workgroup per (chunk, batch, block of HB heads) with one
+// wavefront per head. The dt tile [Q][HB] is read with the head index fastest
+// (coalesced along dt's innermost axis) into LDS; then each wavefront scans
+// its head's Q positions: each lane owns Q/64 consecutive positions, scans
+// them serially, and the lane totals are combined with a log-step wavefront
+// scan (__shfl_up).
 // Optionally the launch also sets a run of 32-bit words to zero (the
 // counters the one-pass kernel that follows synchronises on).
 #include "chunk_cumsum.h"
@@ -21,8 +22,8 @@
 namespace ssd {
 namespace {
 
-constexpr int kHB = 16;       // heads per workgroup
-constexpr int kThreads = 256; // 4 wavefronts
+constexpr int kHB = 16;             // heads per workgroup
+constexpr int kThreads = 64 * kHB;  // one wavefront per head
 
 template <int Q>
 __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(

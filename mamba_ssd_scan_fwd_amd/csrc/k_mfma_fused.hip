@@ -634,6 +634,43 @@ bool fused_forward_supported(const Plan& p) {
   return true;
 }
 
+namespace {
+// workgroups resident per compute unit and heads per workgroup of the launch
+template <int P, int N, int Q>
+void fused_launch_shape(const Plan& p, int& resident, int& hb) {
+  using Cfg = FusedCfg<P, N, Q>;
+  const int by_waves = 8 / Cfg::WAVES;
+  const int by_lds = 160 * 1024 / Cfg::TOTAL;
+  resident = by_waves < by_lds ? by_waves : by_lds;
+  hb = pick_fused_heads(p, resident);
+}
+template <int P>
+bool fused_shape_of(const Plan& p, int& resident, int& hb) {
+  switch (p.N) {
+    case 32: if constexpr (fused_shape_ok(P, 32, 256)) { fused_launch_shape<P, 32, 256>(p, resident, hb); return true; } break;
+    case 64: if constexpr (fused_shape_ok(P, 64, 256)) { fused_launch_shape<P, 64, 256>(p, resident, hb); return true; } break;
+    case 128: if constexpr (fused_shape_ok(P, 128, 256)) { fused_launch_shape<P, 128, 256>(p, resident, hb); return true; } break;
+  }
+  return false;
+}
+}  // namespace
+
+// The one-pass kernel pays for its chains once per round of workgroups: the
+// last chunk's workgroup of a chain first waits for nc - 1 hand-overs (a few
+// microseconds each). It saves the second read of x and the state round trips
+// on every head-chunk. Measured on MI355X: it is ahead once the work takes at
+// least two rounds of workgroups with chains of at most 16 chunks, and behind
+// with one round (the hand-overs not amortised) or longer chains.
+bool fused_forward_preferred(const Plan& p) {
+  if (!fused_forward_supported(p) || p.nc > 16) return false;
+  int resident = 1, hb = 1;
+  const bool ok = p.P == 32 ? fused_shape_of<32>(p, resident, hb) : fused_shape_of<64>(p, resident, hb);
+  if (!ok) return false;
+  const int64_t wgs = p.batch * p.nc * (p.H / hb);
+  const int64_t slots = (int64_t)device_cu_count() * resident;
+  return wgs >= 2 * slots;
+}
+
 size_t fused_ring_bytes(const Plan& p) { return size_t(p.batch * p.H * 2) * size_t(p.P * p.N) * sizeof(float); }
 
 hipError_t launch_fused_forward(const Plan& p, const FusedArgs& a, hipStream_t s) {

@@ -71,6 +71,7 @@ struct FusedArgs {
   uint32_t* status;     // bit 0: a wait for a state was cut off, zero at launch
 };
 bool fused_forward_supported(const Plan& p);
+bool fused_forward_preferred(const Plan& p);  // supported and measured faster than the split path
 size_t fused_ring_bytes(const Plan& p);
 hipError_t launch_chunk_cumsum_clear(const Plan& p, const float* dt, const float* A, float* dA_cs, float* dtc,
                                      uint32_t* clear, int64_t nclear, hipStream_t s);
