@@ -86,11 +86,13 @@ def test_fused_edge_shapes(L, P, N, H, G, init):
     full_check(inp, TOL["bf16"], f"fused edge L={L} P={P} N={N} H={H} G={G}", fused=True)
 
 
-@pytest.mark.parametrize("L,H,G", [(1, 4, 1), (257, 4, 2), (3000, 32, 2), (41 * 256 - 243, 4, 1)])
-def test_fused_chain_completed(L, H, G):
+@pytest.mark.parametrize("L,H,G,batch", [(1, 4, 1, 2), (257, 4, 2, 2), (3000, 32, 2, 2), (41 * 256 - 243, 4, 1, 2),
+                                         (1100, 64, 1, 8), (2048, 64, 1, 8)])
+def test_fused_chain_completed(L, H, G, batch):
     """Every head's counter ends at the last hand-over (nc - 1), the tickets
-    cover the grid, and no wait was cut off."""
-    cfg = BASE.with_(seqlen=L, nheads=H, ngroups=G, init_state=True)
+    cover the grid, and no wait was cut off (batch 8 with 64 heads: the
+    headline's 32 chains of 16 heads)."""
+    cfg = BASE.with_(seqlen=L, nheads=H, ngroups=G, batch=batch, init_state=True)
     inp = make_inputs(cfg, seed=L + H)
     d = to_dev(inp)
     lib = ssd()
