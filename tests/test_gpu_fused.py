@@ -177,3 +177,33 @@ def test_fused_rejects_unsupported_shapes():
         with pytest.raises(lib.SSDError, match="UNSUPPORTED"):
             lib.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"],
                         chunk_size=kw.get("chunk_size", 0), fused=True)
+
+
+def _random_fused_shapes(n=10, seed=2024):
+    """Seeded shapes inside the supported set, from one chunk to multi-round
+    grids (more workgroups than compute units, so chains continue across
+    rounds of workgroups)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        P = int(rng.choice([32, 64]))
+        N = int(rng.choice([32, 64, 128]))
+        if P == 32 and N == 32:
+            continue
+        G = int(rng.choice([1, 2, 4]))
+        H = G * int(rng.choice([1, 2, 4, 8, 16]))
+        B = int(rng.integers(1, 13))
+        L = int(rng.integers(1, 12 * 256))
+        out.append((B, L, H, P, N, G))
+    # multi-round at the headline layer shape: 384 and 768 workgroups
+    out += [(12, 2048, 64, 64, 128, 1), (24, 2048, 64, 64, 128, 1)]
+    return out
+
+
+@pytest.mark.parametrize("B,L,H,P,N,G", _random_fused_shapes())
+def test_fused_random_shapes(B, L, H, P, N, G):
+    cfg = BASE.with_(batch=B, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G, init_state=bool(L % 2))
+    inp = make_inputs(cfg, seed=B * 7 + L)
+    pairs = [(0, 0), (B - 1, H - 1), (B // 2, H // 2)]
+    pairs = list(dict.fromkeys(pairs))
+    sampled_check(inp, pairs, TOL["bf16"], f"fused random B={B} L={L} H={H} P={P} N={N} G={G}", fused=True)
