@@ -639,3 +639,46 @@ def test_conv1d_split_continues_across_calls_bitwise():
     torch.cuda.synchronize()
     for i in range(3):
         assert torch.equal(torch.cat([a[i], c[i]], dim=1), whole[i])
+
+
+# ---- HIP graph capture ----------------------------------------------------
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_forward_replays_from_a_captured_graph(fused):
+    """ssd_forward (and the one-pass entry point) enqueue kernels only, so a
+    call can be captured into a HIP graph with a preallocated workspace and
+    replayed. Every replay, with eager work and synchronisations in between,
+    gives the eager result bit for bit."""
+    cfg = CONFIGS[1].with_(batch=2, seqlen=1100, init_state=True)
+    inp = make_inputs(cfg, seed=41)
+    d = to_dev(inp)
+    lib = ssd()
+    desc = lib.make_desc(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, "bf16")
+    ws = torch.empty(lib.workspace_bytes(desc), dtype=torch.uint8, device=DEV)
+    y = torch.empty_like(d["x"])
+    hT = torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device=DEV)
+
+    def call():
+        lib.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], y=y, final_state=hT,
+                    workspace=ws, fused=fused)
+
+    note(f"[gpu] graph capture and replay (fused={fused})")
+    call()
+    torch.cuda.synchronize()
+    y_ref, h_ref = y.clone(), hT.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for r in range(3):
+        y.fill_(float("nan"))
+        hT.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref) and torch.equal(hT, h_ref), f"replay {r} differs from the eager result"
