@@ -161,7 +161,11 @@ SSD_API ssd_status_t ssd_forward(const ssd_desc_t* desc,
  * dstate 32); anything else returns SSD_ERR_UNSUPPORTED.
  * Results agree with ssd_forward to rounding: the chunk states stay in fp32
  * (ssd_forward rounds them to bf16 between its kernels), and the chunk-state
- * weights are applied to B instead of x before the bf16 rounding. */
+ * weights are applied to B instead of x before the bf16 rounding.
+ * Every wait of one chunk's workgroup for the state of the chunk before is
+ * bounded; a wait that is cut off sets a status bit in the workspace instead
+ * of hanging. With the environment variable SSD_DEBUG set, the call waits for
+ * the kernel and returns SSD_ERR_HIP if that bit is set. */
 SSD_API ssd_status_t ssd_forward_fused(const ssd_desc_t* desc,
                                const void* x, const float* dt, const float* A,
                                const void* B, const void* C, const float* D,

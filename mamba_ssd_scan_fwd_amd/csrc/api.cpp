@@ -281,6 +281,16 @@ ssd_status_t enqueue_forward(const Plan& p, bool fused, const void* x, const flo
                 sync, sync + p.batch * p.H, sync + p.batch * p.H + 1};
     e = launch_chunk_cumsum_clear(p, dt, A, cs, dtc, sync, ws.nsync, s);
     if (e == hipSuccess) e = launch_fused_forward(p, a, s);
+    if (e == hipSuccess && debug_enabled()) {
+      // check the status word: a hand-over wait that was cut off leaves bit 0 set
+      uint32_t status = 0;
+      e = hipMemcpyAsync(&status, a.status, sizeof(status), hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);
+      if (e == hipSuccess && status != 0) {
+        std::fprintf(stderr, "[ssd] one-pass kernel: a state hand-over wait was cut off (status %u)\n", status);
+        e = hipErrorUnknown;
+      }
+    }
   } else {
     e = run_cumsum_chunk_state(p, x, B, dt, A, cs, dtc, states, s);
     if (e == hipSuccess) e = launch_state_passing(p, states, cs, init_state, final_state, s);

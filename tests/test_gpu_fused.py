@@ -207,3 +207,29 @@ def test_fused_random_shapes(B, L, H, P, N, G):
     pairs = [(0, 0), (B - 1, H - 1), (B // 2, H // 2)]
     pairs = list(dict.fromkeys(pairs))
     sampled_check(inp, pairs, TOL["bf16"], f"fused random B={B} L={L} H={H} P={P} N={N} G={G}", fused=True)
+
+
+def test_fused_debug_mode_checks_the_status_word():
+    """With SSD_DEBUG set, the one-pass call waits for its kernel and checks
+    the hand-over status word (a separate process: the setting is read once
+    per process)."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import torch, mamba_ssd_scan_fwd_amd as m\n"
+        "from ssd_inputs import CONFIGS, make_inputs\n"
+        "cfg = CONFIGS[1].with_(batch=2, seqlen=700)\n"
+        "d = {k: (v.cuda() if v is not None else None) for k, v in make_inputs(cfg, seed=5).items()}\n"
+        "y, h = m.forward(d['x'], d['dt'], d['A'], d['B'], d['C'], d['D'], d['init_state'], fused=True)\n"
+        "torch.cuda.synchronize()\n"
+        "print('finite', bool(torch.isfinite(y.float()).all()))\n" % root)
+    note("[gpu] one-pass path with SSD_DEBUG=1 in a subprocess")
+    env = dict(os.environ, SSD_DEBUG="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "path=fused" in r.stderr and "cut off" not in r.stderr, r.stderr[-2000:]
+    assert "finite True" in r.stdout
