@@ -119,7 +119,9 @@ SSD_API ssd_status_t ssd_effective_chunk_size(const ssd_desc_t* desc, int32_t* c
 /* Bytes of device workspace ssd_forward needs for `desc`: dA_cumsum,
  * dt_chunked and states, each starting on a 256-byte boundary, in that order.
  * Where the one-pass kernel supports the shape (see ssd_forward_fused), the
- * states region is at least the size of its state hand-over area. Pure host
+ * states region is at least the size of its state hand-over area. For a few
+ * long sequences (at least 64 chunks, few (batch, head) chains) a scratch
+ * area for the segmented state passing follows the states. Pure host
  * computation; no HIP call. */
 SSD_API ssd_status_t ssd_workspace_bytes(const ssd_desc_t* desc, size_t* bytes);
 
@@ -204,7 +206,11 @@ SSD_API ssd_status_t ssd_cumsum_chunk_state(const ssd_desc_t* desc, const void* 
  * recombined). In place over `states`: on return states[b,h,c] holds the
  * state entering chunk c,  H_{-1} = init_state (or 0),
  * Hin_c = H_{c-1},  H_c = exp(Lam_c) H_{c-1} + S_c. Writes final_state
- * (= H_{nc-1}) in fp32 when non-NULL; final_state may equal init_state. */
+ * (= H_{nc-1}) in fp32 when non-NULL; final_state may equal init_state.
+ * This entry point runs the chain chunk by chunk. For a few long sequences,
+ * ssd_forward instead cuts each chain into segments of 32 chunks that run in
+ * parallel (it has a workspace for their partial states). Its results then
+ * differ from this step's only in the fp32 rounding order. */
 SSD_API ssd_status_t ssd_state_passing(const ssd_desc_t* desc, void* states, const float* dA_cumsum,
                                const float* init_state, float* final_state, void* stream);
 

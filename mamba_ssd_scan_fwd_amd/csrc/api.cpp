@@ -108,6 +108,7 @@ ssd_status_t make_plan(const ssd_desc_t* d, Plan* p) {
 
 struct WsLayout {
   size_t cs_off, dt_off, st_off, tab_off, seq_off, total;
+  size_t sp_off;  // segmented state passing scratch (0 if not used)
   // one-pass path, inside the states region: the state hand-over ring, then
   // the per-head counters, the ticket and the status word (32-bit each)
   size_t ring_off, sync_off;
@@ -136,6 +137,11 @@ WsLayout ws_layout(const Plan& p, bool with_table = false) {
   w.ring_off += w.st_off;
   w.sync_off += w.st_off;
   w.tab_off = align_up(w.st_off + st_bytes, kWsAlign);
+  w.sp_off = 0;
+  if (!with_table && seg_state_passing_applies(p)) {
+    w.sp_off = w.tab_off;
+    w.tab_off = align_up(w.sp_off + seg_scratch_layout(p, nullptr).bytes, kWsAlign);
+  }
   w.seq_off = align_up(w.tab_off + size_t(p.nc) * sizeof(ChunkInfo), kWsAlign);
   w.total = with_table ? align_up(w.seq_off + size_t(p.nseq) * sizeof(int2), kWsAlign) : w.tab_off;
   return w;
@@ -293,7 +299,12 @@ ssd_status_t enqueue_forward(const Plan& p, bool fused, const void* x, const flo
     }
   } else {
     e = run_cumsum_chunk_state(p, x, B, dt, A, cs, dtc, states, s);
-    if (e == hipSuccess) e = launch_state_passing(p, states, cs, init_state, final_state, s);
+    if (e == hipSuccess) {
+      if (ws.sp_off != 0)
+        e = launch_state_passing_seg(p, states, cs, init_state, final_state, w + ws.sp_off, s);
+      else
+        e = launch_state_passing(p, states, cs, init_state, final_state, s);
+    }
     if (e == hipSuccess) e = run_chunk_scan(p, x, B, C, D, cs, dtc, states, y, s);
   }
   if (owned) {

@@ -49,6 +49,21 @@ hipError_t launch_chunk_state(const Plan& p, const void* x, const void* B,
                               hipStream_t s);
 hipError_t launch_state_passing(const Plan& p, void* states, const float* dA_cs,
                                 const float* h0, float* hT, hipStream_t s);
+// State passing for a few long chains: segments of one chain in parallel,
+// with scratch from the workspace (seg_scratch_layout(p, nullptr).bytes).
+struct SegScratch {
+  float* agg;
+  float* agg_lam;
+  uint32_t* flags;  // then the ticket and the status word
+  uint32_t* ticket;
+  uint32_t* status;
+  int64_t nwords;   // flags + ticket + status
+  size_t bytes;
+};
+bool seg_state_passing_applies(const Plan& p);
+SegScratch seg_scratch_layout(const Plan& p, void* base);
+hipError_t launch_state_passing_seg(const Plan& p, void* states, const float* dA_cs, const float* h0, float* hT,
+                                    void* scratch, hipStream_t s);
 hipError_t launch_chunk_scan(const Plan& p, const void* x, const void* B, const void* C,
                              const float* D, const float* dA_cs, const float* dtc,
                              const void* states, void* y, hipStream_t s);

@@ -682,3 +682,38 @@ def test_forward_replays_from_a_captured_graph(fused):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref) and torch.equal(hT, h_ref), f"replay {r} differs from the eager result"
+
+
+# ---- state passing cut into segments (a few long sequences) ---------------
+
+@pytest.mark.parametrize("L,H,P,N,io,init", [(64 * 256 + 77, 4, 64, 128, "bf16", True),
+                                             (96 * 256 + 3, 2, 32, 64, "bf16", False),
+                                             (79 * 256 - 40, 2, 16, 16, "fp32", True)])
+def test_long_sequence_segmented_state_passing(L, H, P, N, io, init):
+    """Few chains of many chunks: ssd_forward cuts each chain into segments
+    of 32 chunks that run in parallel. Checked in full against the oracle,
+    with a ragged last segment."""
+    cfg = BASE.with_(batch=1, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=1, io_dtype=io, init_state=init)
+    inp = make_inputs(cfg, seed=L + H)
+    full_check(inp, TOL[io], f"segmented state passing L={L} H={H} P={P} N={N} {io}")
+
+
+def test_segmented_state_passing_in_place_and_against_the_plain_chain():
+    """The segmented state passing of ssd_forward with the final state written
+    over the initial state, against the plain chain of the step entry point:
+    the same entering states and final state up to fp32 rounding order."""
+    L, H = 70 * 256 + 11, 4
+    cfg = BASE.with_(batch=1, seqlen=L, nheads=H, init_state=True)
+    inp = make_inputs(cfg, seed=43)
+    d = to_dev(inp)
+    lib = ssd()
+    note(f"[gpu] segmented state passing in place, L={L}")
+    state = d["init_state"].clone()
+    y, hT = lib.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], state, final_state=state)
+    cs, dtc, st = lib.cumsum_chunk_state(d["x"], d["B"], d["dt"], d["A"])
+    st, h2 = lib.state_passing(st, cs, d["init_state"], seqlen=L)
+    y2 = lib.chunk_scan(d["x"], d["B"], d["C"], d["D"], cs, dtc, st)
+    torch.cuda.synchronize()
+    assert hT.data_ptr() == state.data_ptr()
+    check_rel(np64(state), np64(h2), 1e-5, "final state: segmented vs plain chain")
+    check_rel(np64(y), np64(y2), 1e-2, "y: segmented vs plain chain (entering states rounded to bf16)")
