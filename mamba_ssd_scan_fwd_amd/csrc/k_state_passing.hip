@@ -317,9 +317,12 @@ hipError_t launch_seg_typed(const Plan& p, void* states, const float* dA_cs, con
 
 // Host-only: the segmented kernel serves batched layouts whose chains are too
 // few to fill the GPU with the plain kernel (under 512 of its workgroups) and
-// long enough to cut (at least two segments).
+// long enough to cut (at least two segments). Each segment folds in every
+// earlier segment's aggregate, so the aggregate reads grow with the square of
+// the segment count: at most 32 segments (1024 chunks) take this path.
+constexpr int64_t kMaxSegs = 32;
 bool seg_state_passing_applies(const Plan& p) {
-  if (p.seqtab != nullptr || p.nc < 2 * kSegChunks) return false;
+  if (p.seqtab != nullptr || p.nc < 2 * kSegChunks || p.nc > kMaxSegs * kSegChunks) return false;
   const int64_t PN = p.P * p.N;
   const int64_t nslice = (PN + kThreads * kVec - 1) / (kThreads * kVec);
   return p.batch * p.H * nslice < 512;
