@@ -120,7 +120,7 @@ SSD_API ssd_status_t ssd_effective_chunk_size(const ssd_desc_t* desc, int32_t* c
  * dt_chunked and states, each starting on a 256-byte boundary, in that order.
  * Where the one-pass kernel supports the shape (see ssd_forward_fused), the
  * states region is at least the size of its state hand-over area. For a few
- * long sequences (at least 64 chunks, few (batch, head) chains) a scratch
+ * long sequences (64 to 1024 chunks, few (batch, head) chains) a scratch
  * area for the segmented state passing follows the states. Pure host
  * computation; no HIP call. */
 SSD_API ssd_status_t ssd_workspace_bytes(const ssd_desc_t* desc, size_t* bytes);
@@ -282,7 +282,7 @@ SSD_API ssd_status_t ssd_conv1d_split(const ssd_desc_t* desc, int32_t conv_width
  * recurrent mode, O(1) state per token). desc->seqlen must be 1 (chunk_size
  * is ignored); shapes are those of ssd_forward with L = 1:
  *     x, y     [batch, H, P]      io dtype
- *     dt       [batch, H]         fp32, used as given
+ *     dt       [batch, H]         fp32 (the descriptor's dt preprocessing applies)
  *     A, D     [H]                fp32 (D nullable: no skip term)
  *     B, C     [batch, G, N]      io dtype
  *     state    [batch, H, P, N]   fp32, read and overwritten in place:
