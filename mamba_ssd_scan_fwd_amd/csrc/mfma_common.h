@@ -136,12 +136,17 @@ __device__ __forceinline__ v4i32_t buffer_words(const void* base, uint32_t bytes
 // The load takes its LDS address from m0, which the compiler reserves but
 // does not otherwise use in these kernels (no other LDS-DMA, interpolation or
 // indexed-register instructions), so nothing it holds there is lost.
+// (The clobber of m0 is the point: the compiler is told the register changes.
+// It warns that m0 is reserved; that warning is expected here.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const v4i32_t& r, uint32_t lds_dst, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(__builtin_amdgcn_readfirstlane(lds_dst)), "v"(voff), "s"(__builtin_bit_cast(__int128, r))
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
