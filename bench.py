@@ -27,6 +27,7 @@ import hashlib
 import json
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -289,28 +290,34 @@ def one_pass_measure(cfg, steps, dev, bufs=None):
         d, y, hT, ws = bufs
     stream = torch.cuda.current_stream(dev)
 
+    def run(**kw):
+        ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], y=y, final_state=hT,
+                    workspace=ws, **kw)
+
     def timed(**kw):
-        def run():
-            ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], y=y, final_state=hT,
-                        workspace=ws, **kw)
-        for _ in range(5):
-            run()
-        torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for _ in range(steps):
-            run()
+            run(**kw)
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps * 1e3
 
-    split_us = timed(fused=False) if os.environ.get("SSD_FORWARD_PATH") is None else None
+    paths = {"split": dict(split=True), "fused": dict(fused=True), "auto": {}}
     try:
-        fused_us = timed(fused=True)
+        for kw in paths.values():
+            for _ in range(5):
+                run(**kw)
     except ssd.SSDError:
         return {"workload": cfg.name, "supported": False}
-    # which path ssd_forward takes here: the one its own time matches
-    auto_us = timed()
+    torch.cuda.synchronize()
+    # the three paths in turn, three times: the medians (a path timed only
+    # first or only last would carry any drift of the clocks)
+    times = {k: [] for k in paths}
+    for _ in range(3):
+        for k, kw in paths.items():
+            times[k].append(timed(**kw))
+    split_us, fused_us, auto_us = (statistics.median(times[k]) for k in ("split", "fused", "auto"))
     T = cfg.tokens
     Q = ssd.effective_chunk_size(desc)
     nc = -(-cfg.seqlen // Q)
@@ -321,9 +328,9 @@ def one_pass_measure(cfg, steps, dev, bufs=None):
     out = {"workload": f"{cfg.name}: B {cfg.batch}, L {cfg.seqlen}, H {H}, P {P}, N {N}, G {G}",
            "supported": True, "one_pass_us": round(fused_us, 2), "one_pass_tokens_per_s": round(T / (fused_us * 1e-6), 1),
            "one_pass_algo_bytes": nbytes}
-    if split_us is not None:
-        out.update({"split_us": round(split_us, 2), "split_tokens_per_s": round(T / (split_us * 1e-6), 1),
-                    "ssd_forward_takes": "one-pass" if abs(auto_us - fused_us) < abs(auto_us - split_us) else "split"})
+    # which path ssd_forward takes here: the one its own time matches
+    out.update({"split_us": round(split_us, 2), "split_tokens_per_s": round(T / (split_us * 1e-6), 1),
+                "ssd_forward_takes": "one-pass" if abs(auto_us - fused_us) < abs(auto_us - split_us) else "split"})
     return out
 
 

@@ -137,9 +137,11 @@ SSD_API ssd_status_t ssd_workspace_bytes(const ssd_desc_t* desc, size_t* bytes);
  *               least ssd_workspace_bytes() bytes, 256-byte aligned, not
  *               overlapping any other argument.
  *   y must not overlap any input.
- * Runs the five steps below on `stream`, in order, or, where the one-pass
- * kernel of ssd_forward_fused supports the shape and is the faster choice for
- * it, that path. */
+ * Runs the five steps below on `stream`, in order (the path of
+ * ssd_forward_split), or, where the one-pass kernel of ssd_forward_fused
+ * supports the shape and is the faster choice for it, that path. The
+ * environment variable SSD_FORWARD_PATH=split or =fused, read once per
+ * process, overrides the choice (fused only where it is supported). */
 SSD_API ssd_status_t ssd_forward(const ssd_desc_t* desc,
                          const void* x, const float* dt, const float* A,
                          const void* B, const void* C, const float* D,
@@ -169,6 +171,21 @@ SSD_API ssd_status_t ssd_forward(const ssd_desc_t* desc,
  * of hanging. With the environment variable SSD_DEBUG set, the call waits for
  * the kernel and returns SSD_ERR_HIP if that bit is set. */
 SSD_API ssd_status_t ssd_forward_fused(const ssd_desc_t* desc,
+                               const void* x, const float* dt, const float* A,
+                               const void* B, const void* C, const float* D,
+                               const float* init_state,
+                               void* y, float* final_state,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* The same forward pass, always on the split path: the five steps below as
+ * separate launches on `stream` (fused where a step's kernels allow it: the
+ * cumsum with the chunk states), the chunk states going through the
+ * workspace between them. This is what ssd_forward runs wherever it does
+ * not take the one-pass kernel, so on those shapes the two give identical
+ * bits. Arguments, ownership, workspace size and errors as for
+ * ssd_forward. */
+SSD_API ssd_status_t ssd_forward_split(const ssd_desc_t* desc,
                                const void* x, const float* dt, const float* A,
                                const void* B, const void* C, const float* D,
                                const float* init_state,

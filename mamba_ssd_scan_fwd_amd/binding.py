@@ -43,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "ssd_workspace_bytes",
     "ssd_forward",
     "ssd_forward_fused",
+    "ssd_forward_split",
     "ssd_chunk_cumsum",
     "ssd_chunk_state",
     "ssd_cumsum_chunk_state",
@@ -117,6 +118,8 @@ def load_library():
         lib.ssd_forward.restype = ctypes.c_int
         lib.ssd_forward_fused.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.ssd_forward_fused.restype = ctypes.c_int
+        lib.ssd_forward_split.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.ssd_forward_split.restype = ctypes.c_int
         lib.ssd_chunk_cumsum.argtypes = [dp, vp, vp, vp, vp, vp]
         lib.ssd_chunk_cumsum.restype = ctypes.c_int
         lib.ssd_chunk_state.argtypes = [dp, vp, vp, vp, vp, vp, vp]
@@ -230,7 +233,8 @@ def _dt_kw(dt_pre, H, dev):
 
 def forward(x, dt, A, B, C, D=None, init_state=None, *, chunk_size: int = 0,
             return_final_state: bool = True, y=None, final_state=None, workspace=None,
-            library_workspace: bool = False, dt_pre=None, fused: bool = False, stream=None):
+            library_workspace: bool = False, dt_pre=None, fused: bool = False, split: bool = False,
+            stream=None):
     """SSD forward pass on the GPU. Returns (y, final_state or None).
 
     x [b, L, H, P] and B, C [b, L, G, N] in fp32 or bf16 (all the same);
@@ -240,8 +244,12 @@ def forward(x, dt, A, B, C, D=None, init_state=None, *, chunk_size: int = 0,
     allocates its workspace itself, in stream order. ``dt_pre`` asks for the
     dt preprocessing: dict(bias=[H] fp32 tensor, softplus=True, limit=(lo, hi)).
     ``fused=True`` calls ssd_forward_fused (the one-pass kernel; raises where
-    the shape is not supported by it) instead of ssd_forward.
+    the shape is not supported by it) and ``split=True`` ssd_forward_split
+    (always the separate steps) instead of ssd_forward, which picks one of
+    the two paths by shape.
     """
+    if fused and split:
+        raise ValueError("fused and split exclude each other")
     dev = x.device
     _need(x, "x", device=dev)
     io = x.dtype
@@ -274,7 +282,7 @@ def forward(x, dt, A, B, C, D=None, init_state=None, *, chunk_size: int = 0,
         wsize = workspace.numel() * workspace.element_size()
         if wsize < nws:
             raise ValueError(f"workspace needs {nws} bytes")
-    name = "ssd_forward_fused" if fused else "ssd_forward"
+    name = "ssd_forward_fused" if fused else "ssd_forward_split" if split else "ssd_forward"
     st = getattr(load_library(), name)(
         ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state),
         _ptr(y), _ptr(final_state), _ptr(workspace), ctypes.c_size_t(wsize), _stream(stream, dev))

@@ -367,6 +367,20 @@ ssd_status_t ssd_forward(const ssd_desc_t* desc, const void* x, const float* dt,
                               static_cast<hipStream_t>(stream));
 }
 
+ssd_status_t ssd_forward_split(const ssd_desc_t* desc, const void* x, const float* dt, const float* A,
+                               const void* B, const void* C, const float* D, const float* init_state,
+                               void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  Plan p;
+  ssd_status_t st = ssd::make_plan(desc, &p);
+  if (st != SSD_OK) return st;
+  const ssd::WsLayout ws = ssd::ws_layout(p);
+  st = ssd::check_forward(p, x, dt, A, B, C, D, init_state, y, final_state, workspace, workspace_bytes, ws);
+  if (st != SSD_OK) return st;
+  return ssd::enqueue_forward(p, false, x, dt, A, B, C, D, init_state, y, final_state, workspace, ws,
+                              static_cast<hipStream_t>(stream));
+}
+
 ssd_status_t ssd_forward_fused(const ssd_desc_t* desc, const void* x, const float* dt, const float* A,
                                const void* B, const void* C, const float* D, const float* init_state,
                                void* y, float* final_state, void* workspace, size_t workspace_bytes,

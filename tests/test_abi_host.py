@@ -309,6 +309,24 @@ def test_fused_entry_validates_like_forward():
     assert call_fwd(d, p, entry="ssd_forward_fused") == ALIAS
 
 
+@pytest.mark.parametrize("entry", ["ssd_forward", "ssd_forward_split"])
+def test_split_entry_validates_like_forward(entry):
+    d = desc()
+    p, s = fwd_args(d, x=None)
+    assert call_fwd(d, p, entry=entry) == NULLP
+    p, s = fwd_args(d)
+    p["B"] += 8
+    assert call_fwd(d, p, entry=entry) == ALIGN
+    p, s = fwd_args(d)
+    assert call_fwd(d, p, ws_bytes=ssd.workspace_bytes(d) - 256, entry=entry) == WS
+    p, s = fwd_args(d)
+    p["y"] = p["B"] + s["B"] - 1024
+    assert call_fwd(d, p, entry=entry) == ALIAS
+    bad = desc(headdim=0)
+    p, s = fwd_args(desc())
+    assert call_fwd(bad, p, ws_bytes=1 << 40, entry=entry) == SHAPE
+
+
 @pytest.mark.parametrize("L", [1, 256, 700, 2048])
 def test_workspace_covers_the_one_pass_hand_over_area(L):
     """Where the one-pass kernel applies, the states region holds its fp32

@@ -115,6 +115,24 @@ def test_workloads_full_size(idx):
     sampled_check(inp, pairs_for(cfg, 3), TOL[cfg.io_dtype], f"{cfg.name} full size")
 
 
+@pytest.mark.parametrize("idx,batch", [(4, None), (1, 32)])
+def test_split_entry_full_size_where_forward_takes_one_pass(idx, batch):
+    """ssd_forward takes the one-pass kernel on these shapes (several rounds
+    of workgroups); ssd_forward_split runs the separate steps on them."""
+    cfg = CONFIGS[idx] if batch is None else CONFIGS[idx].with_(name=f"{CONFIGS[idx].name} batch {batch}", batch=batch)
+    inp = make_inputs(cfg, seed=40 + idx)
+    sampled_check(inp, pairs_for(cfg, 3), TOL[cfg.io_dtype], f"{cfg.name} split entry", split=True)
+
+
+def test_split_entry_is_what_forward_runs_on_the_headline():
+    cfg = CONFIGS[1]
+    inp = make_inputs(cfg, seed=41)
+    note("[gpu] split entry vs ssd_forward, headline")
+    ys, hs = run(inp, split=True)
+    ya, ha = run(inp)
+    assert torch.equal(ys, ya) and torch.equal(hs, ha)
+
+
 # --------------------------------------------------------------------------
 # edge shapes, every P / N / group layout / chunk length, both dtypes
 # --------------------------------------------------------------------------
