@@ -20,10 +20,12 @@
 //    HB heads. The LDS is then reused as a double buffer for the scaled x of
 //    successive heads.
 //  * x has to be scaled by w_j before it is rounded to bf16, so it passes
-//    through registers: the x rows (and l, dt) of head hh+2 are loaded into
-//    one of two register sets while head hh's products run; head hh+1's set
-//    is scaled, rounded and written transposed (8x8 blocks) into the other
-//    LDS buffer, fragment-major; one barrier per head. The slot permutation
+//    through registers: the x rows (and l, dt) of head hh+1 are loaded into
+//    registers while head hh's products run, then scaled, rounded and
+//    written transposed (8x8 blocks) into the other LDS buffer,
+//    fragment-major; one barrier per head. (Loading two heads ahead left the
+//    last two heads' arithmetic with nothing in flight; one ahead is
+//    slightly faster and frees a register set.) The slot permutation
 //    inside each fragment block keeps both the staging writes and the
 //    operand reads free of bank conflicts.
 //  * Output tiles hold four consecutive n per lane: 8-byte stores into
@@ -127,8 +129,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   const int wn = wave % C::WN, wp = wave / C::WN;
 
   // ---- x of one head: raw rows into registers; scaled, transposed into LDS.
-  // Two register sets: the loads of head hh+2 are issued while head hh's
-  // products run, so about two heads of loads are in flight per workgroup. ----
+  // The loads of head hh+1 are issued when head hh starts, so one head of
+  // loads is in flight per workgroup while its products run. ----
   struct XSet {
     uint4 xr[C::XPT][8];
     float4 lr[C::XPT][2], dr[C::XPT][2];
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   };
 
   // ---- prologue. All its global loads are issued first, in the order they
-  // are consumed (dt, then B, then the x of the first two heads), so that each
+  // are consumed (dt, then B, then the x of the first head), so that each
   // wait covers one group only and the three latencies overlap. ----
   const int hlast = h0 + HB - 1;
   // B tile of the chunk straight into the LDS (rows past the end fall
@@ -227,9 +229,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 #pragma unroll
     for (int hh = 0; hh < kMaxHB; ++hh) dtv[hh] = drow[min(h0 + hh, hlast)];
   }
-  XSet sa, sb;
+  XSet sa;
   fetch_x(sa, h0);
-  fetch_x(sb, min(h0 + 1, hlast));
 
   if constexpr (FUSED) {
     // ---- step 1 for this chunk and these heads: dt tile, then one
@@ -286,14 +287,14 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 
   stage_x(sa, lds, 0);
   __syncthreads();
-  // head hh: its inputs are in LDS buffer hh & 1 (staged from `mine`, which
-  // is refilled with head hh+2); `next` holds head hh+1, staged at the end.
-  // The loads are always issued (the last heads re-read the final one), so
-  // every head has the same memory-operation sequence.
-  auto head = [&](XSet& mine, XSet& next, int hh) {
+  // head hh: its inputs are in LDS buffer hh & 1; `mine` is refilled with
+  // head hh+1 at the start and staged into the other buffer at the end. The
+  // loads are always issued (the last head re-reads itself), so every head
+  // has the same memory-operation sequence.
+  auto head = [&](XSet& mine, int hh) {
     const int h = h0 + hh;
     uint4* cur = lds + (hh & 1) * C::X_FRAGS;
-    fetch_x(mine, min(h + 2, hlast));
+    fetch_x(mine, min(h + 1, hlast));
 
     f32x4_t acc[C::TN][C::TP];
 #pragma unroll
@@ -347,12 +348,12 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         }
       }
     }
-    if (hh + 1 < HB) stage_x(next, lds + ((hh + 1) & 1) * C::X_FRAGS, hh + 1);  // the other buffer
+    if (hh + 1 < HB) stage_x(mine, lds + ((hh + 1) & 1) * C::X_FRAGS, hh + 1);  // the other buffer
     __syncthreads();
   };
   for (int hh = 0; hh < HB; hh += 2) {
-    head(sa, sb, hh);
-    if (hh + 1 < HB) head(sb, sa, hh + 1);
+    head(sa, hh);
+    if (hh + 1 < HB) head(sa, hh + 1);
   }
 }
 
