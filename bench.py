@@ -18,6 +18,16 @@ Before the W warm-up steps the GPU runs forward passes for --device-warm-ms
 (untimed): from idle, its clocks take a few hundred milliseconds of load to
 reach their steady state, and a timed region that starts earlier measures
 the ramp (about 10% slower on the headline workload).
+
+Timing protocol. Inputs are resident in HBM and the workspace is allocated
+before the timed region. Each of the K timed steps is preceded, outside its
+own pair of HIP events, by a write of --flush-mib MiB of scratch memory
+(default 1024), which evicts the 256 MB last-level cache (MALL) and the L2s,
+so every step reads its inputs from HBM. The headline is the median of those
+flushed per-step times; the back-to-back (warm) rate over the same K steps
+is reported beside it. The per-kernel times behind `roofline` are taken the
+same way (a flush before each pass, events between the kernels of the pass).
+The other workloads are measured with the same protocol in `workloads`.
 """
 
 from __future__ import annotations
@@ -58,6 +68,12 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain fp32 elementwise copy (negation) of MIB MiB, "
                          "the reference kernel for scaling rocprofv3 byte counters")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="scratch written before every timed step (0: no flush, back-to-back steps only)")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the other workloads' entries")
+    ap.add_argument("--workload-steps", type=int, default=20)
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes for the CPU baseline (0: one per host core, at most 16)")
     return ap.parse_args()
 
 
@@ -86,7 +102,65 @@ def algorithmic_model(cfg, Q, io_bytes):
         "chunk_scan": dict(bytes=2 * T * H * P * s + 2 * T * G * N * s + 2 * cs + st,
                            flops=T * H * (Q + 1) * P + T * G * (Q + 1) * N + 2 * T * H * P * N + 3 * T * H * P),
     }
+    # one-pass kernel (steps 2-5 after the cumsum): x in, y out, B and C,
+    # dA_cumsum and dt_chunked once, every hand-over state written and read
+    # once in fp32, the initial and final states
+    hand = 2 * b * H * (nc - 1) * P * N * 4
+    out["one_pass"] = dict(bytes=2 * T * H * P * s + 2 * T * G * N * s + 2 * cs + hand
+                           + b * H * P * N * 4 * (2 if cfg.init_state else 1),
+                           flops=out["chunk_state"]["flops"] + out["state_passing"]["flops"]
+                           + out["chunk_scan"]["flops"])
     return out
+
+
+def forward_kernels(cfg, path):
+    """The kernels one ssd_forward launches on `path`, by name in the model."""
+    if path == "one-pass":
+        return ["chunk_cumsum", "one_pass"]
+    if cfg.io_dtype != "bf16":
+        return ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
+    return ["cumsum_chunk_state", "state_passing", "chunk_scan"]
+
+
+class Flusher:
+    """Writes `mib` MiB of scratch memory on the current stream: more than the
+    256 MB last-level cache and the L2s hold, so the next kernel reads HBM."""
+
+    def __init__(self, dev, mib):
+        import torch
+        self.buf = torch.empty(mib << 18, dtype=torch.float32, device=dev) if mib > 0 else None
+        self.k = 0
+
+    def __call__(self):
+        if self.buf is not None:
+            self.k += 1
+            self.buf.fill_(float(self.k & 1023))
+
+
+def timed_steps(fn, steps, stream, flush=None):
+    """Per-step times (us) of `steps` calls of fn, each between its own pair of
+    HIP events on `stream`, each preceded by flush() outside the pair.
+    Returns (sorted times, wall seconds between the two synchronisations)."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs = []
+    for _ in range(steps):
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return sorted(a.elapsed_time(b) * 1e3 for a, b in evs), wall
+
+
+def quantile(xs, q):
+    i = min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))
+    return xs[i]
 
 
 def kernel_source_digest(files):
@@ -116,51 +190,88 @@ def traffic_from_profile(kernel, cfg_name, per_launch_algo):
         return None
 
 
-def cpu_baseline(cfg, inp, nseq, min_seconds=10.0, max_reps=4):
-    """The fp64 oracle as it stands, on `nseq` whole sequences (all heads),
-    repeated until about `min_seconds` of CPU work have been timed."""
-    import numpy as np
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _oracle_task(args):
+    """Worker task of the CPU baseline: the fp64 oracle recurrence on one
+    block of chains, one thread; returns its CPU seconds."""
+    import numpy as np  # noqa: F401
+    import contextlib
     try:
         from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
-        threadpool_limits = None
+        limit = contextlib.nullcontext()
     from oracle import ssd_recurrent
+    with limit:
+        t0 = time.perf_counter()
+        ssd_recurrent(*args)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(cfg, inp, nseq, workers):
+    """The fp64 oracle as it stands on `nseq` whole sequences (all heads) of
+    the workload: once in `workers` processes (one per core, tasks of one
+    sequence and a block of heads), and once on one sequence in this process
+    with one thread."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    import numpy as np
 
     def f64(t):
         return None if t is None else t.detach().cpu().float().numpy().astype(np.float64)
 
-    sl = slice(0, nseq)
-    args = [f64(inp["x"][sl]), f64(inp["dt"][sl]), f64(inp["A"]), f64(inp["B"][sl]), f64(inp["C"][sl]),
-            f64(inp["D"]), f64(inp["init_state"][sl]) if inp["init_state"] is not None else None]
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    reps, total = 0, 0.0
-    try:
-        while reps < max_reps and (reps == 0 or total < min_seconds):
-            t0 = time.perf_counter()
-            ssd_recurrent(*args)
-            total += time.perf_counter() - t0
-            reps += 1
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
+    H, G = cfg.nheads, cfg.ngroups
+    hpg = H // G
+    hb = 8 if hpg % 8 == 0 else hpg
+    tasks = []
+    for b in range(nseq):
+        for h0 in range(0, H, hb):
+            h1 = min(h0 + hb, H)
+            g0, g1 = h0 // hpg, (h1 - 1) // hpg + 1
+            sl = (slice(b, b + 1), slice(None), slice(h0, h1))
+            tasks.append((f64(inp["x"][sl]), f64(inp["dt"][sl]), f64(inp["A"][h0:h1]),
+                          f64(inp["B"][b:b + 1, :, g0:g1]), f64(inp["C"][b:b + 1, :, g0:g1]),
+                          f64(inp["D"][h0:h1]),
+                          None if inp["init_state"] is None else f64(inp["init_state"][b:b + 1, h0:h1])))
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        list(ex.map(_oracle_task, tasks[:workers]))  # start the workers and import numpy first
+        t0 = time.perf_counter()
+        cpu_s = sum(ex.map(_oracle_task, tasks))
+        wall = time.perf_counter() - t0
+    # one thread, this process: the first sequence
+    single_s = sum(_oracle_task(t) for t in tasks[:H // hb + (H % hb > 0)])
     tokens = nseq * cfg.seqlen
     return {
-        "value": tokens * reps / total,
+        "value": round(tokens / wall, 1),
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{nseq} of {cfg.batch} sequences x {cfg.seqlen} tokens, all {cfg.nheads} heads, "
-                  f"{reps} pass(es) ({tokens * reps} tokens in {total:.1f} s; fp64 NumPy sequential "
-                  f"recurrence, one thread, {platform.processor() or platform.machine()})",
+        "sample": f"{nseq} of {cfg.batch} sequences x {cfg.seqlen} tokens, all {H} heads ({len(tasks)} tasks "
+                  f"of one sequence and {hb} heads), fp64 NumPy sequential recurrence in {workers} worker "
+                  f"processes of one thread: {tokens} tokens in {wall:.1f} s wall, {cpu_s:.1f} s of CPU time",
+        "host_cpu_count": os.cpu_count(),
+        "cpu_model": cpu_model(),
+        "single_thread_tokens_per_s": round(cfg.seqlen / single_s, 1),
     }
 
 
-def decode_measure(cfg, batch, steps, dev):
+def decode_measure(cfg, batch, steps, dev, flush):
     """The recurrent (decode) step on the layer shape of `cfg` for `batch`
-    sequences: average time per step (HIP events on the launch stream) and
-    algorithmic bytes (fp32 state read and written once, plus x, y, dt, B, C)."""
+    sequences: median time per step (flushed; HIP events on the launch stream)
+    and algorithmic bytes (fp32 state read and written once, plus x, y, dt,
+    B, C)."""
     import torch
 
     import mamba_ssd_scan_fwd_amd as ssd
@@ -172,28 +283,27 @@ def decode_measure(cfg, batch, steps, dev):
     state = d["init_state"]
     y = torch.empty_like(x)
     stream = torch.cuda.current_stream(dev)
+
+    def run():
+        ssd.decode_step(x, dt, d["A"], Bm, Cm, d["D"], state, y=y)
+
     for _ in range(3):
-        ssd.decode_step(x, dt, d["A"], Bm, Cm, d["D"], state, y=y)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        ssd.decode_step(x, dt, d["A"], Bm, Cm, d["D"], state, y=y)
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) / steps * 1e3
+        run()
+    ts, _ = timed_steps(run, steps, stream, flush)
+    us = statistics.median(ts)
     s = 2 if cfg.io_dtype == "bf16" else 4
     H, P, N, G = cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
     nbytes = batch * (2 * 4 * H * P * N + 2 * H * P * s + 2 * G * N * s + 4 * H)
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"workload": f"decode step, {batch} sequences x {cfg.name} layer (H {H}, P {P}, N {N}, G {G})",
-            "batch": batch, "avg_us": round(us, 2), "tokens_per_s": round(batch / (us * 1e-6), 1),
+            "batch": batch, "median_us": round(us, 2), "tokens_per_s": round(batch / (us * 1e-6), 1),
             "algo_bytes": nbytes, "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def varlen_measure(cfg, steps, dev):
+def varlen_measure(cfg, steps, dev, flush):
     """The workload's tokens as packed sequences of mixed lengths (seeded;
-    same total as batch x seqlen): time per forward pass and tokens/s."""
+    same total as batch x seqlen): median time per forward pass (flushed) and
+    tokens/s."""
     import numpy as np
     import torch
 
@@ -218,23 +328,17 @@ def varlen_measure(cfg, steps, dev):
 
     for _ in range(3):
         run()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        run()
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) / steps * 1e3
+    ts, _ = timed_steps(run, steps, stream, flush)
+    us = statistics.median(ts)
     return {"workload": f"{S} packed sequences, {T} tokens in all (lengths {int(lengths.min())}..{int(lengths.max())}), "
-                        f"{cfg.name} layer", "num_seqs": S, "avg_us": round(us, 2),
+                        f"{cfg.name} layer", "num_seqs": S, "median_us": round(us, 2),
             "tokens_per_s": round(T / (us * 1e-6), 1)}
 
 
-def conv_measure(cfg, steps, dev):
+def conv_measure(cfg, steps, dev, flush):
     """The short causal convolution (width 4, SiLU) on the workload's packed
-    [x | B | C] channels, split into x, B, C: time per call and algorithmic
-    GB/s (every input and output once)."""
+    [x | B | C] channels, split into x, B, C: median time per call (flushed)
+    and algorithmic GB/s (every input and output once)."""
     import torch
 
     import mamba_ssd_scan_fwd_amd as ssd
@@ -247,91 +351,210 @@ def conv_measure(cfg, steps, dev):
     bias = torch.randn(CH, generator=g).to(dev)
     kw = dict(nheads=cfg.nheads, headdim=cfg.headdim, ngroups=cfg.ngroups, dstate=cfg.dstate, silu=True)
     stream = torch.cuda.current_stream(dev)
+
+    def run():
+        ssd.conv1d_split(u, w, bias, **kw)
+
     for _ in range(3):
-        ssd.conv1d_split(u, w, bias, **kw)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        ssd.conv1d_split(u, w, bias, **kw)
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) / steps * 1e3
+        run()
+    ts, _ = timed_steps(run, steps, stream, flush)
+    us = statistics.median(ts)
     nbytes = 2 * cfg.batch * cfg.seqlen * CH * (2 if cfg.io_dtype == "bf16" else 4)
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"workload": f"causal conv width 4 + SiLU, [{cfg.batch}, {cfg.seqlen}, {CH}] channels split into x, B, C",
-            "avg_us": round(us, 2), "algo_bytes": nbytes, "GB_per_s": round(gbs, 1),
+            "median_us": round(us, 2), "algo_bytes": nbytes, "GB_per_s": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def one_pass_measure(cfg, steps, dev, bufs=None):
-    """The one-pass path (ssd_forward_fused: the dt cumsum, then one kernel
-    for chunk states, state hand-over and chunk output) next to the split
-    path, on the same buffers: time per forward pass each, which one
-    ssd_forward takes, and the one-pass kernel's algorithmic bytes (x and y,
-    B and C, dA_cumsum and dt_chunked once, each hand-over state written and
-    read once in fp32, the final state). `bufs` = (inputs, y, final state,
-    workspace) already allocated for `cfg`, else fresh ones (the two paths are
-    always compared on the same buffers: where in HBM the buffers lie changes
-    both paths' times)."""
+class Workload:
+    """One workload's device buffers, ready for timed forward passes."""
+
+    def __init__(self, cfg, seed, dev, chunk=0):
+        import torch
+
+        import mamba_ssd_scan_fwd_amd as ssd
+        from ssd_inputs import make_inputs
+
+        self.cfg, self.dev, self.chunk = cfg, dev, chunk
+        self.inp = make_inputs(cfg, seed=seed)
+        self.d = {k: (v.to(dev) if v is not None else None) for k, v in self.inp.items()}
+        self.desc = ssd.make_desc(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups,
+                                  cfg.io_dtype, chunk)
+        self.Q = ssd.effective_chunk_size(self.desc)
+        self.nc = -(-cfg.seqlen // self.Q)
+        self.ws = torch.empty(ssd.workspace_bytes(self.desc), dtype=torch.uint8, device=dev)
+        self.y = torch.empty_like(self.d["x"])
+        self.hT = torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self.io_bytes = 2 if cfg.io_dtype == "bf16" else 4
+
+    def forward(self, **kw):
+        import mamba_ssd_scan_fwd_amd as ssd
+        d = self.d
+        ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], chunk_size=self.chunk,
+                    y=self.y, final_state=self.hT, workspace=self.ws, **kw)
+
+    def path(self):
+        """The path ssd_forward takes here (its workspace record), after one call."""
+        import mamba_ssd_scan_fwd_amd as ssd
+        self.forward()
+        path, status = ssd.workspace_status(self.desc, self.ws)
+        if status != 0:
+            raise RuntimeError(f"{self.cfg.name}: status record {status:#x} after a forward call")
+        return path
+
+    def step_fns(self):
+        """The launches of one split-path pass through the step entry points,
+        by kernel name (the same kernels ssd_forward launches there), on
+        intermediates of their own."""
+        import ctypes
+
+        import mamba_ssd_scan_fwd_amd as ssd
+        lib = ssd.load_library()
+        d, desc, st = self.d, self.desc, self.stream
+        vp = ctypes.c_void_p
+        cfg = self.cfg
+        import torch
+        cs = torch.empty((cfg.batch, cfg.nheads, self.nc, self.Q), dtype=torch.float32, device=self.dev)
+        dtc = torch.empty_like(cs)
+        states = torch.empty((cfg.batch, cfg.nheads, self.nc, cfg.headdim, cfg.dstate), dtype=d["x"].dtype,
+                             device=self.dev)
+        self._keep = (cs, dtc, states)
+        S = vp(st.cuda_stream)
+        P = lambda t: None if t is None else vp(t.data_ptr())  # noqa: E731
+
+        def k_cumsum():
+            assert lib.ssd_chunk_cumsum(ctypes.byref(desc), P(d["dt"]), P(d["A"]), P(cs), P(dtc), S) == 0
+
+        def k_state():
+            assert lib.ssd_chunk_state(ctypes.byref(desc), P(d["x"]), P(d["B"]), P(cs), P(dtc), P(states), S) == 0
+
+        def k_cumsum_state():
+            assert lib.ssd_cumsum_chunk_state(ctypes.byref(desc), P(d["x"]), P(d["B"]), P(d["dt"]), P(d["A"]),
+                                              P(cs), P(dtc), P(states), S) == 0
+
+        def k_pass():
+            assert lib.ssd_state_passing(ctypes.byref(desc), P(states), P(cs), P(d["init_state"]), P(self.hT),
+                                         S) == 0
+
+        def k_scan():
+            assert lib.ssd_chunk_scan(ctypes.byref(desc), P(d["x"]), P(d["B"]), P(d["C"]), P(d["D"]), P(cs),
+                                      P(dtc), P(states), P(self.y), S) == 0
+
+        return {"chunk_cumsum": k_cumsum, "chunk_state": k_state, "cumsum_chunk_state": k_cumsum_state,
+                "state_passing": k_pass, "chunk_scan": k_scan}
+
+
+def kernel_times(wl, path, reps, flush):
+    """Average duration (us) of every kernel of one forward pass on `path`,
+    each pass preceded by a flush, with a HIP event between consecutive
+    kernels on the launch stream (the pass runs through the step entry
+    points). On the one-pass path, whose fused kernel has no entry point of
+    its own, the one-pass kernel's time is the whole path's minus the
+    cumsum's (both flushed), marked derived."""
     import torch
+    names = forward_kernels(wl.cfg, path)
+    fns = wl.step_fns()
+    if path == "one-pass":
+        ts_all, _ = timed_steps(lambda: wl.forward(fused=True), reps, wl.stream, flush)
+        ts_cs, _ = timed_steps(fns["chunk_cumsum"], reps, wl.stream, flush)
+        t_all, t_cs = statistics.median(ts_all), statistics.median(ts_cs)
+        return {"chunk_cumsum": t_cs, "one_pass": t_all - t_cs}, True
+    calls = [fns[n] for n in names]
+    for _ in range(2):
+        for fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    rec = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+        evs[0].record(wl.stream)
+        for i, fn in enumerate(calls):
+            fn()
+            evs[i + 1].record(wl.stream)
+        rec.append(evs)
+    torch.cuda.synchronize()
+    rec = rec[2:] if len(rec) > 4 else rec
+    return {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in rec) / len(rec) * 1e3 for i, n in enumerate(names)}, False
 
+
+def kernel_table(wl, times):
+    model = algorithmic_model(wl.cfg, wl.Q, wl.io_bytes)
+    out = {}
+    for name, us in times.items():
+        m = model[name]
+        out[name] = {"avg_us": round(us, 2), "algo_bytes": m["bytes"], "algo_flops": m["flops"],
+                     "GB_per_s": round(m["bytes"] / (us * 1e-6) / 1e9, 1),
+                     "TFLOP_per_s": round(m["flops"] / (us * 1e-6) / 1e12, 2)}
+    return out
+
+
+def workload_entry(cfg, seed, dev, steps, flush, chunk=0):
+    """Flushed and warm time per forward pass of one workload, the path
+    ssd_forward takes, its useful TFLOP/s and its dominant kernel against the
+    HBM roofline."""
+    import torch
+    wl = Workload(cfg, seed, dev, chunk)
+    path = wl.path()
+    for _ in range(3):
+        wl.forward()
+    ts, _ = timed_steps(wl.forward, steps, wl.stream, flush)
+    warm, _ = timed_steps(wl.forward, steps, wl.stream, None)
+    times, derived = kernel_times(wl, path, max(6, steps), flush)
+    ktab = kernel_table(wl, times)
+    model = algorithmic_model(cfg, wl.Q, wl.io_bytes)
+    flops = sum(model[k]["flops"] for k in forward_kernels(cfg, path))
+    med = statistics.median(ts)
+    dom = max(times, key=times.get)
+    out = {
+        "workload": f"{cfg.name}: B {cfg.batch}, L {cfg.seqlen}, H {cfg.nheads}, P {cfg.headdim}, N {cfg.dstate}, "
+                    f"G {cfg.ngroups}, {cfg.io_dtype}",
+        "path": path, "chunk": wl.Q,
+        "ms_per_step": round(med / 1e3, 4), "p10_ms": round(quantile(ts, 0.1) / 1e3, 4),
+        "p90_ms": round(quantile(ts, 0.9) / 1e3, 4), "warm_ms_per_step": round(statistics.median(warm) / 1e3, 4),
+        "tokens_per_s": round(cfg.tokens / (med * 1e-6), 1),
+        "useful_TFLOP_per_s": round(flops / (med * 1e-6) / 1e12, 2),
+        "kernels": ktab, "kernel_times_derived": derived,
+        "dominant": {"kernel": dom, "avg_us": round(times[dom], 2),
+                     "hbm_frac": round(ktab[dom]["GB_per_s"] / HBM_PEAK_GBS, 4),
+                     "mfma_frac_useful": round(ktab[dom]["TFLOP_per_s"] / MFMA_BF16_PEAK_TFS, 4)},
+    }
+    del wl
+    torch.cuda.empty_cache()
+    return out
+
+
+def one_pass_measure(wl, steps, flush):
+    """The one-pass path (ssd_forward_fused) next to the split path
+    (ssd_forward_split) and ssd_forward itself, on the same buffers `wl`
+    (where in HBM buffers lie changes both paths' times): the three in turn,
+    three times, flushed medians."""
     import mamba_ssd_scan_fwd_amd as ssd
-    from ssd_inputs import make_inputs
-
-    desc = ssd.make_desc(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.io_dtype)
-    if bufs is None:
-        inp = make_inputs(cfg, seed=104)
-        d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
-        y = torch.empty_like(d["x"])
-        hT = torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device=dev)
-        ws = torch.empty(ssd.workspace_bytes(desc), dtype=torch.uint8, device=dev)
-    else:
-        d, y, hT, ws = bufs
-    stream = torch.cuda.current_stream(dev)
-
-    def run(**kw):
-        ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], y=y, final_state=hT,
-                    workspace=ws, **kw)
-
-    def timed(**kw):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(steps):
-            run(**kw)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / steps * 1e3
-
+    cfg = wl.cfg
     paths = {"split": dict(split=True), "fused": dict(fused=True), "auto": {}}
     try:
         for kw in paths.values():
-            for _ in range(5):
-                run(**kw)
+            for _ in range(3):
+                wl.forward(**kw)
     except ssd.SSDError:
         return {"workload": cfg.name, "supported": False}
-    torch.cuda.synchronize()
-    # the three paths in turn, three times: the medians (a path timed only
-    # first or only last would carry any drift of the clocks)
     times = {k: [] for k in paths}
     for _ in range(3):
         for k, kw in paths.items():
-            times[k].append(timed(**kw))
+            ts, _ = timed_steps(lambda: wl.forward(**kw), steps, wl.stream, flush)
+            times[k].extend(ts)
     split_us, fused_us, auto_us = (statistics.median(times[k]) for k in ("split", "fused", "auto"))
     T = cfg.tokens
-    Q = ssd.effective_chunk_size(desc)
-    nc = -(-cfg.seqlen // Q)
-    s = 2
-    H, P, N, G = cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
-    nbytes = (2 * T * H * P * s + 2 * T * G * N * s + 2 * cfg.batch * H * nc * Q * 4
-              + 2 * cfg.batch * H * (nc - 1) * P * N * 4 + cfg.batch * H * P * N * 4 * (2 if cfg.init_state else 1))
-    out = {"workload": f"{cfg.name}: B {cfg.batch}, L {cfg.seqlen}, H {H}, P {P}, N {N}, G {G}",
-           "supported": True, "one_pass_us": round(fused_us, 2), "one_pass_tokens_per_s": round(T / (fused_us * 1e-6), 1),
-           "one_pass_algo_bytes": nbytes}
-    # which path ssd_forward takes here: the one its own time matches
-    out.update({"split_us": round(split_us, 2), "split_tokens_per_s": round(T / (split_us * 1e-6), 1),
-                "ssd_forward_takes": "one-pass" if abs(auto_us - fused_us) < abs(auto_us - split_us) else "split"})
-    return out
+    model = algorithmic_model(cfg, wl.Q, wl.io_bytes)
+    return {"workload": f"{cfg.name}: B {cfg.batch}, L {cfg.seqlen}, H {cfg.nheads}, P {cfg.headdim}, "
+                        f"N {cfg.dstate}, G {cfg.ngroups}",
+            "supported": True, "one_pass_us": round(fused_us, 2),
+            "one_pass_tokens_per_s": round(T / (fused_us * 1e-6), 1),
+            "one_pass_algo_bytes": model["one_pass"]["bytes"],
+            "split_us": round(split_us, 2), "split_tokens_per_s": round(T / (split_us * 1e-6), 1),
+            "ssd_forward_us": round(auto_us, 2), "ssd_forward_takes": wl.path()}
 
 
 def main():
@@ -344,27 +567,18 @@ def main():
     import torch
 
     import mamba_ssd_scan_fwd_amd as ssd
-    from ssd_inputs import CONFIGS, make_inputs
+    from ssd_inputs import CONFIGS
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ssd.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = CONFIGS[args.config]
-    inp = make_inputs(cfg, seed=args.config)
-    d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
-    io_bytes = 2 if cfg.io_dtype == "bf16" else 4
-    desc = ssd.make_desc(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups,
-                         cfg.io_dtype, args.chunk)
-    Q = ssd.effective_chunk_size(desc)
-    ws = torch.empty(ssd.workspace_bytes(desc), dtype=torch.uint8, device=dev)
-    y = torch.empty_like(d["x"])
-    hT = torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step():
-        ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], chunk_size=args.chunk,
-                    y=y, final_state=hT, workspace=ws)
+    # the headline's buffers are the first the process allocates (as in a
+    # fresh program; where later allocations land changes the times)
+    wl = Workload(cfg, args.config, dev, args.chunk)
+    flush = Flusher(dev, args.flush_mib) if args.flush_mib > 0 else None
+    path = wl.path()
 
     if args.copy_calibration:
         # known traffic: reads and writes exactly MIB MiB each
@@ -378,119 +592,32 @@ def main():
     t_warm = time.perf_counter()
     while time.perf_counter() - t_warm < args.device_warm_ms / 1e3:
         for _ in range(10):
-            step()
+            wl.forward()
         torch.cuda.synchronize()
     for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+        wl.forward()
+    # the K timed steps: each flushed, between its own events
+    ts, wall = timed_steps(wl.forward, args.steps, wl.stream, flush)
+    med_us = statistics.median(ts)
+    # the same K steps back to back (warm caches), one event pair
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
+    ev0.record(wl.stream)
     for _ in range(args.steps):
-        step()
-    ev1.record(stream)
+        wl.forward()
+    ev1.record(wl.stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = gpu_ms / args.steps
-    tokens_per_s = cfg.tokens * args.steps / (gpu_ms / 1e3)
+    warm_us = ev0.elapsed_time(ev1) / args.steps * 1e3
+    tokens_per_s = cfg.tokens / (med_us * 1e-6)
 
-    # ---- every kernel on its own: HIP events on the launch stream ----------
+    # ---- every kernel of the pass, flushed passes, events between kernels ----
     reps = args.kernel_reps or max(10, min(args.steps, 50))
-    nc = -(-cfg.seqlen // Q)
-    cs = torch.empty((cfg.batch, cfg.nheads, nc, Q), dtype=torch.float32, device=dev)
-    dtc = torch.empty_like(cs)
-    st = torch.empty((cfg.batch, cfg.nheads, nc, cfg.headdim, cfg.dstate), dtype=d["x"].dtype, device=dev)
-    kw = dict(chunk_size=args.chunk)
-    common = dict(headdim=cfg.headdim, dstate=cfg.dstate, ngroups=cfg.ngroups, io_dtype=cfg.io_dtype)
-
-    def k_cumsum():
-        lib = ssd.load_library()
-        import ctypes
-        r = lib.ssd_chunk_cumsum(ctypes.byref(desc), ctypes.c_void_p(d["dt"].data_ptr()),
-                                 ctypes.c_void_p(d["A"].data_ptr()), ctypes.c_void_p(cs.data_ptr()),
-                                 ctypes.c_void_p(dtc.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
-        assert r == 0
-
-    def k_state():
-        lib = ssd.load_library()
-        import ctypes
-        r = lib.ssd_chunk_state(ctypes.byref(desc), ctypes.c_void_p(d["x"].data_ptr()),
-                                ctypes.c_void_p(d["B"].data_ptr()), ctypes.c_void_p(cs.data_ptr()),
-                                ctypes.c_void_p(dtc.data_ptr()), ctypes.c_void_p(st.data_ptr()),
-                                ctypes.c_void_p(stream.cuda_stream))
-        assert r == 0
-
-    def k_cumsum_state():
-        lib = ssd.load_library()
-        import ctypes
-        r = lib.ssd_cumsum_chunk_state(ctypes.byref(desc), ctypes.c_void_p(d["x"].data_ptr()),
-                                       ctypes.c_void_p(d["B"].data_ptr()), ctypes.c_void_p(d["dt"].data_ptr()),
-                                       ctypes.c_void_p(d["A"].data_ptr()), ctypes.c_void_p(cs.data_ptr()),
-                                       ctypes.c_void_p(dtc.data_ptr()), ctypes.c_void_p(st.data_ptr()),
-                                       ctypes.c_void_p(stream.cuda_stream))
-        assert r == 0
-
-    def k_pass():
-        lib = ssd.load_library()
-        import ctypes
-        h0 = d["init_state"]
-        r = lib.ssd_state_passing(ctypes.byref(desc), ctypes.c_void_p(st.data_ptr()),
-                                  ctypes.c_void_p(cs.data_ptr()),
-                                  None if h0 is None else ctypes.c_void_p(h0.data_ptr()),
-                                  ctypes.c_void_p(hT.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
-        assert r == 0
-
-    def k_scan():
-        lib = ssd.load_library()
-        import ctypes
-        Dp = None if d["D"] is None else ctypes.c_void_p(d["D"].data_ptr())
-        r = lib.ssd_chunk_scan(ctypes.byref(desc), ctypes.c_void_p(d["x"].data_ptr()),
-                               ctypes.c_void_p(d["B"].data_ptr()), ctypes.c_void_p(d["C"].data_ptr()), Dp,
-                               ctypes.c_void_p(cs.data_ptr()), ctypes.c_void_p(dtc.data_ptr()),
-                               ctypes.c_void_p(st.data_ptr()), ctypes.c_void_p(y.data_ptr()),
-                               ctypes.c_void_p(stream.cuda_stream))
-        assert r == 0
-
-    del kw, common
-    # The same four launches as one forward step, issued through the step
-    # entry points with an event between consecutive kernels: each kernel's
-    # duration in the context of the whole pass (caches as the pass leaves them).
-    names = ["cumsum_chunk_state", "state_passing", "chunk_scan"]
-    fns = [k_cumsum_state, k_pass, k_scan]
-    if cfg.io_dtype != "bf16":  # ssd_forward runs the two steps as two kernels there
-        names = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
-        fns = [k_cumsum, k_state, k_pass, k_scan]
-    for _ in range(2):
-        for fn in fns:
-            fn()
-    torch.cuda.synchronize()
-    rec = []
-    for _ in range(reps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
-        evs[0].record(stream)
-        for i, fn in enumerate(fns):
-            fn()
-            evs[i + 1].record(stream)
-        rec.append(evs)
-    torch.cuda.synchronize()
-    rec = rec[2:] if len(rec) > 4 else rec  # the first passes may wait for the host to queue launches
-    durations = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in rec) / len(rec) * 1e3 for i, n in enumerate(names)}
-    model = algorithmic_model(cfg, Q, io_bytes)
-    per_kernel = {}
-    for name, us in durations.items():
-        m = model[name]
-        per_kernel[name] = {
-            "avg_us": round(us, 2),
-            "algo_bytes": m["bytes"],
-            "algo_flops": m["flops"],
-            "GB_per_s": round(m["bytes"] / (us * 1e-6) / 1e9, 1),
-            "TFLOP_per_s": round(m["flops"] / (us * 1e-6) / 1e12, 2),
-        }
-    dom = max(durations, key=durations.get)
+    times, derived = kernel_times(wl, path, reps, flush)
+    per_kernel = kernel_table(wl, times)
+    model = algorithmic_model(cfg, wl.Q, wl.io_bytes)
+    dom = max(times, key=times.get)
     m = model[dom]
-    ach_gbs = m["bytes"] / (durations[dom] * 1e-6) / 1e9
-    traffic = traffic_from_profile(dom, cfg.name, m["bytes"])
+    ach_gbs = m["bytes"] / (times[dom] * 1e-6) / 1e9
+    traffic = None if derived else traffic_from_profile(dom, cfg.name, m["bytes"])
     roofline = {
         "kernel": dom,
         "bound": "hbm",
@@ -500,26 +627,37 @@ def main():
         "frac": round(ach_gbs / HBM_PEAK_GBS, 4),
         "traffic": traffic,
         "algo_bytes_per_launch": m["bytes"],
-        "avg_launch_us": round(durations[dom], 2),
-        "mfma_frac_useful": round(m["flops"] / (durations[dom] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+        "avg_launch_us": round(times[dom], 2),
+        "mfma_frac_useful": round(m["flops"] / (times[dom] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
     }
+    fwd_flops = sum(model[k]["flops"] for k in forward_kernels(cfg, path))
 
     one_pass = None
     if not args.no_one_pass and cfg.io_dtype == "bf16":
-        one_pass = [one_pass_measure(cfg, 30, dev, (d, y, hT, ws)),
-                    one_pass_measure(cfg.with_(name=f"{cfg.name} x4 batch", batch=4 * cfg.batch), 30, dev)]
+        one_pass = [one_pass_measure(wl, 10, flush)]
+        big = Workload(cfg.with_(name=f"{cfg.name} x4 batch", batch=4 * cfg.batch), 104, dev, args.chunk)
+        one_pass.append(one_pass_measure(big, 10, flush))
+        del big
+        torch.cuda.empty_cache()
 
-    decode = None
+    decode = varlen = conv = None
     if not args.no_decode:
-        decode = [decode_measure(cfg, bsz, 50, dev) for bsz in (cfg.batch, 256)]
-    varlen = None if args.no_decode else varlen_measure(cfg, 20, dev)
-    conv = None if args.no_decode else conv_measure(cfg, 20, dev)
+        decode = [decode_measure(cfg, bsz, 30, dev, flush) for bsz in (cfg.batch, 256)]
+        varlen = varlen_measure(cfg, 20, dev, flush)
+        conv = conv_measure(cfg, 20, dev, flush)
+
+    workloads = None
+    if not args.no_workloads:
+        workloads = []
+        for i, c in enumerate(CONFIGS):
+            if i != args.config:
+                workloads.append(workload_entry(c, i, dev, args.workload_steps, flush))
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, inp, min(args.cpu_sample_seqs, cfg.batch))
+        workers = args.cpu_workers or max(1, min(16, os.cpu_count() or 1))
+        cpu = cpu_baseline(cfg, wl.inp, min(args.cpu_sample_seqs, cfg.batch), workers)
 
-    total_flops = sum(v["flops"] for v in model.values())
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -527,7 +665,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(med_us / 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -535,12 +673,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "nheads": cfg.nheads,
                    "headdim": cfg.headdim, "dstate": cfg.dstate, "ngroups": cfg.ngroups,
-                   "chunk": Q, "init_state": cfg.init_state},
-        "tflops_per_s": round(total_flops * args.steps / (gpu_ms / 1e3) / 1e12, 2),
-        "wall_s_timed": round(wall, 3),
+                   "chunk": wl.Q, "init_state": cfg.init_state, "path": path},
+        "timing": {"protocol": f"median of {args.steps} steps, each after a {args.flush_mib} MiB scratch write "
+                               "outside its HIP event pair" if flush else "back-to-back steps",
+                   "p10_ms": round(quantile(ts, 0.1) / 1e3, 4), "p90_ms": round(quantile(ts, 0.9) / 1e3, 4),
+                   "warm_ms_per_step": round(warm_us / 1e3, 4),
+                   "warm_tokens_per_s": round(cfg.tokens / (warm_us * 1e-6), 1),
+                   "wall_s_timed": round(wall, 3)},
+        "tflops_per_s": round(fwd_flops / (med_us * 1e-6) / 1e12, 2),
         "roofline": roofline,
         "kernels": per_kernel,
         "cpu_baseline": cpu,
+        "workloads": workloads,
         "decode_step": decode,
         "varlen": varlen,
         "conv1d_split": conv,

@@ -87,6 +87,28 @@ typedef enum {
   SSD_ERR_HIP = 7           /* the HIP runtime reported an error               */
 } ssd_status_t;
 
+/* Path a whole-forward call took, as recorded in its workspace
+ * (ssd_workspace_status). */
+typedef enum {
+  SSD_PATH_NONE = 0,            /* no forward call recorded in the workspace   */
+  SSD_PATH_SPLIT = 1,           /* separate steps, chain over chunks per lane  */
+  SSD_PATH_SPLIT_SEGMENTED = 2, /* separate steps, chains cut into segments    */
+  SSD_PATH_ONE_PASS = 3         /* the one-pass kernel of ssd_forward_fused    */
+} ssd_path_t;
+
+/* Status bits reported by ssd_workspace_status (0 = the call completed as
+ * designed). Any bit set means y and final_state of that call are not valid,
+ * and, when final_state was the same buffer as init_state, neither is that
+ * buffer. */
+enum {
+  SSD_STATUS_WAIT_CUT_OFF_ONE_PASS = 1u,  /* a one-pass state hand-over wait gave up     */
+  SSD_STATUS_WAIT_CUT_OFF_SEGMENTED = 2u, /* a segmented state-passing wait gave up      */
+  SSD_STATUS_CHAIN_INCOMPLETE = 4u,       /* a hand-over counter or ticket count is not
+                                             at its final value                          */
+  SSD_STATUS_NO_RECORD = 8u               /* the workspace holds no forward record for
+                                             this descriptor                             */
+};
+
 /* Problem description. Plain data; the library reads it during the call only.
  * A zero-initialised tail (dt_bias .. dt_max) means dt is used as given. */
 typedef struct {
@@ -141,7 +163,11 @@ SSD_API ssd_status_t ssd_workspace_bytes(const ssd_desc_t* desc, size_t* bytes);
  * ssd_forward_split), or, where the one-pass kernel of ssd_forward_fused
  * supports the shape and is the faster choice for it, that path. The
  * environment variable SSD_FORWARD_PATH=split or =fused, read once per
- * process, overrides the choice (fused only where it is supported). */
+ * process, overrides the choice (fused only where it is supported).
+ * SSD_OK means every argument was valid and every kernel was enqueued. Both
+ * paths may contain bounded waits between workgroups (see
+ * ssd_workspace_status); a wait cut off after the call returned does not
+ * change the return value, and ssd_workspace_status reports it. */
 SSD_API ssd_status_t ssd_forward(const ssd_desc_t* desc,
                          const void* x, const float* dt, const float* A,
                          const void* B, const void* C, const float* D,
@@ -168,8 +194,9 @@ SSD_API ssd_status_t ssd_forward(const ssd_desc_t* desc,
  * weights are applied to B instead of x before the bf16 rounding.
  * Every wait of one chunk's workgroup for the state of the chunk before is
  * bounded; a wait that is cut off sets a status bit in the workspace instead
- * of hanging. With the environment variable SSD_DEBUG set, the call waits for
- * the kernel and returns SSD_ERR_HIP if that bit is set. */
+ * of hanging, and the call still returns SSD_OK: ssd_workspace_status reads
+ * the bit. With the environment variable SSD_DEBUG set, every whole-forward
+ * call waits for its kernels and returns SSD_ERR_HIP if a bit is set. */
 SSD_API ssd_status_t ssd_forward_fused(const ssd_desc_t* desc,
                                const void* x, const float* dt, const float* A,
                                const void* B, const void* C, const float* D,
@@ -192,6 +219,36 @@ SSD_API ssd_status_t ssd_forward_split(const ssd_desc_t* desc,
                                void* y, float* final_state,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/* Status of the last whole-forward call (ssd_forward, ssd_forward_split or
+ * ssd_forward_fused) that ran with `workspace` and this descriptor.
+ *
+ * Two paths synchronise workgroups of one kernel with bounded waits: the
+ * one-pass kernel (each chunk waits for the state of the chunk before) and
+ * the segmented state passing of ssd_forward for a few long sequences (each
+ * segment waits for the aggregates of the segments before). Every such wait
+ * gives up after a fixed number of polls, so a kernel always ends; the wait
+ * then sets a bit in a status record the call keeps in its workspace, and the
+ * forward call itself has already returned SSD_OK. That record, and for these
+ * two paths the hand-over counters and ticket count, are what this call
+ * checks. (A cut-off is a defect of the launch, not of the inputs: under the
+ * ticket order every wait targets a workgroup that has started and is not
+ * blocked, so it is not expected in any run.)
+ *
+ * Enqueues device-to-host copies of a few words on `stream` and synchronises
+ * that stream (so it cannot be captured into a graph). Allocates nothing.
+ *   desc       the descriptor the forward call was made with.
+ *   workspace  that call's workspace (a caller-provided one: with a NULL
+ *              workspace the library's own is freed when the call ends),
+ *              at least ssd_workspace_bytes() bytes, 256-byte aligned.
+ *   path       nullable; receives the ssd_path_t the call took.
+ *   status     receives the SSD_STATUS_* bits, 0 when the call completed as
+ *              designed.
+ * Returns SSD_ERR_NULL_POINTER, SSD_ERR_ALIGNMENT, SSD_ERR_WORKSPACE for a
+ * bad argument, SSD_ERR_HIP when a copy fails. Packed sequences
+ * (ssd_forward_varlen) use no bounded wait and keep no record. */
+SSD_API ssd_status_t ssd_workspace_status(const ssd_desc_t* desc, const void* workspace, size_t workspace_bytes,
+                                          void* stream, uint32_t* path, uint32_t* status);
 
 /* ---- the steps of the chunked path, each callable on its own ------------ */
 

@@ -7,6 +7,11 @@ library with ``python -m mamba_ssd_scan_fwd_amd.build``.
 
 from .binding import (  # noqa: F401
     EXPORTED_SYMBOLS,
+    PATH_NAMES,
+    STATUS_CHAIN_INCOMPLETE,
+    STATUS_NO_RECORD,
+    STATUS_WAIT_CUT_OFF_ONE_PASS,
+    STATUS_WAIT_CUT_OFF_SEGMENTED,
     SSDDesc,
     SSDError,
     chunk_cumsum,
@@ -24,4 +29,5 @@ from .binding import (  # noqa: F401
     state_passing,
     status_string,
     workspace_bytes,
+    workspace_status,
 )

@@ -22,6 +22,7 @@ __all__ = [
     "status_string",
     "effective_chunk_size",
     "workspace_bytes",
+    "workspace_status",
     "forward",
     "chunk_cumsum",
     "chunk_state",
@@ -44,6 +45,7 @@ EXPORTED_SYMBOLS = (
     "ssd_forward",
     "ssd_forward_fused",
     "ssd_forward_split",
+    "ssd_workspace_status",
     "ssd_chunk_cumsum",
     "ssd_chunk_state",
     "ssd_cumsum_chunk_state",
@@ -120,6 +122,9 @@ def load_library():
         lib.ssd_forward_fused.restype = ctypes.c_int
         lib.ssd_forward_split.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.ssd_forward_split.restype = ctypes.c_int
+        lib.ssd_workspace_status.argtypes = [dp, vp, sz, vp, ctypes.POINTER(ctypes.c_uint32),
+                                             ctypes.POINTER(ctypes.c_uint32)]
+        lib.ssd_workspace_status.restype = ctypes.c_int
         lib.ssd_chunk_cumsum.argtypes = [dp, vp, vp, vp, vp, vp]
         lib.ssd_chunk_cumsum.restype = ctypes.c_int
         lib.ssd_chunk_state.argtypes = [dp, vp, vp, vp, vp, vp, vp]
@@ -288,6 +293,26 @@ def forward(x, dt, A, B, C, D=None, init_state=None, *, chunk_size: int = 0,
         _ptr(y), _ptr(final_state), _ptr(workspace), ctypes.c_size_t(wsize), _stream(stream, dev))
     _check(st, name)
     return y, final_state
+
+
+PATH_NAMES = {0: "none", 1: "split", 2: "split-segmented", 3: "one-pass"}
+STATUS_WAIT_CUT_OFF_ONE_PASS = 1
+STATUS_WAIT_CUT_OFF_SEGMENTED = 2
+STATUS_CHAIN_INCOMPLETE = 4
+STATUS_NO_RECORD = 8
+
+
+def workspace_status(desc: SSDDesc, workspace, stream=None):
+    """(path name, status bits) of the last whole-forward call that used
+    ``workspace`` (a uint8 device tensor) with ``desc``; synchronises the
+    stream. Status 0 means the call completed as designed."""
+    path = ctypes.c_uint32(0)
+    bits = ctypes.c_uint32(0)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().ssd_workspace_status(ctypes.byref(desc), _ptr(workspace), ctypes.c_size_t(nbytes),
+                                               _stream(stream, workspace.device), ctypes.byref(path),
+                                               ctypes.byref(bits)), "ssd_workspace_status")
+    return PATH_NAMES.get(int(path.value), str(path.value)), int(bits.value)
 
 
 def _chunk_shape(desc):

@@ -110,10 +110,13 @@ struct WsLayout {
   size_t cs_off, dt_off, st_off, tab_off, seq_off, total;
   size_t sp_off;  // segmented state passing scratch (0 if not used)
   // one-pass path, inside the states region: the state hand-over ring, then
-  // the per-head counters, the ticket and the status word (32-bit each)
+  // the per-head counters and the ticket (32-bit each)
   size_t ring_off, sync_off;
   int64_t nsync;
+  // whole-forward status record (batched layout only): path tag, status bits
+  size_t stat_off;
 };
+constexpr size_t kStatBytes = 256;
 
 // dA_cumsum, dt_chunked, states and (packed sequences) the chunk table, each
 // on a kWsAlign boundary. p.nc counts chunk slots. Where the one-pass path
@@ -122,7 +125,7 @@ WsLayout ws_layout(const Plan& p, bool with_table = false) {
   WsLayout w;
   const size_t cs_bytes = size_t(p.batch * p.H * p.nc * p.Q) * sizeof(float);
   size_t st_bytes = size_t(p.batch * p.H * p.nc * p.P * p.N) * p.io_bytes();
-  w.nsync = p.batch * p.H + 2;
+  w.nsync = p.batch * p.H + 1;
   w.ring_off = 0;
   w.sync_off = 0;
   if (!with_table && fused_forward_supported(p)) {
@@ -143,7 +146,8 @@ WsLayout ws_layout(const Plan& p, bool with_table = false) {
     w.tab_off = align_up(w.sp_off + seg_scratch_layout(p, nullptr).bytes, kWsAlign);
   }
   w.seq_off = align_up(w.tab_off + size_t(p.nc) * sizeof(ChunkInfo), kWsAlign);
-  w.total = with_table ? align_up(w.seq_off + size_t(p.nseq) * sizeof(int2), kWsAlign) : w.tab_off;
+  w.stat_off = with_table ? 0 : w.tab_off;
+  w.total = with_table ? align_up(w.seq_off + size_t(p.nseq) * sizeof(int2), kWsAlign) : w.stat_off + kStatBytes;
   return w;
 }
 
@@ -280,32 +284,33 @@ ssd_status_t enqueue_forward(const Plan& p, bool fused, const void* x, const flo
                  (long long)p.batch, (long long)p.L, (long long)p.H, (long long)p.P, (long long)p.N,
                  (long long)p.G, p.io == kBF16 ? "bf16" : "fp32", p.Q, (long long)p.nc, ws.total,
                  fused ? "fused" : (mfma_chunk_scan_supported(p) ? "split-mfma" : "split-simt"));
+  uint32_t* stat = reinterpret_cast<uint32_t*>(w + ws.stat_off);
   hipError_t e;
   if (fused) {
     uint32_t* sync = reinterpret_cast<uint32_t*>(w + ws.sync_off);
     FusedArgs a{x,    B,       C,  D,   cs, dtc, init_state, y, final_state, reinterpret_cast<float*>(w + ws.ring_off),
-                sync, sync + p.batch * p.H, sync + p.batch * p.H + 1};
-    e = launch_chunk_cumsum_clear(p, dt, A, cs, dtc, sync, ws.nsync, s);
+                sync, sync + p.batch * p.H, stat + 1};
+    e = launch_chunk_cumsum_clear(p, dt, A, cs, dtc, sync, ws.nsync, stat, kPathOnePass, s);
     if (e == hipSuccess) e = launch_fused_forward(p, a, s);
-    if (e == hipSuccess && debug_enabled()) {
-      // check the status word: a hand-over wait that was cut off leaves bit 0 set
-      uint32_t status = 0;
-      e = hipMemcpyAsync(&status, a.status, sizeof(status), hipMemcpyDeviceToHost, s);
-      if (e == hipSuccess) e = hipStreamSynchronize(s);
-      if (e == hipSuccess && status != 0) {
-        std::fprintf(stderr, "[ssd] one-pass kernel: a state hand-over wait was cut off (status %u)\n", status);
-        e = hipErrorUnknown;
-      }
-    }
   } else {
     e = run_cumsum_chunk_state(p, x, B, dt, A, cs, dtc, states, s);
     if (e == hipSuccess) {
       if (ws.sp_off != 0)
-        e = launch_state_passing_seg(p, states, cs, init_state, final_state, w + ws.sp_off, s);
+        e = launch_state_passing_seg(p, states, cs, init_state, final_state, w + ws.sp_off, stat, s);
       else
-        e = launch_state_passing(p, states, cs, init_state, final_state, s);
+        e = launch_state_passing(p, states, cs, init_state, final_state, s, stat);
     }
     if (e == hipSuccess) e = run_chunk_scan(p, x, B, C, D, cs, dtc, states, y, s);
+  }
+  if (e == hipSuccess && debug_enabled()) {
+    // check the status record: a bounded wait that was cut off leaves a bit set
+    uint32_t rec[2] = {0, 0};
+    e = hipMemcpyAsync(rec, stat, sizeof(rec), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess && rec[1] != 0) {
+      std::fprintf(stderr, "[ssd] path %u: a bounded wait was cut off (status %u)\n", rec[0], rec[1]);
+      e = hipErrorUnknown;
+    }
   }
   if (owned) {
     const hipError_t fe = hipFreeAsync(wbase, s);
@@ -394,6 +399,72 @@ ssd_status_t ssd_forward_fused(const ssd_desc_t* desc, const void* x, const floa
   if (st != SSD_OK) return st;
   return ssd::enqueue_forward(p, true, x, dt, A, B, C, D, init_state, y, final_state, workspace, ws,
                               static_cast<hipStream_t>(stream));
+}
+
+ssd_status_t ssd_workspace_status(const ssd_desc_t* desc, const void* workspace, size_t workspace_bytes,
+                                  void* stream, uint32_t* path, uint32_t* status) {
+  Plan p;
+  ssd_status_t st = ssd::make_plan(desc, &p);
+  if (st != SSD_OK) return st;
+  if (workspace == nullptr || status == nullptr) return SSD_ERR_NULL_POINTER;
+  if (!ssd::aligned(workspace, ssd::kWsAlign)) return SSD_ERR_ALIGNMENT;
+  const ssd::WsLayout ws = ssd::ws_layout(p);
+  if (workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* w = static_cast<const char*>(workspace);
+
+  // Copy n 32-bit words from the workspace and wait for them.
+  auto fetch = [&](uint32_t* dst, const void* src, size_t n) {
+    hipError_t e = hipMemcpyAsync(dst, src, n * sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e == hipSuccess;
+  };
+  // Every word of [src, src + n) equals want(i), read in pieces of kPiece words.
+  constexpr int64_t kPiece = 1024;
+  uint32_t buf[kPiece];
+  bool hip_ok = true;
+  auto all_equal = [&](const uint32_t* src, int64_t n, auto want) {
+    for (int64_t i0 = 0; i0 < n; i0 += kPiece) {
+      const int64_t m = n - i0 < kPiece ? n - i0 : kPiece;
+      if (!fetch(buf, src + i0, size_t(m))) {
+        hip_ok = false;
+        return false;
+      }
+      for (int64_t i = 0; i < m; ++i)
+        if (buf[i] != want(i0 + i)) return false;
+    }
+    return true;
+  };
+
+  uint32_t rec[2] = {0, 0};
+  if (!fetch(rec, w + ws.stat_off, 2)) return SSD_ERR_HIP;
+  uint32_t bits = rec[1] & (SSD_STATUS_WAIT_CUT_OFF_ONE_PASS | SSD_STATUS_WAIT_CUT_OFF_SEGMENTED);
+  uint32_t tag = rec[0];
+  if (tag == ssd::kPathOnePass && ssd::fused_forward_supported(p)) {
+    // every head's counter at its last hand-over, one ticket per workgroup
+    const uint32_t* sync = reinterpret_cast<const uint32_t*>(w + ws.sync_off);
+    const uint32_t last = p.nc > 1 ? uint32_t(p.nc - 1) : 0u;
+    const bool flags_ok = all_equal(sync, p.batch * p.H, [&](int64_t) { return last; });
+    const uint32_t tickets = uint32_t(ssd::fused_forward_grid(p));
+    const bool ticket_ok = flags_ok && all_equal(sync + p.batch * p.H, 1, [&](int64_t) { return tickets; });
+    if (!flags_ok || !ticket_ok) bits |= SSD_STATUS_CHAIN_INCOMPLETE;
+  } else if (tag == ssd::kPathSplitSegmented && ws.sp_off != 0) {
+    // every segment but the last of each (chain, slice) published, one ticket per workgroup
+    const ssd::SegScratch sc = ssd::seg_scratch_layout(p, const_cast<char*>(w + ws.sp_off));
+    const int64_t nseg = sc.nseg;
+    const bool flags_ok = all_equal(sc.flags, sc.chains * sc.nslice * nseg,
+                                    [&](int64_t i) { return (i % nseg) + 1 < nseg ? 1u : 0u; });
+    const uint32_t tickets = uint32_t(ssd::seg_state_passing_grid(p));
+    const bool ticket_ok = flags_ok && all_equal(sc.ticket, 1, [&](int64_t) { return tickets; });
+    if (!flags_ok || !ticket_ok) bits |= SSD_STATUS_CHAIN_INCOMPLETE;
+  } else if (tag != ssd::kPathSplit) {
+    tag = SSD_PATH_NONE;
+    bits = SSD_STATUS_NO_RECORD;
+  }
+  if (!hip_ok) return SSD_ERR_HIP;
+  if (path != nullptr) *path = tag;
+  *status = bits;
+  return SSD_OK;
 }
 
 ssd_status_t ssd_workspace_bytes_varlen(const ssd_desc_t* desc, int64_t num_seqs, size_t* bytes) {

@@ -671,6 +671,12 @@ bool fused_forward_preferred(const Plan& p) {
   return wgs >= 2 * slots;
 }
 
+int64_t fused_forward_grid(const Plan& p) {
+  int resident = 1, hb = 1;
+  const bool ok = p.P == 32 ? fused_shape_of<32>(p, resident, hb) : fused_shape_of<64>(p, resident, hb);
+  return ok ? p.batch * p.nc * (p.H / hb) : 0;
+}
+
 size_t fused_ring_bytes(const Plan& p) { return size_t(p.batch * p.H * 2) * size_t(p.P * p.N) * sizeof(float); }
 
 hipError_t launch_fused_forward(const Plan& p, const FusedArgs& a, hipStream_t s) {

@@ -77,8 +77,13 @@ template <typename TS, int PF>
 __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     TS* __restrict__ states, const float* __restrict__ dA_cs,
     const float* h0, float* hT,  // may be the same buffer (in-place update)
-    int64_t nc, int Q, int PN, int H, const int2* __restrict__ seqtab) {
+    int64_t nc, int Q, int PN, int H, const int2* __restrict__ seqtab, uint32_t* __restrict__ stat,
+    uint32_t tag) {
   const int64_t bh = blockIdx.x;
+  if (stat != nullptr && bh == 0 && blockIdx.y == 0 && threadIdx.x == 0) {  // the forward's status record
+    stat[0] = tag;
+    stat[1] = 0u;
+  }
   const int e0 = (blockIdx.y * kThreads + threadIdx.x) * kVec;
   const bool active = e0 < PN;
   const int lane = threadIdx.x & 63;
@@ -156,6 +161,7 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
 // other workgroup has read the initial state (they may be the same buffer).
 constexpr int kSegChunks = 32;
 constexpr int kSpinLimit = 1 << 18;
+constexpr uint32_t kCutOffBit = 2u;  // in the forward's status word (bit 0 is the one-pass kernel's)
 
 template <typename TS, int KS>
 __global__ __launch_bounds__(kThreads) void state_passing_seg_kernel(
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void state_passing_seg_kernel(
     for (int spins = 0;; ++spins) {
       if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0) break;
       if (spins >= kSpinLimit) {
-        if (lane == 0) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_fetch_or(status, kCutOffBit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
@@ -278,38 +284,43 @@ __global__ __launch_bounds__(kThreads) void state_passing_seg_kernel(
   if (seg + 1 == nseg && active && hT != nullptr) Vec8<float>::store(hT + bh * PN + e0, h);
 }
 
-__global__ void clear_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+__global__ void clear_words_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t* __restrict__ stat, uint32_t tag) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
+  if (stat != nullptr && i == 0) {
+    stat[0] = tag;
+    stat[1] = 0u;
+  }
 }
 
 template <typename TS>
 hipError_t launch_typed(const Plan& p, void* states, const float* dA_cs,
-                        const float* h0, float* hT, hipStream_t s) {
+                        const float* h0, float* hT, uint32_t* stat, hipStream_t s) {
   const int PN = (int)(p.P * p.N);
   const int64_t chains = p.seqtab != nullptr ? p.nseq * p.H : p.batch * p.H;
   dim3 grid((unsigned)chains, (unsigned)((PN + kThreads * kVec - 1) / (kThreads * kVec)));
   state_passing_kernel<TS, 8><<<grid, kThreads, 0, s>>>(
-      static_cast<TS*>(states), dA_cs, h0, hT, p.nc, p.Q, PN, (int)p.H, p.seqtab);
+      static_cast<TS*>(states), dA_cs, h0, hT, p.nc, p.Q, PN, (int)p.H, p.seqtab, stat, kPathSplit);
   return hipGetLastError();
 }
 
 template <typename TS>
 hipError_t launch_seg_typed(const Plan& p, void* states, const float* dA_cs, const float* h0, float* hT,
-                            void* scratch, hipStream_t s) {
+                            void* scratch, uint32_t* stat, hipStream_t s) {
   const int PN = (int)(p.P * p.N);
   const int64_t chains = p.batch * p.H;
   const int nslice = (PN + kThreads * kVec - 1) / (kThreads * kVec);
   const int nseg = (int)((p.nc + kSegChunks - 1) / kSegChunks);
   SegScratch sc = seg_scratch_layout(p, scratch);
   const int64_t nclear = sc.nwords;
-  clear_words_kernel<<<dim3((unsigned)((nclear + 255) / 256)), 256, 0, s>>>(sc.flags, nclear);
+  clear_words_kernel<<<dim3((unsigned)((nclear + 255) / 256)), 256, 0, s>>>(sc.flags, nclear, stat,
+                                                                             kPathSplitSegmented);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t grid = chains * nslice * nseg;
   state_passing_seg_kernel<TS, kSegChunks><<<dim3((unsigned)grid), kThreads, 0, s>>>(
-      static_cast<TS*>(states), dA_cs, h0, hT, sc.agg, sc.agg_lam, sc.flags, sc.ticket, sc.status, p.nc, p.Q, PN,
-      chains, nslice, nseg);
+      static_cast<TS*>(states), dA_cs, h0, hT, sc.agg, sc.agg_lam, sc.flags, sc.ticket,
+      stat != nullptr ? stat + 1 : sc.status, p.nc, p.Q, PN, chains, nslice, nseg);
   return hipGetLastError();
 }
 
@@ -341,6 +352,9 @@ SegScratch seg_scratch_layout(const Plan& p, void* base) {
   const size_t lam_b = up(size_t(chains * nseg) * 4);
   SegScratch sc;
   sc.nwords = chains * nslice * nseg + 2;
+  sc.chains = chains;
+  sc.nslice = nslice;
+  sc.nseg = nseg;
   sc.bytes = agg_b + lam_b + up(size_t(sc.nwords) * 4);
   char* b = static_cast<char*>(base);
   sc.agg = reinterpret_cast<float*>(b);
@@ -352,15 +366,21 @@ SegScratch seg_scratch_layout(const Plan& p, void* base) {
 }
 
 hipError_t launch_state_passing_seg(const Plan& p, void* states, const float* dA_cs, const float* h0, float* hT,
-                                    void* scratch, hipStream_t s) {
-  if (p.io == kBF16) return launch_seg_typed<__hip_bfloat16>(p, states, dA_cs, h0, hT, scratch, s);
-  return launch_seg_typed<float>(p, states, dA_cs, h0, hT, scratch, s);
+                                    void* scratch, uint32_t* stat, hipStream_t s) {
+  if (p.io == kBF16) return launch_seg_typed<__hip_bfloat16>(p, states, dA_cs, h0, hT, scratch, stat, s);
+  return launch_seg_typed<float>(p, states, dA_cs, h0, hT, scratch, stat, s);
 }
 
 hipError_t launch_state_passing(const Plan& p, void* states, const float* dA_cs,
-                                const float* h0, float* hT, hipStream_t s) {
-  if (p.io == kBF16) return launch_typed<__hip_bfloat16>(p, states, dA_cs, h0, hT, s);
-  return launch_typed<float>(p, states, dA_cs, h0, hT, s);
+                                const float* h0, float* hT, hipStream_t s, uint32_t* stat) {
+  if (p.io == kBF16) return launch_typed<__hip_bfloat16>(p, states, dA_cs, h0, hT, stat, s);
+  return launch_typed<float>(p, states, dA_cs, h0, hT, stat, s);
+}
+
+int64_t seg_state_passing_grid(const Plan& p) {
+  const int64_t PN = p.P * p.N;
+  const int64_t nslice = (PN + kThreads * kVec - 1) / (kThreads * kVec);
+  return p.batch * p.H * nslice * ((p.nc + kSegChunks - 1) / kSegChunks);
 }
 
 }  // namespace ssd

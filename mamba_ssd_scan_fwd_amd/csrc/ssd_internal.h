@@ -41,14 +41,22 @@ struct Plan {
   size_t io_bytes() const { return io == kBF16 ? 2 : 4; }
 };
 
+// The status record a whole-forward call leaves in its workspace: word 0 the
+// path it took (tags below, written by its first kernel that runs on every
+// path), word 1 the status bits (cleared by that same kernel; a bounded wait
+// that gives up ORs its bit in).
+constexpr uint32_t kPathSplit = 1, kPathSplitSegmented = 2, kPathOnePass = 3;
+
 // Step launchers. Each returns the hipGetLastError() after its launches.
 hipError_t launch_chunk_cumsum(const Plan& p, const float* dt, const float* A,
                                float* dA_cs, float* dtc, hipStream_t s);
 hipError_t launch_chunk_state(const Plan& p, const void* x, const void* B,
                               const float* dA_cs, const float* dtc, void* states,
                               hipStream_t s);
+// stat: the forward's status record (nullptr for the step entry point and
+// packed sequences), tagged kPathSplit.
 hipError_t launch_state_passing(const Plan& p, void* states, const float* dA_cs,
-                                const float* h0, float* hT, hipStream_t s);
+                                const float* h0, float* hT, hipStream_t s, uint32_t* stat = nullptr);
 // State passing for a few long chains: segments of one chain in parallel,
 // with scratch from the workspace (seg_scratch_layout(p, nullptr).bytes).
 struct SegScratch {
@@ -58,12 +66,16 @@ struct SegScratch {
   uint32_t* ticket;
   uint32_t* status;
   int64_t nwords;   // flags + ticket + status
+  int64_t chains, nslice, nseg;  // flags[(chain * nslice + slice) * nseg + segment]
   size_t bytes;
 };
 bool seg_state_passing_applies(const Plan& p);
 SegScratch seg_scratch_layout(const Plan& p, void* base);
+// stat: the forward's status record, tagged kPathSplitSegmented; a cut-off
+// wait sets bit 1 of its status word.
 hipError_t launch_state_passing_seg(const Plan& p, void* states, const float* dA_cs, const float* h0, float* hT,
-                                    void* scratch, hipStream_t s);
+                                    void* scratch, uint32_t* stat, hipStream_t s);
+int64_t seg_state_passing_grid(const Plan& p);  // workgroups (= tickets) of one launch
 hipError_t launch_chunk_scan(const Plan& p, const void* x, const void* B, const void* C,
                              const float* D, const float* dA_cs, const float* dtc,
                              const void* states, void* y, hipStream_t s);
@@ -83,13 +95,17 @@ struct FusedArgs {
   float* ring;          // [batch, H, 2, P * N] fp32 hand-over slots
   uint32_t* flags;      // [batch * H] per-head chunk counters, zero at launch
   uint32_t* ticket;     // workgroup ticket counter, zero at launch
-  uint32_t* status;     // bit 0: a wait for a state was cut off, zero at launch
+  uint32_t* status;     // the status record's word 1: bit 0 set when a wait for a state was cut off
 };
 bool fused_forward_supported(const Plan& p);
 bool fused_forward_preferred(const Plan& p);  // supported and measured faster than the split path
 size_t fused_ring_bytes(const Plan& p);
+int64_t fused_forward_grid(const Plan& p);  // workgroups (= tickets) of one launch
+// The cumsum, also setting words [clear, clear + nclear) to zero and, when
+// stat != nullptr, writing the status record {tag, 0}.
 hipError_t launch_chunk_cumsum_clear(const Plan& p, const float* dt, const float* A, float* dA_cs, float* dtc,
-                                     uint32_t* clear, int64_t nclear, hipStream_t s);
+                                     uint32_t* clear, int64_t nclear, uint32_t* stat, uint32_t tag,
+                                     hipStream_t s);
 hipError_t launch_fused_forward(const Plan& p, const FusedArgs& a, hipStream_t s);
 
 hipError_t launch_conv1d_split(const Plan& p, int K, const void* xbc, const float* w, const float* bias, int act,

@@ -82,12 +82,13 @@ def test_effective_chunk_and_workspace_layout(Q):
 
     cs = 8 * 64 * nc * q * 4
     st = 8 * 64 * nc * 64 * 128 * 2
-    assert ssd.workspace_bytes(d) == up(up(up(cs) + cs) + st)
+    # dA_cumsum, dt_chunked, states, then the 256-byte status record of the call
+    assert ssd.workspace_bytes(d) == up(up(up(cs) + cs) + st) + 256
     # fp32 states for the fp32 io dtype
     d32 = desc(chunk_size=Q, io_dtype="fp32", seqlen=1000)
     nc = -(-1000 // q)
     cs = 8 * 64 * nc * q * 4
-    assert ssd.workspace_bytes(d32) == up(up(up(cs) + cs) + 8 * 64 * nc * 64 * 128 * 4)
+    assert ssd.workspace_bytes(d32) == up(up(up(cs) + cs) + 8 * 64 * nc * 64 * 128 * 4) + 256
 
 
 @pytest.mark.parametrize(
@@ -342,5 +343,24 @@ def test_workspace_covers_the_one_pass_hand_over_area(L):
     cs = 8 * 64 * nc * 256 * 4
     st = 8 * 64 * nc * 64 * 128 * 2
     ring = 8 * 64 * 2 * 64 * 128 * 4
-    sync = up((8 * 64 + 2) * 4)
-    assert ssd.workspace_bytes(d) == up(up(up(cs) + cs) + max(st, up(ring) + sync))
+    sync = up((8 * 64 + 1) * 4)
+    assert ssd.workspace_bytes(d) == up(up(up(cs) + cs) + max(st, up(ring) + sync)) + 256
+
+
+def test_workspace_status_validates_before_any_copy():
+    """ssd_workspace_status rejects a missing or misaligned workspace, a
+    workspace smaller than the descriptor's and a bad descriptor, all before
+    it copies anything from the device."""
+    L = lib()
+    d = desc()
+    n = ssd.workspace_bytes(d)
+    path, bits = ctypes.c_uint32(), ctypes.c_uint32()
+    call = L.ssd_workspace_status
+    fake = ctypes.c_void_p(1 << 40)
+    assert call(ctypes.byref(d), None, n, None, ctypes.byref(path), ctypes.byref(bits)) == NULLP
+    assert call(ctypes.byref(d), fake, n, None, ctypes.byref(path), None) == NULLP
+    assert call(ctypes.byref(d), ctypes.c_void_p((1 << 40) + 128), n, None, ctypes.byref(path),
+                ctypes.byref(bits)) == ALIGN
+    assert call(ctypes.byref(d), fake, n - 256, None, ctypes.byref(path), ctypes.byref(bits)) == WS
+    assert call(ctypes.byref(desc(batch=0)), fake, n, None, ctypes.byref(path), ctypes.byref(bits)) == SHAPE
+    assert call(None, fake, n, None, ctypes.byref(path), ctypes.byref(bits)) == NULLP

@@ -29,18 +29,21 @@ def up(v):
     return -(-v // 256) * 256
 
 
-def sync_words(ws, cfg, Q=256):
-    """The per-head counters, ticket and status the one-pass kernel leaves in
-    the workspace: after dA_cumsum and dt_chunked (each 256-byte aligned), the
-    states region starts with the hand-over ring, then the counters."""
+def sync_words(ws, cfg, desc, Q=256):
+    """The per-head counters and the ticket the one-pass kernel leaves in the
+    workspace (after dA_cumsum and dt_chunked, each 256-byte aligned, the
+    states region starts with the hand-over ring, then the counters), and
+    the status bits of the call's status record (ssd_workspace_status)."""
     nc = -(-cfg.seqlen // Q)
     cs = cfg.batch * cfg.nheads * nc * Q * 4
     st_off = up(up(cs) + cs)
     ring = cfg.batch * cfg.nheads * 2 * cfg.headdim * cfg.dstate * 4
     off = st_off + up(ring)
-    n = cfg.batch * cfg.nheads + 2
+    n = cfg.batch * cfg.nheads + 1
     w = ws[off:off + 4 * n].view(torch.int32).cpu().numpy()
-    return w[:-2], int(w[-2]), int(w[-1]), nc
+    path, status = ssd().workspace_status(desc, ws)
+    assert path == "one-pass"
+    return w[:-1], int(w[-1]), status, nc
 
 
 def test_fused_covers_the_headline_workload():
@@ -86,22 +89,24 @@ def test_fused_edge_shapes(L, P, N, H, G, init):
     full_check(inp, TOL["bf16"], f"fused edge L={L} P={P} N={N} H={H} G={G}", fused=True)
 
 
-@pytest.mark.parametrize("L,H,G,batch", [(1, 4, 1, 2), (257, 4, 2, 2), (3000, 32, 2, 2), (41 * 256 - 243, 4, 1, 2),
-                                         (1100, 64, 1, 8), (2048, 64, 1, 8)])
-def test_fused_chain_completed(L, H, G, batch):
+@pytest.mark.parametrize("L,H,G,batch,N", [(1, 4, 1, 2, 128), (257, 4, 2, 2, 128), (3000, 32, 2, 2, 128),
+                                           (41 * 256 - 243, 4, 1, 2, 128), (1100, 64, 1, 8, 128),
+                                           (2048, 64, 1, 8, 128), (2048, 64, 1, 32, 128), (4096, 32, 1, 32, 64)])
+def test_fused_chain_completed(L, H, G, batch, N):
     """Every head's counter ends at the last hand-over (nc - 1), the tickets
     cover the grid, and no wait was cut off (batch 8 with 64 heads: the
-    headline's 32 chains of 16 heads)."""
-    cfg = BASE.with_(seqlen=L, nheads=H, ngroups=G, batch=batch, init_state=True)
+    headline's 32 chains of 16 heads; batch 32: the same layer over several
+    rounds of workgroups; 32 x 4096 with N = 64: the small-state workload)."""
+    cfg = BASE.with_(seqlen=L, nheads=H, ngroups=G, batch=batch, dstate=N, init_state=True)
     inp = make_inputs(cfg, seed=L + H)
     d = to_dev(inp)
     lib = ssd()
     desc = lib.make_desc(cfg.batch, L, H, cfg.headdim, cfg.dstate, G, "bf16", 0)
     ws = torch.full((lib.workspace_bytes(desc),), 0xA5, dtype=torch.uint8, device=DEV)
-    note(f"[gpu] fused chain counters L={L} H={H} G={G}")
+    note(f"[gpu] fused chain counters B={batch} L={L} H={H} G={G} N={N}")
     lib.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], workspace=ws, fused=True)
     torch.cuda.synchronize()
-    flags, ticket, status, nc = sync_words(ws, cfg)
+    flags, ticket, status, nc = sync_words(ws, cfg, desc)
     assert status == 0
     assert np.all(flags == (nc - 1 if nc > 1 else 0)), flags
     units = cfg.batch * nc * H
