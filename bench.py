@@ -21,7 +21,7 @@ the ramp (about 10% slower on the headline workload).
 
 Timing protocol. Inputs are resident in HBM and the workspace is allocated
 before the timed region. Each of the K timed steps is preceded, outside its
-own pair of HIP events, by a write of --flush-mib MiB of scratch memory
+own pair of HIP events, by a read of --flush-mib MiB of scratch memory
 (default 1024), which evicts the 256 MB last-level cache (MALL) and the L2s,
 so every step reads its inputs from HBM. The headline is the median of those
 flushed per-step times; the back-to-back (warm) rate over the same K steps
@@ -62,6 +62,7 @@ def parse():
     ap.add_argument("--device-warm-ms", type=float, default=500.0,
                     help="untimed forward passes before the warm-up steps, to reach steady clocks")
     ap.add_argument("--no-one-pass", action="store_true", help="skip the one-pass path measurement")
+    ap.add_argument("--one-pass-steps", type=int, default=10, help="flushed steps per path and round in one_pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step, packed-sequence and convolution measurements")
     ap.add_argument("--cpu-sample-seqs", type=int, default=8)
@@ -69,7 +70,7 @@ def parse():
                     help="also run a plain fp32 elementwise copy (negation) of MIB MiB, "
                          "the reference kernel for scaling rocprofv3 byte counters")
     ap.add_argument("--flush-mib", type=int, default=1024,
-                    help="scratch written before every timed step (0: no flush, back-to-back steps only)")
+                    help="scratch read before every timed step (0: no flush, back-to-back steps only)")
     ap.add_argument("--no-workloads", action="store_true", help="skip the other workloads' entries")
     ap.add_argument("--workload-steps", type=int, default=20)
     ap.add_argument("--cpu-workers", type=int, default=0,
@@ -123,18 +124,21 @@ def forward_kernels(cfg, path):
 
 
 class Flusher:
-    """Writes `mib` MiB of scratch memory on the current stream: more than the
-    256 MB last-level cache and the L2s hold, so the next kernel reads HBM."""
+    """Reads `mib` MiB of scratch memory on the current stream (a sum over
+    it): more than the 256 MB last-level cache and the L2s hold, so the next
+    kernel finds none of its data in them and reads HBM. A read, not a write:
+    a write would leave the caches full of dirty lines, and their write-back
+    would be charged to the next kernel."""
 
     def __init__(self, dev, mib):
         import torch
-        self.buf = torch.empty(mib << 18, dtype=torch.float32, device=dev) if mib > 0 else None
-        self.k = 0
+        self.buf = torch.ones(mib << 18, dtype=torch.float32, device=dev) if mib > 0 else None
+        self.out = torch.empty((), dtype=torch.float32, device=dev) if mib > 0 else None
 
     def __call__(self):
         if self.buf is not None:
-            self.k += 1
-            self.buf.fill_(float(self.k & 1023))
+            import torch
+            torch.sum(self.buf, 0, out=self.out)
 
 
 def timed_steps(fn, steps, stream, flush=None):
@@ -634,9 +638,9 @@ def main():
 
     one_pass = None
     if not args.no_one_pass and cfg.io_dtype == "bf16":
-        one_pass = [one_pass_measure(wl, 10, flush)]
+        one_pass = [one_pass_measure(wl, args.one_pass_steps, flush)]
         big = Workload(cfg.with_(name=f"{cfg.name} x4 batch", batch=4 * cfg.batch), 104, dev, args.chunk)
-        one_pass.append(one_pass_measure(big, 10, flush))
+        one_pass.append(one_pass_measure(big, args.one_pass_steps, flush))
         del big
         torch.cuda.empty_cache()
 
@@ -674,7 +678,7 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "nheads": cfg.nheads,
                    "headdim": cfg.headdim, "dstate": cfg.dstate, "ngroups": cfg.ngroups,
                    "chunk": wl.Q, "init_state": cfg.init_state, "path": path},
-        "timing": {"protocol": f"median of {args.steps} steps, each after a {args.flush_mib} MiB scratch write "
+        "timing": {"protocol": f"median of {args.steps} steps, each after a {args.flush_mib} MiB scratch read "
                                "outside its HIP event pair" if flush else "back-to-back steps",
                    "p10_ms": round(quantile(ts, 0.1) / 1e3, 4), "p90_ms": round(quantile(ts, 0.9) / 1e3, 4),
                    "warm_ms_per_step": round(warm_us / 1e3, 4),

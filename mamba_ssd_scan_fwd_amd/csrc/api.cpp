@@ -85,6 +85,12 @@ ssd_status_t make_plan(const ssd_desc_t* d, Plan* p) {
   int Q = d->chunk_size;
   if (Q == 0) Q = default_chunk(*d);
   if (Q != 64 && Q != 128 && Q != 256) return SSD_ERR_UNSUPPORTED;
+  // headdim 128 on the matrix cores: the intra-chunk kernel's register tiles
+  // do not fit at chunk length 256 (dstate >= 64) or 64 (dstate 256); those
+  // instantiations would spill to scratch, so the pairs are refused
+  if (d->io_dtype == SSD_DTYPE_BF16 && d->headdim == 128 &&
+      ((Q == 256 && d->dstate >= 64) || (Q == 64 && d->dstate == 256)))
+    return SSD_ERR_UNSUPPORTED;
   const int64_t nc = (d->seqlen + Q - 1) / Q;
   // element counts of the largest arrays must stay well inside 64-bit byte math
   if (d->batch * d->seqlen > kMaxElems / (d->nheads * d->headdim)) return SSD_ERR_BAD_SHAPE;

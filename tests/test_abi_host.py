@@ -107,6 +107,9 @@ def test_effective_chunk_and_workspace_layout(Q):
         (dict(chunk_size=100), UNSUP),
         (dict(chunk_size=512), UNSUP),
         (dict(io_dtype=7), UNSUP),
+        (dict(headdim=128, chunk_size=256), UNSUP),              # bf16 register tiles do not fit
+        (dict(headdim=128, dstate=64, chunk_size=256), UNSUP),
+        (dict(headdim=128, dstate=256, chunk_size=64), UNSUP),
     ],
 )
 def test_bad_descriptors_are_rejected(kw, code):
@@ -364,3 +367,13 @@ def test_workspace_status_validates_before_any_copy():
     assert call(ctypes.byref(d), fake, n - 256, None, ctypes.byref(path), ctypes.byref(bits)) == WS
     assert call(ctypes.byref(desc(batch=0)), fake, n, None, ctypes.byref(path), ctypes.byref(bits)) == SHAPE
     assert call(None, fake, n, None, ctypes.byref(path), ctypes.byref(bits)) == NULLP
+
+
+@pytest.mark.parametrize("kw", [dict(headdim=128, dstate=32, chunk_size=256), dict(headdim=128, dstate=128, chunk_size=64),
+                                dict(headdim=128, dstate=256, chunk_size=128), dict(headdim=128, dstate=256),
+                                dict(headdim=128, chunk_size=256, io_dtype="fp32")])
+def test_headdim_128_chunk_sizes_that_fit_are_accepted(kw):
+    lib()
+    d = desc(**kw)
+    assert ssd.workspace_bytes(d) > 0
+    assert ssd.effective_chunk_size(d) == (kw.get("chunk_size") or 128)
