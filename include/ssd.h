@@ -86,7 +86,9 @@ typedef enum {
   SSD_ERR_ALIGNMENT = 4,    /* a base pointer is misaligned                    */
   SSD_ERR_WORKSPACE = 5,    /* workspace given but smaller than required       */
   SSD_ERR_ALIAS = 6,        /* an output overlaps an input it must not overlap */
-  SSD_ERR_HIP = 7           /* the HIP runtime reported an error               */
+  SSD_ERR_HIP = 7,          /* the HIP runtime reported an error               */
+  SSD_ERR_SCRATCH_LIMIT = 8 /* ssd_forward_noalloc: the problem needs more
+                               workspace than its fixed scratch array holds     */
 } ssd_status_t;
 
 /* Path a whole-forward call took, as recorded in its workspace
@@ -251,6 +253,26 @@ SSD_API ssd_status_t ssd_forward_split(const ssd_desc_t* desc,
  * (ssd_forward_varlen) use no bounded wait and keep no record. */
 SSD_API ssd_status_t ssd_workspace_status(const ssd_desc_t* desc, const void* workspace, size_t workspace_bytes,
                                           void* stream, uint32_t* path, uint32_t* status);
+
+/* The whole forward pass of ssd_forward for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): no workspace argument, and nothing is allocated;
+ * the workspace comes from a fixed scratch array of 256 MiB that the library
+ * holds on every GPU it runs this entry point on, until the process ends.
+ * Arguments other than the workspace, the path taken, the results and the
+ * errors are those of ssd_forward (same bits); problems whose
+ * ssd_workspace_bytes() exceeds 256 MiB return SSD_ERR_SCRATCH_LIMIT before
+ * anything is enqueued (the headline layer shape fits up to batch 28 at
+ * L = 2048). All calls on one GPU share that GPU's array: calls that may
+ * overlap in time on one GPU (several streams or host threads) race and must
+ * be ordered by the caller. The first call on each device looks the array's
+ * device address up (a HIP runtime query, no allocation). */
+SSD_API ssd_status_t ssd_forward_noalloc(const ssd_desc_t* desc,
+                                 const void* x, const float* dt, const float* A,
+                                 const void* B, const void* C, const float* D,
+                                 const float* init_state,
+                                 void* y, float* final_state,
+                                 void* stream);
 
 /* ---- the steps of the chunked path, each callable on its own ------------ */
 

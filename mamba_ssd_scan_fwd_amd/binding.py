@@ -24,6 +24,7 @@ __all__ = [
     "workspace_bytes",
     "workspace_status",
     "forward",
+    "forward_noalloc",
     "chunk_cumsum",
     "chunk_state",
     "cumsum_chunk_state",
@@ -46,6 +47,7 @@ EXPORTED_SYMBOLS = (
     "ssd_forward_fused",
     "ssd_forward_split",
     "ssd_workspace_status",
+    "ssd_forward_noalloc",
     "ssd_chunk_cumsum",
     "ssd_chunk_state",
     "ssd_cumsum_chunk_state",
@@ -125,6 +127,8 @@ def load_library():
         lib.ssd_workspace_status.argtypes = [dp, vp, sz, vp, ctypes.POINTER(ctypes.c_uint32),
                                              ctypes.POINTER(ctypes.c_uint32)]
         lib.ssd_workspace_status.restype = ctypes.c_int
+        lib.ssd_forward_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.ssd_forward_noalloc.restype = ctypes.c_int
         lib.ssd_chunk_cumsum.argtypes = [dp, vp, vp, vp, vp, vp]
         lib.ssd_chunk_cumsum.restype = ctypes.c_int
         lib.ssd_chunk_state.argtypes = [dp, vp, vp, vp, vp, vp, vp]
@@ -292,6 +296,42 @@ def forward(x, dt, A, B, C, D=None, init_state=None, *, chunk_size: int = 0,
         ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state),
         _ptr(y), _ptr(final_state), _ptr(workspace), ctypes.c_size_t(wsize), _stream(stream, dev))
     _check(st, name)
+    return y, final_state
+
+
+def forward_noalloc(x, dt, A, B, C, D=None, init_state=None, *, chunk_size: int = 0,
+                    return_final_state: bool = True, y=None, final_state=None, dt_pre=None, stream=None):
+    """ssd_forward_noalloc: the forward pass of ``forward`` with the
+    workspace taken from the library's fixed per-GPU scratch (256 MiB); the
+    library allocates nothing. ``y`` and ``final_state`` are allocated here
+    when not given (pass them to keep the call allocation-free end to end).
+    Returns (y, final_state or None)."""
+    dev = x.device
+    _need(x, "x", device=dev)
+    io = x.dtype
+    bsz, L, H, P = x.shape
+    _need(B, "B", io, dev)
+    G, N = B.shape[2], B.shape[3]
+    _need(C, "C", io, dev, B.shape)
+    _need(dt, "dt", torch.float32, dev, (bsz, L, H))
+    _need(A, "A", torch.float32, dev, (H,))
+    if D is not None:
+        _need(D, "D", torch.float32, dev, (H,))
+    if init_state is not None:
+        _need(init_state, "init_state", torch.float32, dev, (bsz, H, P, N))
+    desc = _desc_from(x, B, chunk_size, dt_pre)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", io, dev, x.shape)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _need(final_state, "final_state", torch.float32, dev, (bsz, H, P, N))
+    st = load_library().ssd_forward_noalloc(
+        ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state),
+        _ptr(y), _ptr(final_state), _stream(stream, dev))
+    _check(st, "ssd_forward_noalloc")
     return y, final_state
 
 

@@ -342,6 +342,8 @@ const char* ssd_status_string(int status) {
     case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace smaller than ssd_workspace_bytes()";
     case SSD_ERR_ALIAS: return "SSD_ERR_ALIAS: an output overlaps an input";
     case SSD_ERR_HIP: return "SSD_ERR_HIP: the HIP runtime reported an error";
+    case SSD_ERR_SCRATCH_LIMIT:
+      return "SSD_ERR_SCRATCH_LIMIT: the problem needs more workspace than the 256 MiB no-allocation scratch";
     default: return "unknown ssd_status_t";
   }
 }

@@ -18,7 +18,7 @@ from mamba_ssd_scan_fwd_amd.binding import SSDDesc, make_desc
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssd.h")
 
-OK, NULLP, SHAPE, UNSUP, ALIGN, WS, ALIAS, HIP = range(8)
+OK, NULLP, SHAPE, UNSUP, ALIGN, WS, ALIAS, HIP, SCRATCH = range(9)
 
 
 def lib():
@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib()
-    for code in range(8):
+    for code in range(9):
         assert ssd.status_string(code).startswith(["SSD_OK", "SSD_ERR"][code > 0])
     assert "unknown" in ssd.status_string(99)
 
@@ -367,6 +367,26 @@ def test_workspace_status_validates_before_any_copy():
     assert call(ctypes.byref(d), fake, n - 256, None, ctypes.byref(path), ctypes.byref(bits)) == WS
     assert call(ctypes.byref(desc(batch=0)), fake, n, None, ctypes.byref(path), ctypes.byref(bits)) == SHAPE
     assert call(None, fake, n, None, ctypes.byref(path), ctypes.byref(bits)) == NULLP
+
+
+def test_no_allocation_entry_rejects_before_any_device_call():
+    """ssd_forward_noalloc checks the descriptor and the size of its fixed
+    scratch before it touches the device: a bad descriptor gives the
+    descriptor's error, a problem needing more than 256 MiB of workspace
+    SSD_ERR_SCRATCH_LIMIT (fake, never dereferenced pointers)."""
+    L = lib()
+    fake = [ctypes.c_void_p((1 << 40) + 4096 * k) for k in range(8)]
+
+    def call(d):
+        return L.ssd_forward_noalloc(ctypes.byref(d), *fake[:8], None, None)
+
+    assert call(desc(batch=0)) == SHAPE
+    assert call(desc(dstate=96)) == UNSUP
+    big = desc(batch=4, seqlen=8192, nheads=128, headdim=64, dstate=256, ngroups=8)  # the large-state workload
+    assert ssd.workspace_bytes(big) > (256 << 20)
+    assert call(big) == SCRATCH
+    assert "256 MiB" in ssd.status_string(SCRATCH)
+    assert L.ssd_forward_noalloc(None, *fake[:8], None, None) == NULLP
 
 
 @pytest.mark.parametrize("kw", [dict(headdim=128, dstate=32, chunk_size=256), dict(headdim=128, dstate=128, chunk_size=64),
