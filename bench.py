@@ -106,6 +106,12 @@ def algorithmic_model(cfg, Q, io_bytes):
     # one-pass kernel (steps 2-5 after the cumsum): x in, y out, B and C,
     # dA_cumsum and dt_chunked once, every hand-over state written and read
     # once in fp32, the initial and final states
+    # segmented state passing: the plain chain's bytes plus each segment's
+    # fp32 aggregate written once and read by every later segment
+    nseg = -(-nc // 32)
+    agg = b * H * P * N * 4
+    out["state_passing_seg"] = dict(bytes=out["state_passing"]["bytes"] + agg * (nseg - 1) * (1 + nseg / 2),
+                                    flops=out["state_passing"]["flops"])
     hand = 2 * b * H * (nc - 1) * P * N * 4
     out["one_pass"] = dict(bytes=2 * T * H * P * s + 2 * T * G * N * s + 2 * cs + hand
                            + b * H * P * N * 4 * (2 if cfg.init_state else 1),
@@ -118,6 +124,8 @@ def forward_kernels(cfg, path):
     """The kernels one ssd_forward launches on `path`, by name in the model."""
     if path == "one-pass":
         return ["chunk_cumsum", "one_pass"]
+    if path == "split-segmented":
+        return ["cumsum_chunk_state", "state_passing_seg", "chunk_scan"]
     if cfg.io_dtype != "bf16":
         return ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
     return ["cumsum_chunk_state", "state_passing", "chunk_scan"]
@@ -391,12 +399,28 @@ class Workload:
         self.hT = torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device=dev)
         self.stream = torch.cuda.current_stream(dev)
         self.io_bytes = 2 if cfg.io_dtype == "bf16" else 4
+        self._args = None
 
-    def forward(self, **kw):
+    def forward(self, fused=False, split=False):
+        """One whole forward pass: a direct call of the C entry point with the
+        arguments marshalled once (the checked binding costs tens of
+        microseconds of Python per call, enough to starve back-to-back
+        steps of the smaller workloads)."""
+        import ctypes
+
         import mamba_ssd_scan_fwd_amd as ssd
-        d = self.d
-        ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["init_state"], chunk_size=self.chunk,
-                    y=self.y, final_state=self.hT, workspace=self.ws, **kw)
+        if self._args is None:
+            P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+            d = self.d
+            self._args = (ctypes.byref(self.desc), P(d["x"]), P(d["dt"]), P(d["A"]), P(d["B"]), P(d["C"]), P(d["D"]),
+                          P(d["init_state"]), P(self.y), P(self.hT), P(self.ws),
+                          ctypes.c_size_t(self.ws.numel()), ctypes.c_void_p(self.stream.cuda_stream))
+            lib = ssd.load_library()
+            self._fns = {(False, False): lib.ssd_forward, (True, False): lib.ssd_forward_fused,
+                         (False, True): lib.ssd_forward_split}
+        st = self._fns[(fused, split)](*self._args)
+        if st != 0:
+            raise ssd.SSDError(st, "forward")
 
     def path(self):
         """The path ssd_forward takes here (its workspace record), after one call."""
@@ -464,6 +488,14 @@ def kernel_times(wl, path, reps, flush):
         ts_cs, _ = timed_steps(fns["chunk_cumsum"], reps, wl.stream, flush)
         t_all, t_cs = statistics.median(ts_all), statistics.median(ts_cs)
         return {"chunk_cumsum": t_cs, "one_pass": t_all - t_cs}, True
+    if path == "split-segmented":
+        # the segmented state passing has no step entry point of its own
+        # (the step entry runs the plain chain): whole pass minus the others
+        times, _ = kernel_times(wl, "split", reps, flush)
+        ts_all, _ = timed_steps(wl.forward, reps, wl.stream, flush)
+        times["state_passing_seg"] = statistics.median(ts_all) - times["cumsum_chunk_state"] - times["chunk_scan"]
+        del times["state_passing"]
+        return times, True
     calls = [fns[n] for n in names]
     for _ in range(2):
         for fn in calls:
