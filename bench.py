@@ -333,18 +333,27 @@ def varlen_measure(cfg, steps, dev, flush):
     S = len(lengths)
     y = torch.empty_like(d["x"])
     hT = torch.empty((S, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device=dev)
+    h0 = torch.zeros_like(hT)
     stream = torch.cuda.current_stream(dev)
 
-    def run():
-        ssd.forward_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], cu_seqlens=cu, y=y, final_states=hT)
+    def timed(init):
+        # without initial states: fixed chunks of the packed stream; with
+        # them: chunks per sequence
+        def run():
+            ssd.forward_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], cu_seqlens=cu, y=y,
+                               final_states=hT, init_states=h0 if init else None)
 
-    for _ in range(3):
-        run()
-    ts, _ = timed_steps(run, steps, stream, flush)
-    us = statistics.median(ts)
+        for _ in range(3):
+            run()
+        ts, _ = timed_steps(run, steps, stream, flush)
+        return statistics.median(ts)
+
+    us = timed(False)
+    us_init = timed(True)
     return {"workload": f"{S} packed sequences, {T} tokens in all (lengths {int(lengths.min())}..{int(lengths.max())}), "
                         f"{cfg.name} layer", "num_seqs": S, "median_us": round(us, 2),
-            "tokens_per_s": round(T / (us * 1e-6), 1)}
+            "tokens_per_s": round(T / (us * 1e-6), 1),
+            "with_initial_states_median_us": round(us_init, 2)}
 
 
 def conv_measure(cfg, steps, dev, flush):

@@ -250,7 +250,8 @@ SSD_API ssd_status_t ssd_forward_split(const ssd_desc_t* desc,
  *              designed.
  * Returns SSD_ERR_NULL_POINTER, SSD_ERR_ALIGNMENT, SSD_ERR_WORKSPACE for a
  * bad argument, SSD_ERR_HIP when a copy fails. Packed sequences
- * (ssd_forward_varlen) use no bounded wait and keep no record. */
+ * (ssd_forward_varlen) keep their record elsewhere in their workspace: read
+ * it with ssd_workspace_status_varlen. */
 SSD_API ssd_status_t ssd_workspace_status(const ssd_desc_t* desc, const void* workspace, size_t workspace_bytes,
                                           void* stream, uint32_t* path, uint32_t* status);
 
@@ -333,6 +334,24 @@ SSD_API ssd_status_t ssd_workspace_bytes_varlen(const ssd_desc_t* desc, int64_t 
  * runs the recurrence of ssd_forward on its own, from init_states[s] (zeros
  * when init_states is NULL) to final_states[s] (not written when NULL). No
  * state crosses a sequence boundary; no padding is needed.
+ *
+ * Two ways of cutting the work:
+ *  - bf16 io and init_states NULL: fixed chunks of Q tokens over the packed
+ *    stream, as for one sequence of T tokens, so a chunk may hold the ends
+ *    and starts of several sequences. A start adds -128 to the chunk's dA
+ *    cumsum from its token on, so every decay factor across it is
+ *    exp(<= -128) = 0 in fp32 (dt*A <= 0): no state or input crosses the
+ *    boundary. Each sequence's final state is then its last chunk's local
+ *    state up to its last token, plus the decayed fp32 state entering that
+ *    chunk. The work is that of ssd_forward on [1, T] (state passing cut
+ *    into segments when the chunks are many), plus one partial chunk state
+ *    per sequence for the final states. After k starts within one chunk the
+ *    cumsum is near -128 k, so the decays of the sequence that follows carry
+ *    a relative rounding of up to 2^-17 k (below bf16's 2^-9 for k < 256).
+ *  - fp32 io, or init_states given: chunks per sequence (a sequence's first
+ *    chunk starts at its first token), each sequence's chain of states
+ *    starting from its own initial state; up to ceil(T/Q) + num_seqs
+ *    chunks.
  *   cu_seqlens   [num_seqs + 1] int32, DEVICE pointer: 0 = cu[0] <= cu[1]
  *                <= ... <= cu[num_seqs] = T. Offsets are clamped into [0, T]
  *                on the device, so an invalid array gives wrong values but no
@@ -342,12 +361,22 @@ SSD_API ssd_status_t ssd_workspace_bytes_varlen(const ssd_desc_t* desc, int64_t 
  *   pointer; other overlaps are rejected).
  *   workspace    nullable, at least ssd_workspace_bytes_varlen() bytes.
  * Errors as ssd_forward; SSD_ERR_BAD_SHAPE also when desc->batch != 1,
- * num_seqs < 1 or T >= 2^31. */
+ * num_seqs < 1 or T >= 2^31. A segmented state passing uses the bounded
+ * waits described at ssd_workspace_status and leaves the same record, read
+ * with ssd_workspace_status_varlen. */
 SSD_API ssd_status_t ssd_forward_varlen(const ssd_desc_t* desc, const int32_t* cu_seqlens, int64_t num_seqs,
                                 const void* x, const float* dt, const float* A,
                                 const void* B, const void* C, const float* D,
                                 const float* init_states, void* y, float* final_states,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Status of the last ssd_forward_varlen call that ran with `workspace`,
+ * this descriptor and num_seqs: as ssd_workspace_status (same path values
+ * and bits; SSD_PATH_SPLIT for a plain state passing, either cut of the
+ * work). Workspace at least ssd_workspace_bytes_varlen() bytes. */
+SSD_API ssd_status_t ssd_workspace_status_varlen(const ssd_desc_t* desc, int64_t num_seqs, const void* workspace,
+                                                 size_t workspace_bytes, void* stream, uint32_t* path,
+                                                 uint32_t* status);
 
 /* ---- the short causal convolution before the SSM --------------------------- */
 

@@ -30,5 +30,7 @@ from .binding import (  # noqa: F401
     state_passing,
     status_string,
     workspace_bytes,
+    workspace_bytes_varlen,
     workspace_status,
+    workspace_status_varlen,
 )

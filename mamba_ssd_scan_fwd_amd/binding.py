@@ -22,7 +22,9 @@ __all__ = [
     "status_string",
     "effective_chunk_size",
     "workspace_bytes",
+    "workspace_bytes_varlen",
     "workspace_status",
+    "workspace_status_varlen",
     "forward",
     "forward_noalloc",
     "chunk_cumsum",
@@ -56,6 +58,7 @@ EXPORTED_SYMBOLS = (
     "ssd_decode_step",
     "ssd_workspace_bytes_varlen",
     "ssd_forward_varlen",
+    "ssd_workspace_status_varlen",
     "ssd_conv1d_split",
 )
 
@@ -127,6 +130,9 @@ def load_library():
         lib.ssd_workspace_status.argtypes = [dp, vp, sz, vp, ctypes.POINTER(ctypes.c_uint32),
                                              ctypes.POINTER(ctypes.c_uint32)]
         lib.ssd_workspace_status.restype = ctypes.c_int
+        lib.ssd_workspace_status_varlen.argtypes = [dp, ctypes.c_int64, vp, sz, vp, ctypes.POINTER(ctypes.c_uint32),
+                                                    ctypes.POINTER(ctypes.c_uint32)]
+        lib.ssd_workspace_status_varlen.restype = ctypes.c_int
         lib.ssd_forward_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.ssd_forward_noalloc.restype = ctypes.c_int
         lib.ssd_chunk_cumsum.argtypes = [dp, vp, vp, vp, vp, vp]
@@ -196,6 +202,13 @@ def effective_chunk_size(desc: SSDDesc) -> int:
 def workspace_bytes(desc: SSDDesc) -> int:
     n = ctypes.c_size_t(0)
     _check(load_library().ssd_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "ssd_workspace_bytes")
+    return int(n.value)
+
+
+def workspace_bytes_varlen(desc: SSDDesc, num_seqs: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().ssd_workspace_bytes_varlen(ctypes.byref(desc), ctypes.c_int64(num_seqs), ctypes.byref(n)),
+           "ssd_workspace_bytes_varlen")
     return int(n.value)
 
 
@@ -355,6 +368,18 @@ def workspace_status(desc: SSDDesc, workspace, stream=None):
     return PATH_NAMES.get(int(path.value), str(path.value)), int(bits.value)
 
 
+def workspace_status_varlen(desc: SSDDesc, num_seqs: int, workspace, stream=None):
+    """workspace_status for the workspace of a forward_varlen call with
+    ``desc`` and ``num_seqs`` sequences."""
+    path = ctypes.c_uint32(0)
+    bits = ctypes.c_uint32(0)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().ssd_workspace_status_varlen(
+        ctypes.byref(desc), ctypes.c_int64(num_seqs), _ptr(workspace), ctypes.c_size_t(nbytes),
+        _stream(stream, workspace.device), ctypes.byref(path), ctypes.byref(bits)), "ssd_workspace_status_varlen")
+    return PATH_NAMES.get(int(path.value), str(path.value)), int(bits.value)
+
+
 def _chunk_shape(desc):
     q = effective_chunk_size(desc)
     nc = -(-desc.seqlen // q)
@@ -485,8 +510,9 @@ def forward_varlen(x, dt, A, B, C, D=None, *, cu_seqlens, init_states=None, chun
                    dt_pre=None, stream=None):
     """Packed variable-length sequences: x [1, T, H, P], dt [1, T, H],
     B/C [1, T, G, N]; sequence s is tokens [cu_seqlens[s], cu_seqlens[s+1])
-    (cu_seqlens: int32 device tensor [S+1]). Returns (y, final_states [S, H, P, N]
-    or None)."""
+    (cu_seqlens: int32 device tensor [S+1]). Without init_states the packed
+    stream is cut into fixed chunks (sequences may share a chunk); with them,
+    into chunks per sequence. Returns (y, final_states [S, H, P, N] or None)."""
     dev = x.device
     _need(x, "x", device=dev)
     io = x.dtype
@@ -509,12 +535,9 @@ def forward_varlen(x, dt, A, B, C, D=None, *, cu_seqlens, init_states=None, chun
         y = torch.empty_like(x)
     if final_states is None and return_final_states:
         final_states = torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
-    n = ctypes.c_size_t()
     lib = load_library()
-    _check(lib.ssd_workspace_bytes_varlen(ctypes.byref(desc), ctypes.c_int64(S), ctypes.byref(n)),
-           "ssd_workspace_bytes_varlen")
     if workspace is None:
-        workspace = torch.empty(n.value, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(workspace_bytes_varlen(desc, S), dtype=torch.uint8, device=dev)
     _check(lib.ssd_forward_varlen(ctypes.byref(desc), _ptr(cu_seqlens), ctypes.c_int64(S), _ptr(x), _ptr(dt),
                                   _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_states), _ptr(y),
                                   _ptr(final_states), _ptr(workspace),

@@ -173,6 +173,64 @@ ssd_status_t make_varlen_plan(const ssd_desc_t* d, int64_t num_seqs, Plan* p) {
   return SSD_OK;
 }
 
+// Packed sequences without initial states: fixed chunks of the packed stream
+// (the plan of one sequence of T tokens), plus one end window per sequence.
+// Workspace: dA_cumsum, dt_chunked, states of the chunks; the segmented
+// state-passing scratch where it applies; dA_cumsum, dt_chunked, states of
+// the windows; the per-token sequence-start flags; the window table; the
+// per-chunk crossing sequence.
+struct PackedLayout {
+  size_t cs_off, dt_off, st_off, sp_off, wcs_off, wdt_off, wst_off, seg_off, wtab_off, xend_off, total;
+};
+Plan packed_chunk_plan(const Plan& pv) {
+  Plan pm = pv;
+  pm.nc = (pv.L + pv.Q - 1) / pv.Q;
+  pm.ctab = nullptr;
+  pm.seqtab = nullptr;
+  pm.nseq = 0;
+  return pm;
+}
+PackedLayout packed_layout(const Plan& pm, int64_t S) {
+  PackedLayout w;
+  const size_t io = pm.io_bytes();
+  const size_t cs = size_t(pm.H * pm.nc * pm.Q) * 4, st = size_t(pm.H * pm.nc * pm.P * pm.N) * io;
+  const size_t wcs = size_t(pm.H * S * pm.Q) * 4, wst = size_t(pm.H * S * pm.P * pm.N) * io;
+  w.cs_off = 0;
+  w.dt_off = align_up(cs, kWsAlign);
+  w.st_off = align_up(w.dt_off + cs, kWsAlign);
+  size_t end = align_up(w.st_off + st, kWsAlign);
+  w.sp_off = 0;
+  if (seg_state_passing_applies(pm)) {
+    w.sp_off = end;
+    end = align_up(w.sp_off + seg_scratch_layout(pm, nullptr).bytes, kWsAlign);
+  }
+  w.wcs_off = end;
+  w.wdt_off = align_up(w.wcs_off + wcs, kWsAlign);
+  w.wst_off = align_up(w.wdt_off + wcs, kWsAlign);
+  w.seg_off = align_up(w.wst_off + wst, kWsAlign);
+  w.wtab_off = align_up(w.seg_off + size_t(pm.L), kWsAlign);
+  w.xend_off = align_up(w.wtab_off + size_t(S) * sizeof(ChunkInfo), kWsAlign);
+  w.total = align_up(w.xend_off + size_t(pm.nc) * sizeof(int32_t), kWsAlign);
+  return w;
+}
+
+// The varlen workspace holds either path's layout (which one runs depends on
+// whether initial states are given), then the status record.
+struct VarlenLayout {
+  WsLayout ws;      // chunks per sequence
+  Plan pm;          // fixed chunks of the packed stream
+  PackedLayout pl;  // ... and their layout
+  size_t stat_off, total;
+};
+VarlenLayout varlen_layout(const Plan& p, int64_t num_seqs) {
+  VarlenLayout v;
+  v.ws = ws_layout(p, true);
+  v.pm = packed_chunk_plan(p);
+  v.pl = packed_layout(v.pm, num_seqs);
+  v.stat_off = align_up(v.ws.total > v.pl.total ? v.ws.total : v.pl.total, kWsAlign);
+  v.total = v.stat_off + kStatBytes;
+  return v;
+}
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -325,6 +383,66 @@ ssd_status_t enqueue_forward(const Plan& p, bool fused, const void* x, const flo
   return from_hip(e);
 }
 
+// Read a status record and, for the paths with bounded waits, check that
+// every hand-over happened: stat the record; sync the one-pass counters and
+// ticket (nullptr where that path cannot run); seg the segmented
+// state-passing scratch (nullptr where it is not laid out).
+ssd_status_t read_status(const Plan& p, const char* stat, const char* sync, const char* seg, hipStream_t s,
+                         uint32_t* path, uint32_t* status) {
+  // Copy n 32-bit words from the workspace and wait for them.
+  auto fetch = [&](uint32_t* dst, const void* src, size_t n) {
+    hipError_t e = hipMemcpyAsync(dst, src, n * sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e == hipSuccess;
+  };
+  // Every word of [src, src + n) equals want(i), read in pieces of kPiece words.
+  constexpr int64_t kPiece = 1024;
+  uint32_t buf[kPiece];
+  bool hip_ok = true;
+  auto all_equal = [&](const uint32_t* src, int64_t n, auto want) {
+    for (int64_t i0 = 0; i0 < n; i0 += kPiece) {
+      const int64_t m = n - i0 < kPiece ? n - i0 : kPiece;
+      if (!fetch(buf, src + i0, size_t(m))) {
+        hip_ok = false;
+        return false;
+      }
+      for (int64_t i = 0; i < m; ++i)
+        if (buf[i] != want(i0 + i)) return false;
+    }
+    return true;
+  };
+
+  uint32_t rec[2] = {0, 0};
+  if (!fetch(rec, stat, 2)) return SSD_ERR_HIP;
+  uint32_t bits = rec[1] & (SSD_STATUS_WAIT_CUT_OFF_ONE_PASS | SSD_STATUS_WAIT_CUT_OFF_SEGMENTED);
+  uint32_t tag = rec[0];
+  if (tag == kPathOnePass && sync != nullptr) {
+    // every head's counter at its last hand-over, one ticket per workgroup
+    const uint32_t* sw = reinterpret_cast<const uint32_t*>(sync);
+    const uint32_t last = p.nc > 1 ? uint32_t(p.nc - 1) : 0u;
+    const bool flags_ok = all_equal(sw, p.batch * p.H, [&](int64_t) { return last; });
+    const uint32_t tickets = uint32_t(fused_forward_grid(p));
+    const bool ticket_ok = flags_ok && all_equal(sw + p.batch * p.H, 1, [&](int64_t) { return tickets; });
+    if (!flags_ok || !ticket_ok) bits |= SSD_STATUS_CHAIN_INCOMPLETE;
+  } else if (tag == kPathSplitSegmented && seg != nullptr) {
+    // every segment but the last of each (chain, slice) published, one ticket per workgroup
+    const SegScratch sc = seg_scratch_layout(p, const_cast<char*>(seg));
+    const int64_t nseg = sc.nseg;
+    const bool flags_ok = all_equal(sc.flags, sc.chains * sc.nslice * nseg,
+                                    [&](int64_t i) { return (i % nseg) + 1 < nseg ? 1u : 0u; });
+    const uint32_t tickets = uint32_t(seg_state_passing_grid(p));
+    const bool ticket_ok = flags_ok && all_equal(sc.ticket, 1, [&](int64_t) { return tickets; });
+    if (!flags_ok || !ticket_ok) bits |= SSD_STATUS_CHAIN_INCOMPLETE;
+  } else if (tag != kPathSplit) {
+    tag = SSD_PATH_NONE;
+    bits = SSD_STATUS_NO_RECORD;
+  }
+  if (!hip_ok) return SSD_ERR_HIP;
+  if (path != nullptr) *path = tag;
+  *status = bits;
+  return SSD_OK;
+}
+
 }  // namespace
 }  // namespace ssd
 
@@ -418,61 +536,10 @@ ssd_status_t ssd_workspace_status(const ssd_desc_t* desc, const void* workspace,
   if (!ssd::aligned(workspace, ssd::kWsAlign)) return SSD_ERR_ALIGNMENT;
   const ssd::WsLayout ws = ssd::ws_layout(p);
   if (workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const char* w = static_cast<const char*>(workspace);
-
-  // Copy n 32-bit words from the workspace and wait for them.
-  auto fetch = [&](uint32_t* dst, const void* src, size_t n) {
-    hipError_t e = hipMemcpyAsync(dst, src, n * sizeof(uint32_t), hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    return e == hipSuccess;
-  };
-  // Every word of [src, src + n) equals want(i), read in pieces of kPiece words.
-  constexpr int64_t kPiece = 1024;
-  uint32_t buf[kPiece];
-  bool hip_ok = true;
-  auto all_equal = [&](const uint32_t* src, int64_t n, auto want) {
-    for (int64_t i0 = 0; i0 < n; i0 += kPiece) {
-      const int64_t m = n - i0 < kPiece ? n - i0 : kPiece;
-      if (!fetch(buf, src + i0, size_t(m))) {
-        hip_ok = false;
-        return false;
-      }
-      for (int64_t i = 0; i < m; ++i)
-        if (buf[i] != want(i0 + i)) return false;
-    }
-    return true;
-  };
-
-  uint32_t rec[2] = {0, 0};
-  if (!fetch(rec, w + ws.stat_off, 2)) return SSD_ERR_HIP;
-  uint32_t bits = rec[1] & (SSD_STATUS_WAIT_CUT_OFF_ONE_PASS | SSD_STATUS_WAIT_CUT_OFF_SEGMENTED);
-  uint32_t tag = rec[0];
-  if (tag == ssd::kPathOnePass && ssd::fused_forward_supported(p)) {
-    // every head's counter at its last hand-over, one ticket per workgroup
-    const uint32_t* sync = reinterpret_cast<const uint32_t*>(w + ws.sync_off);
-    const uint32_t last = p.nc > 1 ? uint32_t(p.nc - 1) : 0u;
-    const bool flags_ok = all_equal(sync, p.batch * p.H, [&](int64_t) { return last; });
-    const uint32_t tickets = uint32_t(ssd::fused_forward_grid(p));
-    const bool ticket_ok = flags_ok && all_equal(sync + p.batch * p.H, 1, [&](int64_t) { return tickets; });
-    if (!flags_ok || !ticket_ok) bits |= SSD_STATUS_CHAIN_INCOMPLETE;
-  } else if (tag == ssd::kPathSplitSegmented && ws.sp_off != 0) {
-    // every segment but the last of each (chain, slice) published, one ticket per workgroup
-    const ssd::SegScratch sc = ssd::seg_scratch_layout(p, const_cast<char*>(w + ws.sp_off));
-    const int64_t nseg = sc.nseg;
-    const bool flags_ok = all_equal(sc.flags, sc.chains * sc.nslice * nseg,
-                                    [&](int64_t i) { return (i % nseg) + 1 < nseg ? 1u : 0u; });
-    const uint32_t tickets = uint32_t(ssd::seg_state_passing_grid(p));
-    const bool ticket_ok = flags_ok && all_equal(sc.ticket, 1, [&](int64_t) { return tickets; });
-    if (!flags_ok || !ticket_ok) bits |= SSD_STATUS_CHAIN_INCOMPLETE;
-  } else if (tag != ssd::kPathSplit) {
-    tag = SSD_PATH_NONE;
-    bits = SSD_STATUS_NO_RECORD;
-  }
-  if (!hip_ok) return SSD_ERR_HIP;
-  if (path != nullptr) *path = tag;
-  *status = bits;
-  return SSD_OK;
+  return ssd::read_status(p, w + ws.stat_off, ssd::fused_forward_supported(p) ? w + ws.sync_off : nullptr,
+                          ws.sp_off != 0 ? w + ws.sp_off : nullptr, static_cast<hipStream_t>(stream), path,
+                          status);
 }
 
 ssd_status_t ssd_workspace_bytes_varlen(const ssd_desc_t* desc, int64_t num_seqs, size_t* bytes) {
@@ -480,8 +547,22 @@ ssd_status_t ssd_workspace_bytes_varlen(const ssd_desc_t* desc, int64_t num_seqs
   Plan p;
   const ssd_status_t st = ssd::make_varlen_plan(desc, num_seqs, &p);
   if (st != SSD_OK) return st;
-  *bytes = ssd::ws_layout(p, true).total;
+  *bytes = ssd::varlen_layout(p, num_seqs).total;
   return SSD_OK;
+}
+
+ssd_status_t ssd_workspace_status_varlen(const ssd_desc_t* desc, int64_t num_seqs, const void* workspace,
+                                         size_t workspace_bytes, void* stream, uint32_t* path, uint32_t* status) {
+  Plan p;
+  ssd_status_t st = ssd::make_varlen_plan(desc, num_seqs, &p);
+  if (st != SSD_OK) return st;
+  if (workspace == nullptr || status == nullptr) return SSD_ERR_NULL_POINTER;
+  if (!ssd::aligned(workspace, ssd::kWsAlign)) return SSD_ERR_ALIGNMENT;
+  const ssd::VarlenLayout v = ssd::varlen_layout(p, num_seqs);
+  if (workspace_bytes < v.total) return SSD_ERR_WORKSPACE;
+  const char* w = static_cast<const char*>(workspace);
+  return ssd::read_status(v.pm, w + v.stat_off, nullptr, v.pl.sp_off != 0 ? w + v.pl.sp_off : nullptr,
+                          static_cast<hipStream_t>(stream), path, status);
 }
 
 ssd_status_t ssd_forward_varlen(const ssd_desc_t* desc, const int32_t* cu_seqlens, int64_t num_seqs,
@@ -497,8 +578,16 @@ ssd_status_t ssd_forward_varlen(const ssd_desc_t* desc, const int32_t* cu_seqlen
       !ssd::aligned(A, 4) || !ssd::aligned(D, 4) || !ssd::aligned(cu_seqlens, 4) ||
       !ssd::aligned(workspace, ssd::kWsAlign))
     return SSD_ERR_ALIGNMENT;
-  const ssd::WsLayout ws = ssd::ws_layout(p, true);
-  if (workspace != nullptr && workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
+  const ssd::VarlenLayout v = ssd::varlen_layout(p, num_seqs);
+  const ssd::WsLayout& ws = v.ws;
+  const ssd::PackedLayout& pl = v.pl;
+  // bf16 io without initial states: fixed chunks of the packed stream.
+  // Otherwise chunks per sequence: each sequence's recurrence starts from its
+  // own state, and fp32 io keeps every decay to a few fp32 roundings (in
+  // fixed chunks a sequence after k starts in one chunk has its dA cumsum
+  // near -128 k, resolved to 2^-16 k)
+  const bool fixed_chunks = init_states == nullptr && p.io == ssd::kBF16;
+  if (workspace != nullptr && workspace_bytes < v.total) return SSD_ERR_WORKSPACE;
 
   const size_t io = p.io_bytes();
   const size_t xy_bytes = size_t(p.L * p.H * p.P) * io;
@@ -511,7 +600,7 @@ ssd_status_t ssd_forward_varlen(const ssd_desc_t* desc, const int32_t* cu_seqlen
                            ssd::range_of(cu_seqlens, size_t(num_seqs + 1) * sizeof(int32_t))};
   const ssd::Range ry = ssd::range_of(y, xy_bytes);
   const ssd::Range rf = ssd::range_of(final_states, st_bytes);
-  const ssd::Range rw = ssd::range_of(workspace, ws.total);
+  const ssd::Range rw = ssd::range_of(workspace, v.total);
   for (const ssd::Range& r : in) {
     if (ssd::overlap(ry, r) || ssd::overlap(rw, r)) return SSD_ERR_ALIAS;
     if (ssd::overlap(rf, r) && !(r.lo == reinterpret_cast<uintptr_t>(init_states) && rf.lo == r.lo))
@@ -523,21 +612,58 @@ ssd_status_t ssd_forward_varlen(const ssd_desc_t* desc, const int32_t* cu_seqlen
   void* wbase = workspace;
   bool owned = false;
   if (wbase == nullptr) {
-    if (hipMallocAsync(&wbase, ws.total, s) != hipSuccess) return SSD_ERR_HIP;
+    if (hipMallocAsync(&wbase, v.total, s) != hipSuccess) return SSD_ERR_HIP;
     owned = true;
   }
   char* w = static_cast<char*>(wbase);
-  float* cs = reinterpret_cast<float*>(w + ws.cs_off);
-  float* dtc = reinterpret_cast<float*>(w + ws.dt_off);
-  void* states = w + ws.st_off;
-  ssd::ChunkInfo* tab = reinterpret_cast<ssd::ChunkInfo*>(w + ws.tab_off);
-  int2* seqtab = reinterpret_cast<int2*>(w + ws.seq_off);
-  p.ctab = tab;
-  p.seqtab = seqtab;
-  hipError_t e = ssd::launch_build_chunk_table(cu_seqlens, num_seqs, p.L, p.Q, p.nc, tab, seqtab, s);
-  if (e == hipSuccess) e = ssd::run_cumsum_chunk_state(p, x, B, dt, A, cs, dtc, states, s);
-  if (e == hipSuccess) e = ssd::launch_state_passing(p, states, cs, init_states, final_states, s);
-  if (e == hipSuccess) e = ssd::run_chunk_scan(p, x, B, C, D, cs, dtc, states, y, s);
+  uint32_t* stat = reinterpret_cast<uint32_t*>(w + v.stat_off);
+  hipError_t e;
+  if (fixed_chunks) {
+    float* cs = reinterpret_cast<float*>(w + pl.cs_off);
+    float* dtc = reinterpret_cast<float*>(w + pl.dt_off);
+    void* states = w + pl.st_off;
+    uint8_t* seg = reinterpret_cast<uint8_t*>(w + pl.seg_off);
+    ssd::ChunkInfo* wtab = reinterpret_cast<ssd::ChunkInfo*>(w + pl.wtab_off);
+    int32_t* xend = final_states != nullptr ? reinterpret_cast<int32_t*>(w + pl.xend_off) : nullptr;
+    Plan pc = v.pm;
+    pc.seg_start = seg;
+    pc.cross_end = xend;             // state passing leaves the entering states of the
+    pc.cross_hin = final_states;     // sequences that cross into their last chunk here
+    e = ssd::launch_build_packed_tables(cu_seqlens, num_seqs, pc.L, pc.Q, pc.nc, seg, wtab, xend, s);
+    if (e == hipSuccess) e = ssd::run_cumsum_chunk_state(pc, x, B, dt, A, cs, dtc, states, s);
+    if (e == hipSuccess) {
+      if (pl.sp_off != 0)
+        e = ssd::launch_state_passing_seg(pc, states, cs, nullptr, nullptr, w + pl.sp_off, stat, s);
+      else
+        e = ssd::launch_state_passing(pc, states, cs, nullptr, nullptr, s, stat);
+    }
+    if (e == hipSuccess) e = ssd::run_chunk_scan(pc, x, B, C, D, cs, dtc, states, y, s);
+    if (e == hipSuccess && final_states != nullptr) {
+      // the end windows: their local states, then the final states
+      Plan pw = pc;
+      pw.ctab = wtab;
+      pw.nc = num_seqs;
+      pw.cross_end = nullptr;
+      pw.cross_hin = nullptr;
+      float* wcs = reinterpret_cast<float*>(w + pl.wcs_off);
+      e = ssd::run_cumsum_chunk_state(pw, x, B, dt, A, wcs, reinterpret_cast<float*>(w + pl.wdt_off),
+                                      w + pl.wst_off, s);
+      if (e == hipSuccess)
+        e = ssd::launch_packed_finals(pc, wtab, num_seqs, w + pl.wst_off, wcs, final_states, s);
+    }
+  } else {
+    float* cs = reinterpret_cast<float*>(w + ws.cs_off);
+    float* dtc = reinterpret_cast<float*>(w + ws.dt_off);
+    void* states = w + ws.st_off;
+    ssd::ChunkInfo* tab = reinterpret_cast<ssd::ChunkInfo*>(w + ws.tab_off);
+    int2* seqtab = reinterpret_cast<int2*>(w + ws.seq_off);
+    p.ctab = tab;
+    p.seqtab = seqtab;
+    e = ssd::launch_build_chunk_table(cu_seqlens, num_seqs, p.L, p.Q, p.nc, tab, seqtab, s);
+    if (e == hipSuccess) e = ssd::run_cumsum_chunk_state(p, x, B, dt, A, cs, dtc, states, s);
+    if (e == hipSuccess) e = ssd::launch_state_passing(p, states, cs, init_states, final_states, s, stat);
+    if (e == hipSuccess) e = ssd::run_chunk_scan(p, x, B, C, D, cs, dtc, states, y, s);
+  }
   if (owned) {
     const hipError_t fe = hipFreeAsync(wbase, s);
     if (e == hipSuccess) e = fe;

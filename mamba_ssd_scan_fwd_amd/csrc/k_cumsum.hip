@@ -32,7 +32,8 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(
     const float* __restrict__ dt, const float* __restrict__ A,
     float* __restrict__ dA_cs, float* __restrict__ dtc,
     int64_t L, int H, int64_t nc, DtOpts dto, const ChunkInfo* __restrict__ ctab,
-    uint32_t* __restrict__ clear, int64_t nclear, uint32_t* __restrict__ stat, uint32_t tag) {
+    const uint8_t* __restrict__ seg, uint32_t* __restrict__ clear, int64_t nclear,
+    uint32_t* __restrict__ stat, uint32_t tag) {
   constexpr int QPL = Q / 64;  // positions per lane
   __shared__ float tile[Q][kHB + 1];
   const int64_t c = blockIdx.x;
@@ -69,7 +70,17 @@ __global__ __launch_bounds__(kThreads) void chunk_cumsum_kernel(
     float d[QPL], s[QPL];
 #pragma unroll
     for (int k = 0; k < QPL; ++k) d[k] = tile[lane * QPL + k][hh];
-    wave_chunk_cumsum(d, a, s, lane);
+    if (seg != nullptr) {  // packed sequences in fixed chunks: the jumps at sequence starts
+      bool st[QPL];
+#pragma unroll
+      for (int k = 0; k < QPL; ++k) {
+        const int pos = lane * QPL + k;
+        st[k] = pos < rows && seg[row0 + pos] != 0;
+      }
+      wave_chunk_cumsum_jump(d, a, st, s, lane);
+    } else {
+      wave_chunk_cumsum(d, a, s, lane);
+    }
     const int64_t base = (((b * H + h) * nc) + c) * Q + lane * QPL;
 #pragma unroll
     for (int k = 0; k < QPL; ++k) {
@@ -87,15 +98,15 @@ hipError_t launch_chunk_cumsum_clear(const Plan& p, const float* dt, const float
   dim3 grid((unsigned)p.nc, (unsigned)p.batch, (unsigned)((p.H + kHB - 1) / kHB));
   switch (p.Q) {
     case 64:
-      chunk_cumsum_kernel<64><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab, clear,
+      chunk_cumsum_kernel<64><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab, p.seg_start, clear,
                                                         nclear, stat, tag);
       break;
     case 128:
-      chunk_cumsum_kernel<128><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab, clear,
+      chunk_cumsum_kernel<128><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab, p.seg_start, clear,
                                                          nclear, stat, tag);
       break;
     case 256:
-      chunk_cumsum_kernel<256><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab, clear,
+      chunk_cumsum_kernel<256><<<grid, kThreads, 0, s>>>(dt, A, dA_cs, dtc, p.L, (int)p.H, p.nc, p.dto, p.ctab, p.seg_start, clear,
                                                          nclear, stat, tag);
       break;
     default:

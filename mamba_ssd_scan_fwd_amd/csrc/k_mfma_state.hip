@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const float* __restrict__ dt, const float* __restrict__ A,
     float* __restrict__ dA_cs, float* __restrict__ dtc,
     uint16_t* __restrict__ states, int64_t L, int H, int G, int N, int64_t nc, int HB, DtOpts dto,
-    const ChunkInfo* __restrict__ ctab) {
+    const ChunkInfo* __restrict__ ctab, const uint8_t* __restrict__ seg) {
   using C = StateCfg<P, NB, Q>;
   constexpr int KS = C::KS;
   constexpr int TAB_U4 = FUSED ? C::TAB_FLOATS / 4 : 0;
@@ -246,7 +246,17 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
       float d[QPL], sc[QPL];
 #pragma unroll
       for (int k = 0; k < QPL; ++k) d[k] = tab[(2 * hh + 1) * Q + lane * QPL + k];
-      wave_chunk_cumsum(d, A[h0 + hh], sc, lane);
+      if (seg != nullptr) {  // packed sequences in fixed chunks: the jumps at sequence starts
+        bool st[QPL];
+#pragma unroll
+        for (int k = 0; k < QPL; ++k) {
+          const int pos = lane * QPL + k;
+          st[k] = pos < rows && seg[row0 + pos] != 0;
+        }
+        wave_chunk_cumsum_jump(d, A[h0 + hh], st, sc, lane);
+      } else {
+        wave_chunk_cumsum(d, A[h0 + hh], sc, lane);
+      }
 #pragma unroll
       for (int k = 0; k < QPL; ++k) tab[2 * hh * Q + lane * QPL + k] = sc[k];
       if (nb == 0) {
@@ -376,7 +386,8 @@ hipError_t launch_pnq(const Plan& p, const void* x, const void* B, const float* 
   const int64_t grid = p.batch * p.nc * (p.H / hb) * nnb;
   chunk_state_mfma_kernel<P, NB, Q, FUSED><<<dim3((unsigned)grid), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), dt, A, cs, dtc,
-      static_cast<uint16_t*>(st), p.L, (int)p.H, (int)p.G, (int)p.N, p.nc, hb, p.dto, p.ctab);
+      static_cast<uint16_t*>(st), p.L, (int)p.H, (int)p.G, (int)p.N, p.nc, hb, p.dto, p.ctab,
+      FUSED ? p.seg_start : nullptr);
   return hipGetLastError();
 }
 

@@ -73,12 +73,15 @@ template <> struct Vec8<__hip_bfloat16> {
 // sequence; with packed sequences (seqtab != nullptr, batch 1) chain
 // bh = s*H + h walks the seqtab[s].y chunk slots from seqtab[s].x of head h,
 // so every sequence is a chain of its own. h0 and hT are indexed by the chain.
+// With xend (packed sequences in fixed chunks, batch 1): at chunk c with
+// xend[c] = q >= 0, the fp32 state entering the chunk is also stored to
+// xhin[q, h] (q's final state is completed from it).
 template <typename TS, int PF>
 __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     TS* __restrict__ states, const float* __restrict__ dA_cs,
     const float* h0, float* hT,  // may be the same buffer (in-place update)
     int64_t nc, int Q, int PN, int H, const int2* __restrict__ seqtab, uint32_t* __restrict__ stat,
-    uint32_t tag) {
+    uint32_t tag, const int32_t* __restrict__ xend, float* __restrict__ xhin) {
   const int64_t bh = blockIdx.x;
   if (stat != nullptr && bh == 0 && blockIdx.y == 0 && threadIdx.x == 0) {  // the forward's status record
     stat[0] = tag;
@@ -116,22 +119,26 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     if (active && k < cnt) ring[k].load(s + (int64_t)k * PN);
 
   float dec = 0.f;
+  int xq = -1;
   for (int64_t c0 = 0; c0 < cnt; c0 += PF) {
 #pragma unroll
     for (int k = 0; k < PF; ++k) {
       const int64_t c = c0 + k;
       if (c < cnt) {
-        if ((c & 63) == 0) {  // refresh: lane l holds exp(Lam_{c+l})
+        if ((c & 63) == 0) {  // refresh: lane l holds exp(Lam_{c+l}) (and xend[c+l])
           const int64_t cl = c + lane;
           dec = cl < cnt ? __expf(lam[cl * Q]) : 0.f;
+          if (xend != nullptr) xq = cl < cnt ? xend[c_beg + cl] : -1;
         }
         const float d = __int_as_float(
             __builtin_amdgcn_readlane(__float_as_int(dec), (int)(c & 63)));
+        const int q = __builtin_amdgcn_readlane(xq, (int)(c & 63));  // wavefront-uniform
         if (active) {
           float sv[kVec];
           ring[k].to(sv);
           if (c + PF < cnt) ring[k].load(s + (c + PF) * PN);
           Vec8<TS>::store(s + c * PN, h);
+          if (q >= 0) Vec8<float>::store(xhin + ((int64_t)q * H + row) * PN + e0, h);
 #pragma unroll
           for (int e = 0; e < kVec; ++e) h[e] = fmaf(d, h[e], sv[e]);
         }
@@ -163,12 +170,13 @@ constexpr int kSegChunks = 32;
 constexpr int kSpinLimit = 1 << 18;
 constexpr uint32_t kCutOffBit = 2u;  // in the forward's status word (bit 0 is the one-pass kernel's)
 
+// xend / xhin as for state_passing_kernel (batch 1: the chain is the head).
 template <typename TS, int KS>
 __global__ __launch_bounds__(kThreads) void state_passing_seg_kernel(
     TS* __restrict__ states, const float* __restrict__ dA_cs, const float* h0, float* hT,
     float* __restrict__ agg, float* __restrict__ agg_lam, uint32_t* __restrict__ flags,
     uint32_t* __restrict__ ticket, uint32_t* __restrict__ status, int64_t nc, int Q, int PN, int64_t chains,
-    int nslice, int nseg) {
+    int nslice, int nseg, const int32_t* __restrict__ xend, float* __restrict__ xhin) {
   __shared__ uint32_t stk;
   if (threadIdx.x == 0) stk = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -193,6 +201,7 @@ __global__ __launch_bounds__(kThreads) void state_passing_seg_kernel(
     if (active && k < cnt) sv[k].load(s + (int64_t)k * PN);
   const float lam_l = lane < cnt ? lam[(int64_t)lane * Q] : 0.f;
   const float dec_l = __expf(lam_l);
+  const int xq_l = xend != nullptr && lane < cnt ? xend[c_beg + lane] : -1;
   float hin0[8];
   if (active && h0 != nullptr) {
     Vec8<float> v;
@@ -272,10 +281,12 @@ __global__ __launch_bounds__(kThreads) void state_passing_seg_kernel(
   for (int k = 0; k < KS; ++k) {
     if (k < cnt) {
       const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dec_l), k));
+      const int q = __builtin_amdgcn_readlane(xq_l, k);  // wavefront-uniform
       if (active) {
         float v[8];
         sv[k].to(v);
         Vec8<TS>::store(s + (int64_t)k * PN, h);
+        if (q >= 0) Vec8<float>::store(xhin + ((int64_t)q * chains + bh) * PN + e0, h);
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = fmaf(d, h[e], v[e]);
       }
@@ -300,7 +311,8 @@ hipError_t launch_typed(const Plan& p, void* states, const float* dA_cs,
   const int64_t chains = p.seqtab != nullptr ? p.nseq * p.H : p.batch * p.H;
   dim3 grid((unsigned)chains, (unsigned)((PN + kThreads * kVec - 1) / (kThreads * kVec)));
   state_passing_kernel<TS, 8><<<grid, kThreads, 0, s>>>(
-      static_cast<TS*>(states), dA_cs, h0, hT, p.nc, p.Q, PN, (int)p.H, p.seqtab, stat, kPathSplit);
+      static_cast<TS*>(states), dA_cs, h0, hT, p.nc, p.Q, PN, (int)p.H, p.seqtab, stat, kPathSplit, p.cross_end,
+      p.cross_hin);
   return hipGetLastError();
 }
 
@@ -320,7 +332,7 @@ hipError_t launch_seg_typed(const Plan& p, void* states, const float* dA_cs, con
   const int64_t grid = chains * nslice * nseg;
   state_passing_seg_kernel<TS, kSegChunks><<<dim3((unsigned)grid), kThreads, 0, s>>>(
       static_cast<TS*>(states), dA_cs, h0, hT, sc.agg, sc.agg_lam, sc.flags, sc.ticket,
-      stat != nullptr ? stat + 1 : sc.status, p.nc, p.Q, PN, chains, nslice, nseg);
+      stat != nullptr ? stat + 1 : sc.status, p.nc, p.Q, PN, chains, nslice, nseg, p.cross_end, p.cross_hin);
   return hipGetLastError();
 }
 

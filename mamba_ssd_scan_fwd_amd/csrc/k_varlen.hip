@@ -76,7 +76,137 @@ __global__ __launch_bounds__(kTabThreads) void build_chunk_table_kernel(
     tab[slot] = ChunkInfo{0, 0, -1, 0};
 }
 
+// ---- packed sequences in fixed chunks -------------------------------------
+//
+// Without initial states the packed stream is cut into the fixed Q-token
+// chunks of one long sequence, and every sequence start enters the chunk
+// cumsum as a jump of -kSegJump (chunk_cumsum.h): every decay across a start
+// is then exactly 0, so the chunk-state, state-passing and chunk-scan steps
+// run unchanged and keep each sequence to itself. A chunk may hold the end of
+// one sequence and the start of the next; no chunk is partial except the
+// last of the stream.
+//
+// The final state of sequence s is the state after its last token e. Its end
+// window runs from the start of the chunk holding e to e; the window's local
+// state (the chunk-state step on the window, with the same jumps) plus the
+// state entering that chunk times exp(l'_e) (the window's cumsum at e: 0 when
+// the sequence starts inside the window) is the final state.
+
+__device__ __forceinline__ int64_t clamped_start(const int32_t* cu, int64_t s, int64_t T) {
+  const int64_t a = cu[s];
+  return a < 0 ? 0 : (a > T ? T : a);
+}
+
+// seg_start[t] = 1 where a non-empty sequence starts after token 0 (nothing
+// precedes token 0, so no decay has to be cut there). wtab[s] = the end
+// window of sequence s: its last token's chunk from that chunk's first row to
+// the last token (rows 0 for an empty sequence), flags kCrossing when the
+// sequence started in an earlier chunk. cross_end[c] = the sequence that
+// holds chunk c's first token, started earlier and ends in chunk c, else -1
+// (with valid offsets, at most one sequence per chunk).
+constexpr int32_t kCrossing = 1;
+__device__ __forceinline__ int64_t seq_holding(const int32_t* cu, int64_t S, int64_t T, int64_t t) {
+  // the last sequence whose start is <= t: with valid offsets, the non-empty
+  // sequence that holds t (an empty one starts where the next one does)
+  int64_t lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (clamped_start(cu, mid, T) <= t)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void build_packed_tables_kernel(const int32_t* __restrict__ cu, int64_t S,
+                                                                  int64_t T, int Q, int64_t nc,
+                                                                  uint8_t* __restrict__ seg_start,
+                                                                  ChunkInfo* __restrict__ wtab,
+                                                                  int32_t* __restrict__ cross_end) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int64_t t = i0; t < T; t += stride)
+    seg_start[t] = t > 0 && clamped_start(cu, seq_holding(cu, S, T, t), T) == t ? 1 : 0;
+  for (int64_t s = i0; s < S; s += stride) {
+    int64_t start, len;
+    seq_span(cu, s, T, start, len);
+    if (len == 0) {
+      wtab[s] = ChunkInfo{0, 0, (int32_t)s, 0};
+    } else {
+      const int64_t e = start + len - 1;
+      const int64_t t0 = e / Q * Q;
+      wtab[s] = ChunkInfo{(int32_t)t0, (int32_t)(e - t0 + 1), (int32_t)s, start < t0 ? kCrossing : 0};
+    }
+  }
+  if (cross_end != nullptr) {
+    for (int64_t c = i0; c < nc; c += stride) {
+      const int64_t t0 = c * Q;
+      const int64_t s = seq_holding(cu, S, T, t0);
+      int64_t start, len;
+      seq_span(cu, s, T, start, len);
+      const bool crosses = len > 0 && start < t0 && (start + len - 1) / Q == c;
+      cross_end[c] = crosses ? (int32_t)s : -1;
+    }
+  }
+}
+
+// final[s, h] = window state + exp(l'_e) * state entering the window's chunk
+// (that state left in `finals` by state passing; only for a sequence that
+// started in an earlier chunk: for the others the window holds the whole
+// sequence), eight elements per thread; one block row per (s, h).
+template <typename TS>
+__global__ __launch_bounds__(256) void packed_finals_kernel(const ChunkInfo* __restrict__ wtab,
+                                                            const TS* __restrict__ states_w,
+                                                            const float* __restrict__ cs_w,
+                                                            float* __restrict__ finals, int64_t S, int H, int PN,
+                                                            int Q) {
+  const int64_t sh = blockIdx.x;  // s * H + h
+  const int64_t s = sh / H;
+  const int h = (int)(sh % H);
+  const int e0 = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+  if (e0 >= PN) return;
+  const ChunkInfo ci = wtab[s];
+  float* out = finals + sh * PN + e0;
+  if (ci.rows <= 0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out[k] = 0.f;
+    return;
+  }
+  const TS* w = states_w + ((int64_t)h * S + s) * PN + e0;
+  if (ci.flags & kCrossing) {
+    const float carry = __expf(cs_w[((int64_t)h * S + s) * Q + ci.rows - 1]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out[k] = to_f32(w[k]) + carry * out[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out[k] = to_f32(w[k]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_build_packed_tables(const int32_t* cu, int64_t S, int64_t T, int Q, int64_t nc, uint8_t* seg_start,
+                                      ChunkInfo* wtab, int32_t* cross_end, hipStream_t s) {
+  const int64_t work = T > S ? T : S;
+  const int64_t blocks = (work + 255) / 256 < 4096 ? (work + 255) / 256 : 4096;
+  build_packed_tables_kernel<<<dim3((unsigned)(blocks > 0 ? blocks : 1)), 256, 0, s>>>(cu, S, T, Q, nc, seg_start,
+                                                                                     wtab, cross_end);
+  return hipGetLastError();
+}
+
+hipError_t launch_packed_finals(const Plan& p, const ChunkInfo* wtab, int64_t S, const void* states_w,
+                                const float* cs_w, float* finals, hipStream_t s) {
+  const int PN = (int)(p.P * p.N);
+  dim3 grid((unsigned)(S * p.H), (unsigned)((PN / 8 + 255) / 256));
+  if (p.io == kBF16)
+    packed_finals_kernel<__hip_bfloat16><<<grid, 256, 0, s>>>(
+        wtab, static_cast<const __hip_bfloat16*>(states_w), cs_w, finals, S, (int)p.H, PN, p.Q);
+  else
+    packed_finals_kernel<float><<<grid, 256, 0, s>>>(wtab, static_cast<const float*>(states_w), cs_w, finals, S,
+                                                     (int)p.H, PN, p.Q);
+  return hipGetLastError();
+}
 
 hipError_t launch_build_chunk_table(const int32_t* cu, int64_t S, int64_t T, int Q, int64_t nslots,
                                     ChunkInfo* tab, int2* seqtab, hipStream_t s) {

@@ -33,6 +33,15 @@ struct Plan {
   const ChunkInfo* ctab = nullptr;  // packed sequences: per-chunk table (device), else null
   const int2* seqtab = nullptr;     // packed sequences: (first slot, chunk count) per sequence
   int64_t nseq = 0;                 // packed sequences: their number
+  // packed sequences in fixed chunks: 1 at every token where a sequence
+  // starts (the cumsum's jumps, kSegJump), else nullptr
+  const uint8_t* seg_start = nullptr;
+  // ... and their final states wanted (batch 1): per chunk, the sequence that
+  // enters it from an earlier chunk and ends in it (else -1), and where state
+  // passing leaves, in fp32, the state entering that chunk for that sequence
+  // ([S, H, P, N]); both nullptr otherwise
+  const int32_t* cross_end = nullptr;
+  float* cross_hin = nullptr;
   int64_t batch, L, H, P, N, G;
   int io;       // IoType of x, B, C, y and of the chunk states
   int Q;        // chunk length
@@ -107,6 +116,15 @@ hipError_t launch_chunk_cumsum_clear(const Plan& p, const float* dt, const float
                                      uint32_t* clear, int64_t nclear, uint32_t* stat, uint32_t tag,
                                      hipStream_t s);
 hipError_t launch_fused_forward(const Plan& p, const FusedArgs& a, hipStream_t s);
+
+// Packed sequences in fixed chunks (k_varlen.hip): the per-token sequence
+// start flags and, per sequence, its end window (from the start of the chunk
+// holding its last token to that token); then each sequence's final state
+// from its window's local state and the state entering the window's chunk.
+hipError_t launch_build_packed_tables(const int32_t* cu, int64_t S, int64_t T, int Q, int64_t nc, uint8_t* seg_start,
+                                      ChunkInfo* wtab, int32_t* cross_end, hipStream_t s);
+hipError_t launch_packed_finals(const Plan& p, const ChunkInfo* wtab, int64_t S, const void* states_w,
+                                const float* cs_w, float* finals, hipStream_t s);
 
 hipError_t launch_conv1d_split(const Plan& p, int K, const void* xbc, const float* w, const float* bias, int act,
                                const float* st_in, float* st_out, void* x, void* B, void* C, hipStream_t s);

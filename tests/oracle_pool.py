@@ -111,6 +111,50 @@ def compare_all(inp: dict, y, hT, out_eps: float, batches=None, heads=None, bloc
     return agg
 
 
+def compare_packed(inp: dict, cu, y, hT, out_eps: float, init_states=None, block: int = 16) -> dict:
+    """compare_all for packed sequences: ``inp`` holds [1, T, ...] inputs,
+    ``cu`` the S + 1 offsets, ``y`` [1, T, H, P] and ``hT`` [S, H, P, N] the
+    GPU outputs, ``init_states`` [S, H, P, N] or None. Every (sequence, head)
+    chain runs the oracle recurrence on its own tokens; an empty sequence's
+    final state must equal its initial state (zeros without one) exactly."""
+    to_np = _to_numpy
+    x, dt, Bm, Cm = (to_np(inp[k])[0] for k in ("x", "dt", "B", "C"))
+    A = to_np(inp["A"])
+    D = None if inp["D"] is None else to_np(inp["D"])
+    h0 = None if init_states is None else to_np(init_states)
+    yg = to_np(y)[0]
+    hg = None if hT is None else to_np(hT)
+    cu = [int(v) for v in cu]
+    T, H, P = x.shape
+    G = Bm.shape[1]
+    hpg = H // G
+    blocks = head_blocks(H, G, block)
+    tasks, empty_ok = [], True
+    for s in range(len(cu) - 1):
+        a, e = cu[s], cu[s + 1]
+        if e == a:
+            if hg is not None:
+                want = np.zeros_like(hg[s]) if h0 is None else h0[s]
+                empty_ok = empty_ok and np.array_equal(hg[s], want)
+            continue
+        for ha, he in blocks:
+            ga, ge = ha // hpg, (he - 1) // hpg + 1
+            tasks.append((x[a:e, ha:he], dt[a:e, ha:he], A[ha:he], Bm[a:e, ga:ge], Cm[a:e, ga:ge],
+                          None if D is None else D[ha:he], None if h0 is None else h0[s, ha:he],
+                          yg[a:e, ha:he], None if hg is None else hg[s, ha:he], out_eps))
+    res = list(_pool().map(_task, tasks))
+    agg = {
+        "y": max(r["y_err"] for r in res) / max(max(r["y_ref"] for r in res), 1e-30),
+        "ssm": max(r["ssm_excess"] for r in res) / max(max(r["ssm_ref"] for r in res), 1e-30),
+        "finite": all(r["finite"] for r in res),
+        "chains": sum(1 for s in range(len(cu) - 1) if cu[s + 1] > cu[s]) * H,
+        "empty_ok": empty_ok,
+    }
+    if hg is not None:
+        agg["final_state"] = max(r["h_err"] for r in res) / max(max(r["h_ref"] for r in res), 1e-30)
+    return agg
+
+
 def _to_numpy(t):
     if isinstance(t, np.ndarray):
         return t

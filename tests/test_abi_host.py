@@ -261,11 +261,19 @@ def test_varlen_validates():
     # chunk slots ceil(T/Q) + S: ceil(10000 / 256) + 7 = 47
     q = ctypes.c_int32()
     assert L.ssd_effective_chunk_size(ctypes.byref(d), ctypes.byref(q)) == OK and q.value == 256
+    up = lambda b: -(-b // 256) * 256
+    # chunks per sequence (with initial states)
     slots = -(-10000 // 256) + 7
-    expect = 0
-    for nbytes in (64 * slots * 256 * 4, 64 * slots * 256 * 4, 64 * slots * 64 * 128 * 2, slots * 16, 7 * 8):
-        expect += -(-nbytes // 256) * 256
-    assert n.value == expect
+    per_seq = sum(up(b) for b in (64 * slots * 256 * 4, 64 * slots * 256 * 4, 64 * slots * 64 * 128 * 2,
+                                  slots * 16, 7 * 8))
+    # fixed chunks of the packed stream (without): 40 chunks (too few for the
+    # segmented state passing), 7 end windows, 10000 start flags, the window
+    # table, the crossing sequence of each chunk
+    nc = -(-10000 // 256)
+    packed = sum(up(b) for b in (64 * nc * 256 * 4, 64 * nc * 256 * 4, 64 * nc * 64 * 128 * 2,
+                                 64 * 7 * 256 * 4, 64 * 7 * 256 * 4, 64 * 7 * 64 * 128 * 2, 10000, 7 * 16,
+                                 nc * 4))
+    assert n.value == max(per_seq, packed) + 256  # then the status record
     p = [ctypes.c_void_p(BASE + k * (1 << 30)) for k in range(12)]
     # cu x dt A B C D h0 y hT ws
     args = lambda q: (ctypes.byref(d), q[0], ctypes.c_int64(7), *q[1:10], q[10], ctypes.c_size_t(n.value), None)
@@ -279,6 +287,16 @@ def test_varlen_validates():
     q2 = list(p)
     q2[9] = ctypes.c_void_p(p[7].value + 4096)  # final_states partly over init_states
     assert L.ssd_forward_varlen(*args(q2)) == ALIAS
+    # the status query of a varlen workspace: argument checks only
+    path, bits = ctypes.c_uint32(), ctypes.c_uint32()
+    st = lambda ws, nb, S=7, dd=d: L.ssd_workspace_status_varlen(ctypes.byref(dd), ctypes.c_int64(S), ws,
+                                                                 ctypes.c_size_t(nb), None, ctypes.byref(path),
+                                                                 ctypes.byref(bits))
+    assert st(None, n.value) == NULLP
+    assert st(ctypes.c_void_p(BASE + 16), n.value) == ALIGN
+    assert st(p[11], n.value - 1) == WS
+    assert st(p[11], n.value, S=0) == SHAPE
+    assert st(p[11], n.value, dd=desc(batch=2)) == SHAPE
 
 
 def test_default_chunk_rule():

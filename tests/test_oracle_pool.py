@@ -49,3 +49,48 @@ def test_one_changed_element_in_one_chain_is_caught(where):
     r = compare_all(inp, y, hT, 2.0 ** -8, block=4)
     key = "y" if where == "y" else "final_state"
     assert r[key] > 2e-2
+
+
+def _packed(lengths, seed):
+    from ssd_inputs import make_inputs as mk
+    cfg = CONFIGS[1].with_(batch=1, seqlen=sum(lengths), nheads=8, headdim=16, dstate=16, ngroups=2)
+    inp = mk(cfg, seed=seed)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    ys, hs = [], []
+    for s in range(len(lengths)):
+        a, e = cu[s], cu[s + 1]
+        if a == e:
+            ys.append(np.zeros((1, 0, 8, 16)))
+            hs.append(np.zeros((1, 8, 16, 16)))
+            continue
+        y, hT = ssd_recurrent(*(inp[k][:, a:e] for k in ("x", "dt")), inp["A"],
+                              *(inp[k][:, a:e] for k in ("B", "C")), inp["D"], None)
+        ys.append(y)
+        hs.append(hT)
+    return inp, cu, np.concatenate(ys, axis=1), np.concatenate(hs, axis=0)
+
+
+def test_packed_comparison_of_per_sequence_oracle_runs_is_exact():
+    inp, cu, y, hT = _packed([5, 0, 17, 1, 0, 9], seed=7)
+    from oracle_pool import compare_packed
+    r = compare_packed(inp, cu, y, hT, 2.0 ** -8, block=4)
+    assert r["chains"] == 4 * 8 and r["finite"] and r["empty_ok"]
+    assert r["y"] == 0.0 and r["ssm"] == 0.0 and r["final_state"] == 0.0
+
+
+@pytest.mark.parametrize("where", ["y", "state", "empty"])
+def test_packed_comparison_catches_one_changed_element(where):
+    from oracle_pool import compare_packed
+    inp, cu, y, hT = _packed([5, 0, 17, 1, 0, 9], seed=8)
+    y, hT = y.copy(), hT.copy()
+    if where == "y":
+        y[0, 22, 6, 3] += 0.05 * np.abs(y).max()  # the length-1 sequence's token
+    elif where == "state":
+        hT[5, 1, 2, 9] += 0.05 * np.abs(hT).max()
+    else:
+        hT[4, 0, 0, 0] = 1e-30  # an empty sequence's final state must be exactly zero
+    r = compare_packed(inp, cu, y, hT, 2.0 ** -8, block=4)
+    if where == "empty":
+        assert not r["empty_ok"]
+    else:
+        assert r["y" if where == "y" else "final_state"] > 2e-2
