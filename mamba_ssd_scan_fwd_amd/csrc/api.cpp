@@ -176,11 +176,10 @@ ssd_status_t make_varlen_plan(const ssd_desc_t* d, int64_t num_seqs, Plan* p) {
 // Packed sequences without initial states: fixed chunks of the packed stream
 // (the plan of one sequence of T tokens), plus one end window per sequence.
 // Workspace: dA_cumsum, dt_chunked, states of the chunks; the segmented
-// state-passing scratch where it applies; dA_cumsum, dt_chunked, states of
-// the windows; the per-token sequence-start flags; the window table; the
-// per-chunk crossing sequence.
+// state-passing scratch where it applies; the per-token sequence-start
+// flags; the window table; the per-chunk crossing sequence.
 struct PackedLayout {
-  size_t cs_off, dt_off, st_off, sp_off, wcs_off, wdt_off, wst_off, seg_off, wtab_off, xend_off, total;
+  size_t cs_off, dt_off, st_off, sp_off, seg_off, wtab_off, xend_off, total;
 };
 Plan packed_chunk_plan(const Plan& pv) {
   Plan pm = pv;
@@ -194,7 +193,6 @@ PackedLayout packed_layout(const Plan& pm, int64_t S) {
   PackedLayout w;
   const size_t io = pm.io_bytes();
   const size_t cs = size_t(pm.H * pm.nc * pm.Q) * 4, st = size_t(pm.H * pm.nc * pm.P * pm.N) * io;
-  const size_t wcs = size_t(pm.H * S * pm.Q) * 4, wst = size_t(pm.H * S * pm.P * pm.N) * io;
   w.cs_off = 0;
   w.dt_off = align_up(cs, kWsAlign);
   w.st_off = align_up(w.dt_off + cs, kWsAlign);
@@ -204,10 +202,7 @@ PackedLayout packed_layout(const Plan& pm, int64_t S) {
     w.sp_off = end;
     end = align_up(w.sp_off + seg_scratch_layout(pm, nullptr).bytes, kWsAlign);
   }
-  w.wcs_off = end;
-  w.wdt_off = align_up(w.wcs_off + wcs, kWsAlign);
-  w.wst_off = align_up(w.wdt_off + wcs, kWsAlign);
-  w.seg_off = align_up(w.wst_off + wst, kWsAlign);
+  w.seg_off = end;
   w.wtab_off = align_up(w.seg_off + size_t(pm.L), kWsAlign);
   w.xend_off = align_up(w.wtab_off + size_t(S) * sizeof(ChunkInfo), kWsAlign);
   w.total = align_up(w.xend_off + size_t(pm.nc) * sizeof(int32_t), kWsAlign);
@@ -639,17 +634,15 @@ ssd_status_t ssd_forward_varlen(const ssd_desc_t* desc, const int32_t* cu_seqlen
     }
     if (e == hipSuccess) e = ssd::run_chunk_scan(pc, x, B, C, D, cs, dtc, states, y, s);
     if (e == hipSuccess && final_states != nullptr) {
-      // the end windows: their local states, then the final states
+      // the end windows: each one's local state, completed into the final
+      // state by the chunk-state kernel itself (bf16 io: the matrix-core kernel)
       Plan pw = pc;
       pw.ctab = wtab;
       pw.nc = num_seqs;
       pw.cross_end = nullptr;
       pw.cross_hin = nullptr;
-      float* wcs = reinterpret_cast<float*>(w + pl.wcs_off);
-      e = ssd::run_cumsum_chunk_state(pw, x, B, dt, A, wcs, reinterpret_cast<float*>(w + pl.wdt_off),
-                                      w + pl.wst_off, s);
-      if (e == hipSuccess)
-        e = ssd::launch_packed_finals(pc, wtab, num_seqs, w + pl.wst_off, wcs, final_states, s);
+      pw.window_finals = final_states;
+      e = ssd::launch_cumsum_chunk_state_mfma(pw, x, B, dt, A, nullptr, nullptr, nullptr, s);
     }
   } else {
     float* cs = reinterpret_cast<float*>(w + ws.cs_off);

@@ -90,18 +90,26 @@ __device__ __forceinline__ int bsw(int j) {
   return NB == 32 ? row_xor(j, 0, 2, 0, 2) : NB == 64 ? row_xor(j, 2, 4, 0, 2) : NB == 128 ? row_xor(j, 2, 4, 0, 8) : 0;
 }
 
-// FUSED: the workgroup also computes the chunk's dA_cumsum and dt_chunked
-// for its heads from dt and A (step 1), keeps them in LDS, and writes them to
-// the workspace for the later steps (the workgroup of the first block of
-// state columns does). Otherwise it reads them from dA_cs / dtc.
-template <int P, int NB, int Q, bool FUSED>
+// MODE kReadCumsum: reads dA_cumsum and dt_chunked from dA_cs / dtc.
+// MODE kFuseCumsum: the workgroup also computes the chunk's dA_cumsum and
+// dt_chunked for its heads from dt and A (step 1), keeps them in LDS, and
+// writes them to the workspace for the later steps (the workgroup of the
+// first block of state columns does).
+// MODE kWindowFinals: as kFuseCumsum over the end windows of packed
+// sequences (ctab = the window table), writing each sequence's fp32 final
+// state to `fin` instead of a chunk state, and no cumsum (an instantiation
+// of its own, so the other modes keep their register budget).
+constexpr int kReadCumsum = 0, kFuseCumsum = 1, kWindowFinals = 2;
+template <int P, int NB, int Q, int MODE>
 __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const float* __restrict__ dt, const float* __restrict__ A,
     float* __restrict__ dA_cs, float* __restrict__ dtc,
     uint16_t* __restrict__ states, int64_t L, int H, int G, int N, int64_t nc, int HB, DtOpts dto,
-    const ChunkInfo* __restrict__ ctab, const uint8_t* __restrict__ seg) {
+    const ChunkInfo* __restrict__ ctab, const uint8_t* __restrict__ seg, float* __restrict__ fin) {
   using C = StateCfg<P, NB, Q>;
+  constexpr bool FUSED = MODE != kReadCumsum;
+  constexpr bool WIN = MODE == kWindowFinals;
   constexpr int KS = C::KS;
   constexpr int TAB_U4 = FUSED ? C::TAB_FLOATS / 4 : 0;
   __shared__ __align__(16) uint4 lds[C::LDS_FRAGS + TAB_U4];
@@ -125,7 +133,22 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   int64_t row0;  // first token row of this chunk in the [batch * L] arrays
   int rows;      // valid positions in this chunk
   chunk_span(ctab, b, c, L, Q, row0, rows);
-  if (rows <= 0) return;  // unused slot of a packed-sequence table (uniform)
+  if (rows <= 0) {  // unused slot of a packed-sequence table (uniform)
+    if constexpr (WIN) {  // the end window of an empty sequence: final state 0
+      for (int hh = 0; hh < HB; ++hh) {
+        float* o = fin + ((int64_t)c * H + h0 + hh) * (int64_t)P * N;
+        for (int i = tid; i < P * NB / 4; i += kThreads) {
+          const int p = i / (NB / 4), n = nb * NB + 4 * (i % (NB / 4));
+          *reinterpret_cast<float4*>(o + (int64_t)p * N + n) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
+    return;
+  }
+  // end windows: the sequence started before the window (its final state
+  // takes the decayed entering state)
+  bool cross = false;
+  if constexpr (WIN) cross = (ctab[c].flags & kWindowCrossing) != 0;
   const int wn = wave % C::WN, wp = wave / C::WN;
 
   // ---- x of one head: raw rows into registers; scaled, transposed into LDS.
@@ -259,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
       }
 #pragma unroll
       for (int k = 0; k < QPL; ++k) tab[2 * hh * Q + lane * QPL + k] = sc[k];
-      if (nb == 0) {
+      if (nb == 0 && !WIN) {
         const int64_t base = ((b * H + h0 + hh) * nc + c) * Q + lane * QPL;
 #pragma unroll
         for (int k = 0; k < QPL; ++k) {
@@ -332,6 +355,38 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     }
 
     // lane holds S^T[n = 4*g4 + i][p = r16] of each tile: four consecutive n
+    if constexpr (WIN) {
+      // end window of a packed sequence (batch 1, slot c = the sequence): its
+      // final state in fp32, the window's state plus, for a sequence that
+      // started earlier, exp(l at its last token) times the fp32 state
+      // entering the chunk (left at the same place by state passing)
+      const float carry = cross ? __expf(tab[2 * hh * Q + rows - 1]) : 0.f;
+      float* o = fin + ((int64_t)c * H + h) * (int64_t)P * N;
+#pragma unroll
+      for (int tp = 0; tp < C::TP; ++tp) {
+        const int pt = wp * C::TP + tp;
+        if (C::WP * C::TP == C::NT_P || pt < C::NT_P) {
+          const int p = pt * 16 + r16;
+#pragma unroll
+          for (int tn = 0; tn < C::TN; ++tn) {
+            const int n = nb * NB + (wn * C::TN + tn) * 16 + 4 * g4;
+            float4* q = reinterpret_cast<float4*>(o + (int64_t)p * N + n);
+            f32x4_t v = acc[tn][tp];
+            if (cross) {
+              const float4 t = *q;
+              v[0] = fmaf(carry, t.x, v[0]);
+              v[1] = fmaf(carry, t.y, v[1]);
+              v[2] = fmaf(carry, t.z, v[2]);
+              v[3] = fmaf(carry, t.w, v[3]);
+            }
+            *q = make_float4(v[0], v[1], v[2], v[3]);
+          }
+        }
+      }
+      if (hh + 1 < HB) stage_x(mine, lds + ((hh + 1) & 1) * C::X_FRAGS, hh + 1);  // the other buffer
+      __syncthreads();
+      return;
+    }
     uint16_t* out = states + ((b * H + h) * nc + c) * (int64_t)P * N;
 #pragma unroll
     for (int tp = 0; tp < C::TP; ++tp) {
@@ -378,49 +433,49 @@ int pick_heads_per_wg(const Plan& p, int nnb) {
   return hb;
 }
 
-template <int P, int NB, int Q, bool FUSED>
+template <int P, int NB, int Q, int MODE>
 hipError_t launch_pnq(const Plan& p, const void* x, const void* B, const float* dt, const float* A,
                       float* cs, float* dtc, void* st, hipStream_t s) {
   const int nnb = (int)(p.N / NB);
   const int hb = pick_heads_per_wg(p, nnb);
   const int64_t grid = p.batch * p.nc * (p.H / hb) * nnb;
-  chunk_state_mfma_kernel<P, NB, Q, FUSED><<<dim3((unsigned)grid), kThreads, 0, s>>>(
+  chunk_state_mfma_kernel<P, NB, Q, MODE><<<dim3((unsigned)grid), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), dt, A, cs, dtc,
       static_cast<uint16_t*>(st), p.L, (int)p.H, (int)p.G, (int)p.N, p.nc, hb, p.dto, p.ctab,
-      FUSED ? p.seg_start : nullptr);
+      MODE != kReadCumsum ? p.seg_start : nullptr, MODE == kWindowFinals ? p.window_finals : nullptr);
   return hipGetLastError();
 }
 
-template <int P, int NB, bool FUSED>
+template <int P, int NB, int MODE>
 hipError_t launch_pn(const Plan& p, const void* x, const void* B, const float* dt, const float* A,
                      float* cs, float* dtc, void* st, hipStream_t s) {
   switch (p.Q) {
-    case 64: return launch_pnq<P, NB, 64, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
-    case 128: return launch_pnq<P, NB, 128, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
-    case 256: return launch_pnq<P, NB, 256, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
+    case 64: return launch_pnq<P, NB, 64, MODE>(p, x, B, dt, A, cs, dtc, st, s);
+    case 128: return launch_pnq<P, NB, 128, MODE>(p, x, B, dt, A, cs, dtc, st, s);
+    case 256: return launch_pnq<P, NB, 256, MODE>(p, x, B, dt, A, cs, dtc, st, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int P, bool FUSED>
+template <int P, int MODE>
 hipError_t launch_p(const Plan& p, const void* x, const void* B, const float* dt, const float* A,
                     float* cs, float* dtc, void* st, hipStream_t s) {
   switch (p.N) {
-    case 16: return launch_pn<P, 16, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
-    case 32: return launch_pn<P, 32, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
-    case 64: return launch_pn<P, 64, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
-    default: return launch_pn<P, 128, FUSED>(p, x, B, dt, A, cs, dtc, st, s);  // 128, 256
+    case 16: return launch_pn<P, 16, MODE>(p, x, B, dt, A, cs, dtc, st, s);
+    case 32: return launch_pn<P, 32, MODE>(p, x, B, dt, A, cs, dtc, st, s);
+    case 64: return launch_pn<P, 64, MODE>(p, x, B, dt, A, cs, dtc, st, s);
+    default: return launch_pn<P, 128, MODE>(p, x, B, dt, A, cs, dtc, st, s);  // 128, 256
   }
 }
 
-template <bool FUSED>
+template <int MODE>
 hipError_t launch_any(const Plan& p, const void* x, const void* B, const float* dt, const float* A,
                       float* cs, float* dtc, void* st, hipStream_t s) {
   switch (p.P) {
-    case 16: return launch_p<16, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
-    case 32: return launch_p<32, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
-    case 64: return launch_p<64, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
-    case 128: return launch_p<128, FUSED>(p, x, B, dt, A, cs, dtc, st, s);
+    case 16: return launch_p<16, MODE>(p, x, B, dt, A, cs, dtc, st, s);
+    case 32: return launch_p<32, MODE>(p, x, B, dt, A, cs, dtc, st, s);
+    case 64: return launch_p<64, MODE>(p, x, B, dt, A, cs, dtc, st, s);
+    case 128: return launch_p<128, MODE>(p, x, B, dt, A, cs, dtc, st, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -436,14 +491,15 @@ bool mfma_chunk_state_supported(const Plan& p) {
 hipError_t launch_chunk_state_mfma(const Plan& p, const void* x, const void* B,
                                    const float* dA_cs, const float* dtc, void* states,
                                    hipStream_t s) {
-  return launch_any<false>(p, x, B, nullptr, nullptr, const_cast<float*>(dA_cs), const_cast<float*>(dtc),
+  return launch_any<kReadCumsum>(p, x, B, nullptr, nullptr, const_cast<float*>(dA_cs), const_cast<float*>(dtc),
                            states, s);
 }
 
 hipError_t launch_cumsum_chunk_state_mfma(const Plan& p, const void* x, const void* B, const float* dt,
                                           const float* A, float* dA_cs, float* dtc, void* states,
                                           hipStream_t s) {
-  return launch_any<true>(p, x, B, dt, A, dA_cs, dtc, states, s);
+  if (p.window_finals != nullptr) return launch_any<kWindowFinals>(p, x, B, dt, A, nullptr, nullptr, nullptr, s);
+  return launch_any<kFuseCumsum>(p, x, B, dt, A, dA_cs, dtc, states, s);
 }
 
 }  // namespace ssd

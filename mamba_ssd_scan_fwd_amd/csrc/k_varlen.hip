@@ -100,11 +100,10 @@ __device__ __forceinline__ int64_t clamped_start(const int32_t* cu, int64_t s, i
 // seg_start[t] = 1 where a non-empty sequence starts after token 0 (nothing
 // precedes token 0, so no decay has to be cut there). wtab[s] = the end
 // window of sequence s: its last token's chunk from that chunk's first row to
-// the last token (rows 0 for an empty sequence), flags kCrossing when the
-// sequence started in an earlier chunk. cross_end[c] = the sequence that
+// the last token (rows 0 for an empty sequence), flags kWindowCrossing when
+// the sequence started in an earlier chunk. cross_end[c] = the sequence that
 // holds chunk c's first token, started earlier and ends in chunk c, else -1
 // (with valid offsets, at most one sequence per chunk).
-constexpr int32_t kCrossing = 1;
 __device__ __forceinline__ int64_t seq_holding(const int32_t* cu, int64_t S, int64_t T, int64_t t) {
   // the last sequence whose start is <= t: with valid offsets, the non-empty
   // sequence that holds t (an empty one starts where the next one does)
@@ -136,7 +135,7 @@ __global__ __launch_bounds__(256) void build_packed_tables_kernel(const int32_t*
     } else {
       const int64_t e = start + len - 1;
       const int64_t t0 = e / Q * Q;
-      wtab[s] = ChunkInfo{(int32_t)t0, (int32_t)(e - t0 + 1), (int32_t)s, start < t0 ? kCrossing : 0};
+      wtab[s] = ChunkInfo{(int32_t)t0, (int32_t)(e - t0 + 1), (int32_t)s, start < t0 ? kWindowCrossing : 0};
     }
   }
   if (cross_end != nullptr) {
@@ -151,39 +150,6 @@ __global__ __launch_bounds__(256) void build_packed_tables_kernel(const int32_t*
   }
 }
 
-// final[s, h] = window state + exp(l'_e) * state entering the window's chunk
-// (that state left in `finals` by state passing; only for a sequence that
-// started in an earlier chunk: for the others the window holds the whole
-// sequence), eight elements per thread; one block row per (s, h).
-template <typename TS>
-__global__ __launch_bounds__(256) void packed_finals_kernel(const ChunkInfo* __restrict__ wtab,
-                                                            const TS* __restrict__ states_w,
-                                                            const float* __restrict__ cs_w,
-                                                            float* __restrict__ finals, int64_t S, int H, int PN,
-                                                            int Q) {
-  const int64_t sh = blockIdx.x;  // s * H + h
-  const int64_t s = sh / H;
-  const int h = (int)(sh % H);
-  const int e0 = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
-  if (e0 >= PN) return;
-  const ChunkInfo ci = wtab[s];
-  float* out = finals + sh * PN + e0;
-  if (ci.rows <= 0) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) out[k] = 0.f;
-    return;
-  }
-  const TS* w = states_w + ((int64_t)h * S + s) * PN + e0;
-  if (ci.flags & kCrossing) {
-    const float carry = __expf(cs_w[((int64_t)h * S + s) * Q + ci.rows - 1]);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) out[k] = to_f32(w[k]) + carry * out[k];
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) out[k] = to_f32(w[k]);
-  }
-}
-
 }  // namespace
 
 hipError_t launch_build_packed_tables(const int32_t* cu, int64_t S, int64_t T, int Q, int64_t nc, uint8_t* seg_start,
@@ -192,19 +158,6 @@ hipError_t launch_build_packed_tables(const int32_t* cu, int64_t S, int64_t T, i
   const int64_t blocks = (work + 255) / 256 < 4096 ? (work + 255) / 256 : 4096;
   build_packed_tables_kernel<<<dim3((unsigned)(blocks > 0 ? blocks : 1)), 256, 0, s>>>(cu, S, T, Q, nc, seg_start,
                                                                                      wtab, cross_end);
-  return hipGetLastError();
-}
-
-hipError_t launch_packed_finals(const Plan& p, const ChunkInfo* wtab, int64_t S, const void* states_w,
-                                const float* cs_w, float* finals, hipStream_t s) {
-  const int PN = (int)(p.P * p.N);
-  dim3 grid((unsigned)(S * p.H), (unsigned)((PN / 8 + 255) / 256));
-  if (p.io == kBF16)
-    packed_finals_kernel<__hip_bfloat16><<<grid, 256, 0, s>>>(
-        wtab, static_cast<const __hip_bfloat16*>(states_w), cs_w, finals, S, (int)p.H, PN, p.Q);
-  else
-    packed_finals_kernel<float><<<grid, 256, 0, s>>>(wtab, static_cast<const float*>(states_w), cs_w, finals, S,
-                                                     (int)p.H, PN, p.Q);
   return hipGetLastError();
 }
 

@@ -24,6 +24,11 @@ struct ChunkInfo {
   int32_t t0, rows, seq, flags;
 };
 constexpr int32_t kFirstChunk = 1, kLastChunk = 2;
+// End windows of packed sequences in fixed chunks (one slot per sequence: its
+// last token's chunk, from that chunk's first row to the token): the
+// sequence started in an earlier chunk, so its final state takes the decayed
+// state entering the window's chunk.
+constexpr int32_t kWindowCrossing = 4;
 // The chunk count of a sequence is also kept per sequence (first slot, count)
 // so that state passing can run one chain per sequence.
 
@@ -42,6 +47,11 @@ struct Plan {
   // ([S, H, P, N]); both nullptr otherwise
   const int32_t* cross_end = nullptr;
   float* cross_hin = nullptr;
+  // end windows (ctab = the window table, nc = S): the chunk-state kernel
+  // writes each sequence's fp32 final state here ([S, H, P, N], holding the
+  // entering states state passing left for the crossing sequences) instead
+  // of chunk states
+  float* window_finals = nullptr;
   int64_t batch, L, H, P, N, G;
   int io;       // IoType of x, B, C, y and of the chunk states
   int Q;        // chunk length
@@ -123,8 +133,6 @@ hipError_t launch_fused_forward(const Plan& p, const FusedArgs& a, hipStream_t s
 // from its window's local state and the state entering the window's chunk.
 hipError_t launch_build_packed_tables(const int32_t* cu, int64_t S, int64_t T, int Q, int64_t nc, uint8_t* seg_start,
                                       ChunkInfo* wtab, int32_t* cross_end, hipStream_t s);
-hipError_t launch_packed_finals(const Plan& p, const ChunkInfo* wtab, int64_t S, const void* states_w,
-                                const float* cs_w, float* finals, hipStream_t s);
 
 hipError_t launch_conv1d_split(const Plan& p, int K, const void* xbc, const float* w, const float* bias, int act,
                                const float* st_in, float* st_out, void* x, void* B, void* C, hipStream_t s);

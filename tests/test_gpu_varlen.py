@@ -90,10 +90,13 @@ def test_final_states_do_not_change_y():
 
 
 @pytest.mark.parametrize("L,Q,H", [(700, 256, 4), (300, 64, 4), (16700, 256, 4)])
-def test_one_sequence_equals_the_batched_split_path_bitwise(L, Q, H):
+def test_one_sequence_equals_the_batched_split_path(L, Q, H):
     """One sequence: no start after token 0, so the fixed chunks are the
-    batched layout's at batch 1 and the two paths give the same bits (at
-    16700 tokens both cut state passing into segments)."""
+    batched layout's at batch 1 and y has the batched split path's bits (at
+    16700 tokens both cut state passing into segments). The final state
+    differs only in that the end window keeps its local state in fp32 where
+    the batched path rounds the last chunk state to bf16: within 2^-8 of
+    max|final state|."""
     lib = ssd()
     cfg = BASE.with_(batch=1, seqlen=L, nheads=H, ngroups=2, init_state=False)
     inp = make_inputs(cfg, seed=91)
@@ -103,4 +106,6 @@ def test_one_sequence_equals_the_batched_split_path_bitwise(L, Q, H):
     cu = torch.tensor([0, L], dtype=torch.int32, device=DEV)
     y2, h2 = lib.forward_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], cu_seqlens=cu, chunk_size=Q)
     torch.cuda.synchronize()
-    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    assert torch.equal(y1, y2)
+    scale = h1.abs().max().item()
+    assert (h2 - h1).abs().max().item() <= 2.0 ** -8 * scale
