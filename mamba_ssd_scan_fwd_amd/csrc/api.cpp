@@ -177,9 +177,9 @@ ssd_status_t make_varlen_plan(const ssd_desc_t* d, int64_t num_seqs, Plan* p) {
 // (the plan of one sequence of T tokens), plus one end window per sequence.
 // Workspace: dA_cumsum, dt_chunked, states of the chunks; the segmented
 // state-passing scratch where it applies; the per-token sequence-start
-// flags; the window table; the per-chunk crossing sequence.
+// flags; the window table.
 struct PackedLayout {
-  size_t cs_off, dt_off, st_off, sp_off, seg_off, wtab_off, xend_off, total;
+  size_t cs_off, dt_off, st_off, sp_off, seg_off, wtab_off, total;
 };
 Plan packed_chunk_plan(const Plan& pv) {
   Plan pm = pv;
@@ -204,8 +204,7 @@ PackedLayout packed_layout(const Plan& pm, int64_t S) {
   }
   w.seg_off = end;
   w.wtab_off = align_up(w.seg_off + size_t(pm.L), kWsAlign);
-  w.xend_off = align_up(w.wtab_off + size_t(S) * sizeof(ChunkInfo), kWsAlign);
-  w.total = align_up(w.xend_off + size_t(pm.nc) * sizeof(int32_t), kWsAlign);
+  w.total = align_up(w.wtab_off + size_t(S) * sizeof(ChunkInfo), kWsAlign);
   return w;
 }
 
@@ -619,16 +618,24 @@ ssd_status_t ssd_forward_varlen(const ssd_desc_t* desc, const int32_t* cu_seqlen
     void* states = w + pl.st_off;
     uint8_t* seg = reinterpret_cast<uint8_t*>(w + pl.seg_off);
     ssd::ChunkInfo* wtab = reinterpret_cast<ssd::ChunkInfo*>(w + pl.wtab_off);
-    int32_t* xend = final_states != nullptr ? reinterpret_cast<int32_t*>(w + pl.xend_off) : nullptr;
     Plan pc = v.pm;
     pc.seg_start = seg;
-    pc.cross_end = xend;             // state passing leaves the entering states of the
-    pc.cross_hin = final_states;     // sequences that cross into their last chunk here
-    e = ssd::launch_build_packed_tables(cu_seqlens, num_seqs, pc.L, pc.Q, pc.nc, seg, wtab, xend, s);
+    // the tables kernel also clears the segmented state passing's scratch
+    // and writes the status record
+    const bool seg_sp = pl.sp_off != 0;
+    uint32_t* clr = nullptr;
+    int64_t nclr = 0;
+    if (seg_sp) {
+      const ssd::SegScratch sc = ssd::seg_scratch_layout(pc, w + pl.sp_off);
+      clr = sc.flags;
+      nclr = sc.nwords;
+    }
+    e = ssd::launch_build_packed_tables(cu_seqlens, num_seqs, pc.L, pc.Q, seg, wtab, clr, nclr,
+                                        seg_sp ? stat : nullptr, ssd::kPathSplitSegmented, s);
     if (e == hipSuccess) e = ssd::run_cumsum_chunk_state(pc, x, B, dt, A, cs, dtc, states, s);
     if (e == hipSuccess) {
-      if (pl.sp_off != 0)
-        e = ssd::launch_state_passing_seg(pc, states, cs, nullptr, nullptr, w + pl.sp_off, stat, s);
+      if (seg_sp)
+        e = ssd::launch_state_passing_seg(pc, states, cs, nullptr, nullptr, w + pl.sp_off, stat, s, true);
       else
         e = ssd::launch_state_passing(pc, states, cs, nullptr, nullptr, s, stat);
     }
@@ -639,9 +646,10 @@ ssd_status_t ssd_forward_varlen(const ssd_desc_t* desc, const int32_t* cu_seqlen
       Plan pw = pc;
       pw.ctab = wtab;
       pw.nc = num_seqs;
-      pw.cross_end = nullptr;
-      pw.cross_hin = nullptr;
+      pw.seg_start = nullptr;  // a window holds one sequence's tokens
       pw.window_finals = final_states;
+      pw.window_hin = states;
+      pw.window_nc = pc.nc;
       e = ssd::launch_cumsum_chunk_state_mfma(pw, x, B, dt, A, nullptr, nullptr, nullptr, s);
     }
   } else {

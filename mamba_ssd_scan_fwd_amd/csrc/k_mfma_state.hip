@@ -96,9 +96,12 @@ __device__ __forceinline__ int bsw(int j) {
 // writes them to the workspace for the later steps (the workgroup of the
 // first block of state columns does).
 // MODE kWindowFinals: as kFuseCumsum over the end windows of packed
-// sequences (ctab = the window table), writing each sequence's fp32 final
-// state to `fin` instead of a chunk state, and no cumsum (an instantiation
-// of its own, so the other modes keep their register budget).
+// sequences (ctab = the window table, slot c = sequence c), writing each
+// sequence's fp32 final state to `fin` instead of a chunk state and no
+// cumsum; for a window that continues a sequence from earlier chunks it adds
+// the decayed state entering the window's chunk, read from hin ([H, hnc,
+// P, N] bf16, the fixed chunks' entering states after state passing). An
+// instantiation of its own, so the other modes keep their register budget.
 constexpr int kReadCumsum = 0, kFuseCumsum = 1, kWindowFinals = 2;
 template <int P, int NB, int Q, int MODE>
 __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
@@ -106,7 +109,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const float* __restrict__ dt, const float* __restrict__ A,
     float* __restrict__ dA_cs, float* __restrict__ dtc,
     uint16_t* __restrict__ states, int64_t L, int H, int G, int N, int64_t nc, int HB, DtOpts dto,
-    const ChunkInfo* __restrict__ ctab, const uint8_t* __restrict__ seg, float* __restrict__ fin) {
+    const ChunkInfo* __restrict__ ctab, const uint8_t* __restrict__ seg, float* __restrict__ fin,
+    const uint16_t* __restrict__ hin, int64_t hnc) {
   using C = StateCfg<P, NB, Q>;
   constexpr bool FUSED = MODE != kReadCumsum;
   constexpr bool WIN = MODE == kWindowFinals;
@@ -329,6 +333,25 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     uint4* cur = lds + (hh & 1) * C::X_FRAGS;
     fetch_x(mine, min(h + 1, hlast));
 
+    // end windows that continue a sequence: the entering state's four bf16
+    // of each tile, loaded now so the loads overlap the products
+    uint2 hv[C::TN][C::TP];
+    if constexpr (WIN) {
+      if (cross) {
+        const uint16_t* hp = hin + ((int64_t)h * hnc + row0 / Q) * (int64_t)P * N;
+#pragma unroll
+        for (int tp = 0; tp < C::TP; ++tp) {
+          const int pt = wp * C::TP + tp;
+          if (C::WP * C::TP == C::NT_P || pt < C::NT_P) {
+#pragma unroll
+            for (int tn = 0; tn < C::TN; ++tn) {
+              const int n = nb * NB + (wn * C::TN + tn) * 16 + 4 * g4;
+              hv[tn][tp] = *reinterpret_cast<const uint2*>(hp + (int64_t)(pt * 16 + r16) * N + n);
+            }
+          }
+        }
+      }
+    }
     f32x4_t acc[C::TN][C::TP];
 #pragma unroll
     for (int tn = 0; tn < C::TN; ++tn)
@@ -358,8 +381,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     if constexpr (WIN) {
       // end window of a packed sequence (batch 1, slot c = the sequence): its
       // final state in fp32, the window's state plus, for a sequence that
-      // started earlier, exp(l at its last token) times the fp32 state
-      // entering the chunk (left at the same place by state passing)
+      // started earlier, exp(l at its last token) times the state entering
+      // the chunk (the window then starts at the chunk's first row)
       const float carry = cross ? __expf(tab[2 * hh * Q + rows - 1]) : 0.f;
       float* o = fin + ((int64_t)c * H + h) * (int64_t)P * N;
 #pragma unroll
@@ -373,11 +396,11 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
             float4* q = reinterpret_cast<float4*>(o + (int64_t)p * N + n);
             f32x4_t v = acc[tn][tp];
             if (cross) {
-              const float4 t = *q;
-              v[0] = fmaf(carry, t.x, v[0]);
-              v[1] = fmaf(carry, t.y, v[1]);
-              v[2] = fmaf(carry, t.z, v[2]);
-              v[3] = fmaf(carry, t.w, v[3]);
+              const uint2 t = hv[tn][tp];
+              v[0] = fmaf(carry, __uint_as_float(t.x << 16), v[0]);
+              v[1] = fmaf(carry, __uint_as_float(t.x & 0xffff0000u), v[1]);
+              v[2] = fmaf(carry, __uint_as_float(t.y << 16), v[2]);
+              v[3] = fmaf(carry, __uint_as_float(t.y & 0xffff0000u), v[3]);
             }
             *q = make_float4(v[0], v[1], v[2], v[3]);
           }
@@ -424,7 +447,9 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 
 // Heads per workgroup: a divisor of the heads in one B/C group, at most 8,
 // as large as keeps the grid at >= 512 workgroups (two resident per compute
-// unit; the B^T staging is amortised over more heads).
+// unit; the B^T staging is amortised over more heads). The end windows of
+// packed sequences take the same rule: measured on the 32-sequence workload,
+// grids of 1024 and 2048 smaller workgroups were 2% and 5% slower overall.
 int pick_heads_per_wg(const Plan& p, int nnb) {
   const int64_t hpg = p.H / p.G;
   const int64_t base = p.batch * p.nc * nnb * p.H;
@@ -442,7 +467,8 @@ hipError_t launch_pnq(const Plan& p, const void* x, const void* B, const float* 
   chunk_state_mfma_kernel<P, NB, Q, MODE><<<dim3((unsigned)grid), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), dt, A, cs, dtc,
       static_cast<uint16_t*>(st), p.L, (int)p.H, (int)p.G, (int)p.N, p.nc, hb, p.dto, p.ctab,
-      MODE != kReadCumsum ? p.seg_start : nullptr, MODE == kWindowFinals ? p.window_finals : nullptr);
+      MODE == kFuseCumsum ? p.seg_start : nullptr, MODE == kWindowFinals ? p.window_finals : nullptr,
+      MODE == kWindowFinals ? static_cast<const uint16_t*>(p.window_hin) : nullptr, p.window_nc);
   return hipGetLastError();
 }
 

@@ -73,15 +73,12 @@ template <> struct Vec8<__hip_bfloat16> {
 // sequence; with packed sequences (seqtab != nullptr, batch 1) chain
 // bh = s*H + h walks the seqtab[s].y chunk slots from seqtab[s].x of head h,
 // so every sequence is a chain of its own. h0 and hT are indexed by the chain.
-// With xend (packed sequences in fixed chunks, batch 1): at chunk c with
-// xend[c] = q >= 0, the fp32 state entering the chunk is also stored to
-// xhin[q, h] (q's final state is completed from it).
 template <typename TS, int PF>
 __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     TS* __restrict__ states, const float* __restrict__ dA_cs,
     const float* h0, float* hT,  // may be the same buffer (in-place update)
     int64_t nc, int Q, int PN, int H, const int2* __restrict__ seqtab, uint32_t* __restrict__ stat,
-    uint32_t tag, const int32_t* __restrict__ xend, float* __restrict__ xhin) {
+    uint32_t tag) {
   const int64_t bh = blockIdx.x;
   if (stat != nullptr && bh == 0 && blockIdx.y == 0 && threadIdx.x == 0) {  // the forward's status record
     stat[0] = tag;
@@ -119,26 +116,22 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     if (active && k < cnt) ring[k].load(s + (int64_t)k * PN);
 
   float dec = 0.f;
-  int xq = -1;
   for (int64_t c0 = 0; c0 < cnt; c0 += PF) {
 #pragma unroll
     for (int k = 0; k < PF; ++k) {
       const int64_t c = c0 + k;
       if (c < cnt) {
-        if ((c & 63) == 0) {  // refresh: lane l holds exp(Lam_{c+l}) (and xend[c+l])
+        if ((c & 63) == 0) {  // refresh: lane l holds exp(Lam_{c+l})
           const int64_t cl = c + lane;
           dec = cl < cnt ? __expf(lam[cl * Q]) : 0.f;
-          if (xend != nullptr) xq = cl < cnt ? xend[c_beg + cl] : -1;
         }
         const float d = __int_as_float(
             __builtin_amdgcn_readlane(__float_as_int(dec), (int)(c & 63)));
-        const int q = __builtin_amdgcn_readlane(xq, (int)(c & 63));  // wavefront-uniform
         if (active) {
           float sv[kVec];
           ring[k].to(sv);
           if (c + PF < cnt) ring[k].load(s + (c + PF) * PN);
           Vec8<TS>::store(s + c * PN, h);
-          if (q >= 0) Vec8<float>::store(xhin + ((int64_t)q * H + row) * PN + e0, h);
 #pragma unroll
           for (int e = 0; e < kVec; ++e) h[e] = fmaf(d, h[e], sv[e]);
         }
@@ -170,13 +163,12 @@ constexpr int kSegChunks = 32;
 constexpr int kSpinLimit = 1 << 18;
 constexpr uint32_t kCutOffBit = 2u;  // in the forward's status word (bit 0 is the one-pass kernel's)
 
-// xend / xhin as for state_passing_kernel (batch 1: the chain is the head).
 template <typename TS, int KS>
 __global__ __launch_bounds__(kThreads) void state_passing_seg_kernel(
     TS* __restrict__ states, const float* __restrict__ dA_cs, const float* h0, float* hT,
     float* __restrict__ agg, float* __restrict__ agg_lam, uint32_t* __restrict__ flags,
     uint32_t* __restrict__ ticket, uint32_t* __restrict__ status, int64_t nc, int Q, int PN, int64_t chains,
-    int nslice, int nseg, const int32_t* __restrict__ xend, float* __restrict__ xhin) {
+    int nslice, int nseg) {
   __shared__ uint32_t stk;
   if (threadIdx.x == 0) stk = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -201,7 +193,6 @@ __global__ __launch_bounds__(kThreads) void state_passing_seg_kernel(
     if (active && k < cnt) sv[k].load(s + (int64_t)k * PN);
   const float lam_l = lane < cnt ? lam[(int64_t)lane * Q] : 0.f;
   const float dec_l = __expf(lam_l);
-  const int xq_l = xend != nullptr && lane < cnt ? xend[c_beg + lane] : -1;
   float hin0[8];
   if (active && h0 != nullptr) {
     Vec8<float> v;
@@ -281,12 +272,10 @@ __global__ __launch_bounds__(kThreads) void state_passing_seg_kernel(
   for (int k = 0; k < KS; ++k) {
     if (k < cnt) {
       const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dec_l), k));
-      const int q = __builtin_amdgcn_readlane(xq_l, k);  // wavefront-uniform
       if (active) {
         float v[8];
         sv[k].to(v);
         Vec8<TS>::store(s + (int64_t)k * PN, h);
-        if (q >= 0) Vec8<float>::store(xhin + ((int64_t)q * chains + bh) * PN + e0, h);
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = fmaf(d, h[e], v[e]);
       }
@@ -311,28 +300,29 @@ hipError_t launch_typed(const Plan& p, void* states, const float* dA_cs,
   const int64_t chains = p.seqtab != nullptr ? p.nseq * p.H : p.batch * p.H;
   dim3 grid((unsigned)chains, (unsigned)((PN + kThreads * kVec - 1) / (kThreads * kVec)));
   state_passing_kernel<TS, 8><<<grid, kThreads, 0, s>>>(
-      static_cast<TS*>(states), dA_cs, h0, hT, p.nc, p.Q, PN, (int)p.H, p.seqtab, stat, kPathSplit, p.cross_end,
-      p.cross_hin);
+      static_cast<TS*>(states), dA_cs, h0, hT, p.nc, p.Q, PN, (int)p.H, p.seqtab, stat, kPathSplit);
   return hipGetLastError();
 }
 
 template <typename TS>
 hipError_t launch_seg_typed(const Plan& p, void* states, const float* dA_cs, const float* h0, float* hT,
-                            void* scratch, uint32_t* stat, hipStream_t s) {
+                            void* scratch, uint32_t* stat, bool cleared, hipStream_t s) {
   const int PN = (int)(p.P * p.N);
   const int64_t chains = p.batch * p.H;
   const int nslice = (PN + kThreads * kVec - 1) / (kThreads * kVec);
   const int nseg = (int)((p.nc + kSegChunks - 1) / kSegChunks);
   SegScratch sc = seg_scratch_layout(p, scratch);
-  const int64_t nclear = sc.nwords;
-  clear_words_kernel<<<dim3((unsigned)((nclear + 255) / 256)), 256, 0, s>>>(sc.flags, nclear, stat,
-                                                                             kPathSplitSegmented);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!cleared) {
+    const int64_t nclear = sc.nwords;
+    clear_words_kernel<<<dim3((unsigned)((nclear + 255) / 256)), 256, 0, s>>>(sc.flags, nclear, stat,
+                                                                               kPathSplitSegmented);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t grid = chains * nslice * nseg;
   state_passing_seg_kernel<TS, kSegChunks><<<dim3((unsigned)grid), kThreads, 0, s>>>(
       static_cast<TS*>(states), dA_cs, h0, hT, sc.agg, sc.agg_lam, sc.flags, sc.ticket,
-      stat != nullptr ? stat + 1 : sc.status, p.nc, p.Q, PN, chains, nslice, nseg, p.cross_end, p.cross_hin);
+      stat != nullptr ? stat + 1 : sc.status, p.nc, p.Q, PN, chains, nslice, nseg);
   return hipGetLastError();
 }
 
@@ -378,9 +368,9 @@ SegScratch seg_scratch_layout(const Plan& p, void* base) {
 }
 
 hipError_t launch_state_passing_seg(const Plan& p, void* states, const float* dA_cs, const float* h0, float* hT,
-                                    void* scratch, uint32_t* stat, hipStream_t s) {
-  if (p.io == kBF16) return launch_seg_typed<__hip_bfloat16>(p, states, dA_cs, h0, hT, scratch, stat, s);
-  return launch_seg_typed<float>(p, states, dA_cs, h0, hT, scratch, stat, s);
+                                    void* scratch, uint32_t* stat, hipStream_t s, bool cleared) {
+  if (p.io == kBF16) return launch_seg_typed<__hip_bfloat16>(p, states, dA_cs, h0, hT, scratch, stat, cleared, s);
+  return launch_seg_typed<float>(p, states, dA_cs, h0, hT, scratch, stat, cleared, s);
 }
 
 hipError_t launch_state_passing(const Plan& p, void* states, const float* dA_cs,

@@ -99,11 +99,10 @@ __device__ __forceinline__ int64_t clamped_start(const int32_t* cu, int64_t s, i
 
 // seg_start[t] = 1 where a non-empty sequence starts after token 0 (nothing
 // precedes token 0, so no decay has to be cut there). wtab[s] = the end
-// window of sequence s: its last token's chunk from that chunk's first row to
-// the last token (rows 0 for an empty sequence), flags kWindowCrossing when
-// the sequence started in an earlier chunk. cross_end[c] = the sequence that
-// holds chunk c's first token, started earlier and ends in chunk c, else -1
-// (with valid offsets, at most one sequence per chunk).
+// window of sequence s: from the later of its first token and its last
+// token's chunk start, to its last token (rows 0 for an empty sequence), so
+// it holds tokens of s only; flags kWindowCrossing when s started in an
+// earlier chunk. Also zeroes clear[0, nclear) and writes the status record.
 __device__ __forceinline__ int64_t seq_holding(const int32_t* cu, int64_t S, int64_t T, int64_t t) {
   // the last sequence whose start is <= t: with valid offsets, the non-empty
   // sequence that holds t (an empty one starts where the next one does)
@@ -119,12 +118,17 @@ __device__ __forceinline__ int64_t seq_holding(const int32_t* cu, int64_t S, int
 }
 
 __global__ __launch_bounds__(256) void build_packed_tables_kernel(const int32_t* __restrict__ cu, int64_t S,
-                                                                  int64_t T, int Q, int64_t nc,
-                                                                  uint8_t* __restrict__ seg_start,
+                                                                  int64_t T, int Q, uint8_t* __restrict__ seg_start,
                                                                   ChunkInfo* __restrict__ wtab,
-                                                                  int32_t* __restrict__ cross_end) {
+                                                                  uint32_t* __restrict__ clear, int64_t nclear,
+                                                                  uint32_t* __restrict__ stat, uint32_t tag) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (stat != nullptr && i0 == 0) {
+    stat[0] = tag;
+    stat[1] = 0u;
+  }
+  for (int64_t i = i0; i < nclear; i += stride) clear[i] = 0u;
   for (int64_t t = i0; t < T; t += stride)
     seg_start[t] = t > 0 && clamped_start(cu, seq_holding(cu, S, T, t), T) == t ? 1 : 0;
   for (int64_t s = i0; s < S; s += stride) {
@@ -134,30 +138,23 @@ __global__ __launch_bounds__(256) void build_packed_tables_kernel(const int32_t*
       wtab[s] = ChunkInfo{0, 0, (int32_t)s, 0};
     } else {
       const int64_t e = start + len - 1;
-      const int64_t t0 = e / Q * Q;
-      wtab[s] = ChunkInfo{(int32_t)t0, (int32_t)(e - t0 + 1), (int32_t)s, start < t0 ? kWindowCrossing : 0};
-    }
-  }
-  if (cross_end != nullptr) {
-    for (int64_t c = i0; c < nc; c += stride) {
-      const int64_t t0 = c * Q;
-      const int64_t s = seq_holding(cu, S, T, t0);
-      int64_t start, len;
-      seq_span(cu, s, T, start, len);
-      const bool crosses = len > 0 && start < t0 && (start + len - 1) / Q == c;
-      cross_end[c] = crosses ? (int32_t)s : -1;
+      const int64_t c0 = e / Q * Q;
+      const int64_t t0 = start > c0 ? start : c0;
+      wtab[s] = ChunkInfo{(int32_t)t0, (int32_t)(e - t0 + 1), (int32_t)s, start < c0 ? kWindowCrossing : 0};
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_build_packed_tables(const int32_t* cu, int64_t S, int64_t T, int Q, int64_t nc, uint8_t* seg_start,
-                                      ChunkInfo* wtab, int32_t* cross_end, hipStream_t s) {
-  const int64_t work = T > S ? T : S;
+hipError_t launch_build_packed_tables(const int32_t* cu, int64_t S, int64_t T, int Q, uint8_t* seg_start,
+                                      ChunkInfo* wtab, uint32_t* clear, int64_t nclear, uint32_t* stat,
+                                      uint32_t tag, hipStream_t s) {
+  int64_t work = T > S ? T : S;
+  if (nclear > work) work = nclear;
   const int64_t blocks = (work + 255) / 256 < 4096 ? (work + 255) / 256 : 4096;
-  build_packed_tables_kernel<<<dim3((unsigned)(blocks > 0 ? blocks : 1)), 256, 0, s>>>(cu, S, T, Q, nc, seg_start,
-                                                                                     wtab, cross_end);
+  build_packed_tables_kernel<<<dim3((unsigned)(blocks > 0 ? blocks : 1)), 256, 0, s>>>(cu, S, T, Q, seg_start, wtab,
+                                                                                     clear, nclear, stat, tag);
   return hipGetLastError();
 }
 

@@ -24,10 +24,10 @@ struct ChunkInfo {
   int32_t t0, rows, seq, flags;
 };
 constexpr int32_t kFirstChunk = 1, kLastChunk = 2;
-// End windows of packed sequences in fixed chunks (one slot per sequence: its
-// last token's chunk, from that chunk's first row to the token): the
-// sequence started in an earlier chunk, so its final state takes the decayed
-// state entering the window's chunk.
+// End windows of packed sequences in fixed chunks (one slot per sequence:
+// from the later of its first token and its last token's chunk start, to its
+// last token): the sequence started in an earlier chunk, so its final state
+// takes the decayed state entering the window's chunk.
 constexpr int32_t kWindowCrossing = 4;
 // The chunk count of a sequence is also kept per sequence (first slot, count)
 // so that state passing can run one chain per sequence.
@@ -41,17 +41,14 @@ struct Plan {
   // packed sequences in fixed chunks: 1 at every token where a sequence
   // starts (the cumsum's jumps, kSegJump), else nullptr
   const uint8_t* seg_start = nullptr;
-  // ... and their final states wanted (batch 1): per chunk, the sequence that
-  // enters it from an earlier chunk and ends in it (else -1), and where state
-  // passing leaves, in fp32, the state entering that chunk for that sequence
-  // ([S, H, P, N]); both nullptr otherwise
-  const int32_t* cross_end = nullptr;
-  float* cross_hin = nullptr;
-  // end windows (ctab = the window table, nc = S): the chunk-state kernel
-  // writes each sequence's fp32 final state here ([S, H, P, N], holding the
-  // entering states state passing left for the crossing sequences) instead
-  // of chunk states
+  // end windows of packed sequences (ctab = the window table, nc = S, batch
+  // 1): the chunk-state kernel writes each sequence's fp32 final state here
+  // ([S, H, P, N]) instead of chunk states, taking the states entering the
+  // fixed chunks (bf16 [H, window_nc, P, N], after state passing) from
+  // window_hin
   float* window_finals = nullptr;
+  const void* window_hin = nullptr;
+  int64_t window_nc = 0;
   int64_t batch, L, H, P, N, G;
   int io;       // IoType of x, B, C, y and of the chunk states
   int Q;        // chunk length
@@ -92,8 +89,11 @@ bool seg_state_passing_applies(const Plan& p);
 SegScratch seg_scratch_layout(const Plan& p, void* base);
 // stat: the forward's status record, tagged kPathSplitSegmented; a cut-off
 // wait sets bit 1 of its status word.
+// cleared: the scratch's flags, ticket and status words are already zero and
+// the record written (by an earlier kernel on the stream), so the launch
+// skips its clearing kernel.
 hipError_t launch_state_passing_seg(const Plan& p, void* states, const float* dA_cs, const float* h0, float* hT,
-                                    void* scratch, uint32_t* stat, hipStream_t s);
+                                    void* scratch, uint32_t* stat, hipStream_t s, bool cleared = false);
 int64_t seg_state_passing_grid(const Plan& p);  // workgroups (= tickets) of one launch
 hipError_t launch_chunk_scan(const Plan& p, const void* x, const void* B, const void* C,
                              const float* D, const float* dA_cs, const float* dtc,
@@ -131,8 +131,11 @@ hipError_t launch_fused_forward(const Plan& p, const FusedArgs& a, hipStream_t s
 // start flags and, per sequence, its end window (from the start of the chunk
 // holding its last token to that token); then each sequence's final state
 // from its window's local state and the state entering the window's chunk.
-hipError_t launch_build_packed_tables(const int32_t* cu, int64_t S, int64_t T, int Q, int64_t nc, uint8_t* seg_start,
-                                      ChunkInfo* wtab, int32_t* cross_end, hipStream_t s);
+// Also zeroes clear[0, nclear) and, when stat is given, writes the status
+// record {tag, 0}.
+hipError_t launch_build_packed_tables(const int32_t* cu, int64_t S, int64_t T, int Q, uint8_t* seg_start,
+                                      ChunkInfo* wtab, uint32_t* clear, int64_t nclear, uint32_t* stat,
+                                      uint32_t tag, hipStream_t s);
 
 hipError_t launch_conv1d_split(const Plan& p, int K, const void* xbc, const float* w, const float* bias, int act,
                                const float* st_in, float* st_out, void* x, void* B, void* C, hipStream_t s);

@@ -268,10 +268,9 @@ def test_varlen_validates():
                                   slots * 16, 7 * 8))
     # fixed chunks of the packed stream (bf16 without): 40 chunks (too few
     # for the segmented state passing), 10000 start flags, the table of 7 end
-    # windows, the crossing sequence of each chunk
+    # windows
     nc = -(-10000 // 256)
-    packed = sum(up(b) for b in (64 * nc * 256 * 4, 64 * nc * 256 * 4, 64 * nc * 64 * 128 * 2, 10000, 7 * 16,
-                                 nc * 4))
+    packed = sum(up(b) for b in (64 * nc * 256 * 4, 64 * nc * 256 * 4, 64 * nc * 64 * 128 * 2, 10000, 7 * 16))
     assert n.value == max(per_seq, packed) + 256  # then the status record
     p = [ctypes.c_void_p(BASE + k * (1 << 30)) for k in range(12)]
     # cu x dt A B C D h0 y hT ws

@@ -94,9 +94,10 @@ def test_one_sequence_equals_the_batched_split_path(L, Q, H):
     """One sequence: no start after token 0, so the fixed chunks are the
     batched layout's at batch 1 and y has the batched split path's bits (at
     16700 tokens both cut state passing into segments). The final state
-    differs only in that the end window keeps its local state in fp32 where
-    the batched path rounds the last chunk state to bf16: within 2^-8 of
-    max|final state|."""
+    differs in two roundings: the end window keeps its local state in fp32
+    where the batched path rounds the last chunk state to bf16, and carries
+    the entering state as stored for the chunk scan (bf16) where the batched
+    path keeps it in fp32: within 2^-7 of max|final state|."""
     lib = ssd()
     cfg = BASE.with_(batch=1, seqlen=L, nheads=H, ngroups=2, init_state=False)
     inp = make_inputs(cfg, seed=91)
@@ -108,4 +109,4 @@ def test_one_sequence_equals_the_batched_split_path(L, Q, H):
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     scale = h1.abs().max().item()
-    assert (h2 - h1).abs().max().item() <= 2.0 ** -8 * scale
+    assert (h2 - h1).abs().max().item() <= 2.0 ** -7 * scale
