@@ -402,31 +402,6 @@ SSD_API ssd_status_t ssd_conv1d_split(const ssd_desc_t* desc, int32_t conv_width
                               const float* conv_state_in, float* conv_state_out,
                               void* x, void* B, void* C, void* stream);
 
-/* The short causal convolution and the whole forward pass in one call, the
- * convolution applied inside the forward's first kernel as it loads its
- * tiles (the Mamba-2 block's input path: Telegram post "Mamba3", paragraph on
- * the removed short causal convolution). Same result, bit for bit, as
- * ssd_conv1d_split(desc, conv_width, xbc, weight, bias, silu, conv_state_in,
- * conv_state_out, x, B, C) followed by ssd_forward_split(desc, x, dt, A, B,
- * C, D, init_state, y, final_state, ...), but the first kernel reads the
- * packed activations instead of x and B: one launch and one read of x fewer.
- * The convolved x, B, C are still written (the chunk scan reads them).
- *   xbc, weight, bias, silu, conv_state_in, conv_state_out, conv_width  as
- *       for ssd_conv1d_split; conv_state_in's values are used rounded to
- *       bf16 (exact for a state this library wrote: it holds past inputs).
- *   dt, A, D, init_state, y, final_state, workspace (ssd_workspace_bytes()
- *       bytes, nullable)  as for ssd_forward.
- *   x [batch, L, H, P], B, C [batch, L, G, N]  outputs, io dtype.
- * Always the split path (the status record names it). bf16 io only
- * (SSD_ERR_UNSUPPORTED for fp32 or a width outside 1..4). Outputs must not
- * overlap any input or each other, except final_state == init_state. */
-SSD_API ssd_status_t ssd_forward_conv(const ssd_desc_t* desc, int32_t conv_width, const void* xbc,
-                              const float* weight, const float* bias, int32_t silu,
-                              const float* conv_state_in, float* conv_state_out,
-                              const float* dt, const float* A, const float* D, const float* init_state,
-                              void* x, void* B, void* C, void* y, float* final_state,
-                              void* workspace, size_t workspace_bytes, void* stream);
-
 /* ---- the recurrent (decode) step ------------------------------------------ */
 
 /* One token of a batch of sequences through the recurrence, the state kept

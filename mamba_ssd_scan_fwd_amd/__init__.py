@@ -22,7 +22,6 @@ from .binding import (  # noqa: F401
     decode_step,
     effective_chunk_size,
     forward,
-    forward_conv,
     forward_noalloc,
     forward_varlen,
     lib_path,

@@ -35,7 +35,6 @@ __all__ = [
     "decode_step",
     "forward_varlen",
     "conv1d_split",
-    "forward_conv",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -61,7 +60,6 @@ EXPORTED_SYMBOLS = (
     "ssd_forward_varlen",
     "ssd_workspace_status_varlen",
     "ssd_conv1d_split",
-    "ssd_forward_conv",
 )
 
 SSD_DTYPE_F32 = 0
@@ -155,9 +153,6 @@ def load_library():
         lib.ssd_forward_varlen.restype = ctypes.c_int
         lib.ssd_conv1d_split.argtypes = [dp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
         lib.ssd_conv1d_split.restype = ctypes.c_int
-        lib.ssd_forward_conv.argtypes = [dp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
-                                         vp]
-        lib.ssd_forward_conv.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -573,43 +568,3 @@ def conv1d_split(xbc, weight, bias=None, *, nheads, headdim, ngroups, dstate, si
                                            _ptr(conv_state_out), _ptr(x), _ptr(B), _ptr(C), _stream(stream, dev)),
            "ssd_conv1d_split")
     return x, B, C
-
-
-def forward_conv(xbc, weight, dt, A, D=None, init_state=None, *, nheads, headdim, ngroups, dstate, bias=None,
-                 silu=True, conv_state_in=None, conv_state_out=None, chunk_size: int = 0, dt_pre=None,
-                 return_final_state: bool = True, workspace=None, stream=None):
-    """ssd_forward_conv: the short causal convolution of the packed [x | B | C]
-    activations (xbc [b, L, CH] bf16, weight [CH, K] fp32) and the forward
-    pass in one call, the convolution applied by the forward's first kernel.
-    Returns (y, final_state or None, x, B, C), x, B, C being the convolved
-    activations."""
-    dev = xbc.device
-    _need(xbc, "xbc", device=dev)
-    bsz, L, CH = xbc.shape
-    H, P, G, N = nheads, headdim, ngroups, dstate
-    if CH != H * P + 2 * G * N:
-        raise ValueError("xbc channels must be H*P + 2*G*N")
-    _need(weight, "weight", torch.float32, dev)
-    K = weight.shape[1]
-    if bias is not None:
-        _need(bias, "bias", torch.float32, dev, (CH,))
-    _need(dt, "dt", torch.float32, dev, (bsz, L, H))
-    _need(A, "A", torch.float32, dev, (H,))
-    if D is not None:
-        _need(D, "D", torch.float32, dev, (H,))
-    if init_state is not None:
-        _need(init_state, "init_state", torch.float32, dev, (bsz, H, P, N))
-    desc = make_desc(bsz, L, H, P, N, G, xbc.dtype, chunk_size, **_dt_kw(dt_pre, H, dev))
-    x = torch.empty((bsz, L, H, P), dtype=xbc.dtype, device=dev)
-    B = torch.empty((bsz, L, G, N), dtype=xbc.dtype, device=dev)
-    C = torch.empty_like(B)
-    y = torch.empty_like(x)
-    final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=dev) if return_final_state else None
-    if workspace is None:
-        workspace = torch.empty(workspace_bytes(desc), dtype=torch.uint8, device=dev)
-    _check(load_library().ssd_forward_conv(
-        ctypes.byref(desc), ctypes.c_int32(K), _ptr(xbc), _ptr(weight), _ptr(bias), ctypes.c_int32(1 if silu else 0),
-        _ptr(conv_state_in), _ptr(conv_state_out), _ptr(dt), _ptr(A), _ptr(D), _ptr(init_state), _ptr(x), _ptr(B),
-        _ptr(C), _ptr(y), _ptr(final_state), _ptr(workspace),
-        ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream, dev)), "ssd_forward_conv")
-    return y, final_state, x, B, C

@@ -326,8 +326,7 @@ ssd_status_t check_forward(const Plan& p, const void* x, const float* dt, const 
 // when the caller passes none).
 ssd_status_t enqueue_forward(const Plan& p, bool fused, const void* x, const float* dt, const float* A,
                              const void* B, const void* C, const float* D, const float* init_state, void* y,
-                             float* final_state, void* workspace, const WsLayout& ws, hipStream_t s,
-                             const ConvArgs* conv = nullptr) {
+                             float* final_state, void* workspace, const WsLayout& ws, hipStream_t s) {
   void* wbase = workspace;
   bool owned = false;
   if (wbase == nullptr) {
@@ -352,13 +351,7 @@ ssd_status_t enqueue_forward(const Plan& p, bool fused, const void* x, const flo
     e = launch_chunk_cumsum_clear(p, dt, A, cs, dtc, sync, ws.nsync, stat, kPathOnePass, s);
     if (e == hipSuccess) e = launch_fused_forward(p, a, s);
   } else {
-    if (conv != nullptr) {  // steps 1 and 2 with the convolution (it writes x, B, C)
-      Plan pc = p;
-      pc.conv = conv;
-      e = launch_cumsum_chunk_state_mfma(pc, nullptr, nullptr, dt, A, cs, dtc, states, s);
-    } else {
-      e = run_cumsum_chunk_state(p, x, B, dt, A, cs, dtc, states, s);
-    }
+    e = run_cumsum_chunk_state(p, x, B, dt, A, cs, dtc, states, s);
     if (e == hipSuccess) {
       if (ws.sp_off != 0)
         e = launch_state_passing_seg(p, states, cs, init_state, final_state, w + ws.sp_off, stat, s);
@@ -777,70 +770,6 @@ ssd_status_t ssd_decode_step(const ssd_desc_t* desc, const void* x, const float*
   for (const ssd::Range& r : ins)
     if (ssd::overlap(rs, r) || ssd::overlap(ry, r)) return SSD_ERR_ALIAS;
   return ssd::from_hip(ssd::launch_decode_step(p, x, dt, A, B, C, D, state, y, static_cast<hipStream_t>(stream)));
-}
-
-ssd_status_t ssd_forward_conv(const ssd_desc_t* desc, int32_t conv_width, const void* xbc, const float* weight,
-                              const float* bias, int32_t silu, const float* conv_state_in, float* conv_state_out,
-                              const float* dt, const float* A, const float* D, const float* init_state, void* x,
-                              void* B, void* C, void* y, float* final_state, void* workspace, size_t workspace_bytes,
-                              void* stream) {
-  Plan p;
-  ssd_status_t st = ssd::make_plan(desc, &p);
-  if (st != SSD_OK) return st;
-  if (p.io != ssd::kBF16 || !ssd::mfma_chunk_state_supported(p) || conv_width < 1 || conv_width > 4)
-    return SSD_ERR_UNSUPPORTED;
-  if ((p.H * p.P + 2 * p.G * p.N) * 4 >= (int64_t(1) << 31)) return SSD_ERR_BAD_SHAPE;  // 32-bit channel indices
-  if (!xbc || !weight) return SSD_ERR_NULL_POINTER;
-  if (!ssd::aligned(xbc, 16) || !ssd::aligned(weight, 4) || !ssd::aligned(bias, 16) ||
-      !ssd::aligned(conv_state_in, 4) || !ssd::aligned(conv_state_out, 4))
-    return SSD_ERR_ALIGNMENT;
-  const ssd::WsLayout ws = ssd::ws_layout(p);
-  // the forward's own checks, with x, B, C (outputs here) in the place of its inputs
-  st = ssd::check_forward(p, x, dt, A, B, C, D, init_state, y, final_state, workspace, workspace_bytes, ws);
-  if (st != SSD_OK) return st;
-  const size_t io = p.io_bytes();
-  const int64_t CH = p.H * p.P + 2 * p.G * p.N;
-  const size_t km1 = size_t(conv_width - 1);
-  const size_t st_bytes = size_t(p.batch * p.H * p.P * p.N) * sizeof(float);
-  const ssd::Range ins[] = {ssd::range_of(xbc, size_t(p.batch * p.L * CH) * io),
-                            ssd::range_of(weight, size_t(CH * conv_width) * sizeof(float)),
-                            ssd::range_of(bias, bias ? size_t(CH) * sizeof(float) : 0),
-                            ssd::range_of(conv_state_in, conv_state_in ? size_t(p.batch * CH) * km1 * 4 : 0),
-                            ssd::range_of(dt, size_t(p.batch * p.L * p.H) * sizeof(float)),
-                            ssd::range_of(A, size_t(p.H) * sizeof(float)),
-                            ssd::range_of(D, size_t(p.H) * sizeof(float)),
-                            ssd::range_of(init_state, st_bytes)};
-  const ssd::Range outs[] = {ssd::range_of(x, size_t(p.batch * p.L * p.H * p.P) * io),
-                             ssd::range_of(B, size_t(p.batch * p.L * p.G * p.N) * io),
-                             ssd::range_of(C, size_t(p.batch * p.L * p.G * p.N) * io),
-                             ssd::range_of(conv_state_out, conv_state_out ? size_t(p.batch * CH) * km1 * 4 : 0),
-                             ssd::range_of(y, size_t(p.batch * p.L * p.H * p.P) * io),
-                             ssd::range_of(final_state, st_bytes),
-                             ssd::range_of(workspace, ws.total)};
-  constexpr int kOuts = 7;
-  for (int i = 0; i < kOuts; ++i) {
-    for (const ssd::Range& r : ins) {
-      // final_state may be exactly init_state (in place), as for ssd_forward
-      const bool in_place = i == 5 && r.lo == reinterpret_cast<uintptr_t>(init_state) && outs[i].lo == r.lo;
-      if (ssd::overlap(outs[i], r) && !in_place) return SSD_ERR_ALIAS;
-    }
-    for (int j = i + 1; j < kOuts; ++j)
-      if (ssd::overlap(outs[i], outs[j])) return SSD_ERR_ALIAS;
-  }
-  ssd::ConvArgs cv;
-  cv.xbc = static_cast<const uint16_t*>(xbc);
-  cv.w = weight;
-  cv.bias = bias;
-  cv.st_in = conv_state_in;
-  cv.st_out = conv_state_out;
-  cv.xo = static_cast<uint16_t*>(x);
-  cv.bo = static_cast<uint16_t*>(B);
-  cv.co = static_cast<uint16_t*>(C);
-  cv.K = conv_width;
-  cv.silu = silu != 0 ? 1 : 0;
-  cv.CH = (int)CH;
-  return ssd::enqueue_forward(p, false, x, dt, A, B, C, D, init_state, y, final_state, workspace, ws,
-                              static_cast<hipStream_t>(stream), &cv);
 }
 
 ssd_status_t ssd_conv1d_split(const ssd_desc_t* desc, int32_t conv_width, const void* xbc, const float* weight,

@@ -16,7 +16,7 @@
 // access per token) and walks a tile of kTT tokens, kU tokens' loads at a
 // time, keeping the K-1 previous inputs in registers, so every input is read
 // once per tile plus a K-1 halo.
-#include "conv_math.h"
+#include "ssd_internal.h"
 
 namespace ssd {
 namespace {
@@ -42,6 +42,9 @@ template <> struct V4<__hip_bfloat16> {
   }
 };
 
+// z * sigmoid(z), with the hardware reciprocal (about 1 ulp) instead of an
+// IEEE division
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
 template <typename TIO, int K>
 __global__ __launch_bounds__(kThreads) void conv1d_split_kernel(
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void conv1d_split_kernel(
           z.z = fmaf(wk[k].z, v.z, z.z);
           z.w = fmaf(wk[k].w, v.w, z.w);
         }
-        if (act) z = make_float4(conv_silu(z.x), conv_silu(z.y), conv_silu(z.z), conv_silu(z.w));
+        if (act) z = make_float4(silu(z.x), silu(z.y), silu(z.z), silu(z.w));
         V4<TIO>::store(out + (tb + u) * ostride, z);
 #pragma unroll
         for (int k = 0; k + 1 < K - 1; ++k) hist[k] = hist[k + 1];

@@ -31,7 +31,6 @@
 //  * Output tiles hold four consecutive n per lane: 8-byte stores into
 //    states[b,h,c][p][n].
 #include "chunk_cumsum.h"
-#include "conv_math.h"
 #include "mfma_common.h"
 
 namespace ssd {
@@ -103,66 +102,7 @@ __device__ __forceinline__ int bsw(int j) {
 // the decayed state entering the window's chunk, read from hin ([H, hnc,
 // P, N] bf16, the fixed chunks' entering states after state passing). An
 // instantiation of its own, so the other modes keep their register budget.
-// MODE kConvCumsum: as kFuseCumsum, with the short causal convolution
-// (batched layout, ConvArgs) applied as x and B are loaded: x and B come
-// from the packed activations, are convolved (the K-1 rows before the chunk
-// from the previous chunk, the carried state or zeros), written out for the
-// later steps (x by the workgroups of the first block of state columns, B by
-// those of the first head group of their B/C group, which also convolve and
-// write their slice of C) and used for the products. The arithmetic is that
-// of the stand-alone convolution kernel, so both give the same bits.
-constexpr int kReadCumsum = 0, kFuseCumsum = 1, kWindowFinals = 2, kConvCumsum = 3;
-
-// Weights of eight consecutive channels, left-padded to four taps (zeros
-// before the first of the K), and their biases.
-struct ConvW {
-  float w[4][8];
-  float bias[8];
-};
-__device__ __forceinline__ void conv_weights(const ConvArgs& cv, int ch, ConvW& cw) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = k - (4 - cv.K);
-      cw.w[k][s] = i >= 0 ? cv.w[(ch + s) * cv.K + i] : 0.f;
-    }
-    cw.bias[s] = cv.bias != nullptr ? cv.bias[ch + s] : 0.f;
-  }
-}
-// Eight channels of one convolved row from its input rows t-3 .. t (bf16),
-// rounded to bf16: z = bias + sum_k w[k] in[t-3+k] (the padded taps add
-// exact zeros), then the optional SiLU.
-__device__ __forceinline__ uint4 conv_row8(const ConvW& cw, int silu, const uint4& a, const uint4& b2, const uint4& c2,
-                                           const uint4& d) {
-  float z[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    z[s] = cw.bias[s];
-    z[s] = fmaf(cw.w[0][s], bf16_at(a, s), z[s]);
-    z[s] = fmaf(cw.w[1][s], bf16_at(b2, s), z[s]);
-    z[s] = fmaf(cw.w[2][s], bf16_at(c2, s), z[s]);
-    z[s] = fmaf(cw.w[3][s], bf16_at(d, s), z[s]);
-    if (silu) z[s] = conv_silu(z[s]);
-  }
-  return make_uint4(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]), pack_bf16x2(z[4], z[5]),
-                    pack_bf16x2(z[6], z[7]));
-}
-// Input row j of a chunk (relative to its first row, row0 in the [batch * L]
-// rows; pos0 = the chunk's first position in its sequence) for eight channels
-// from ch: j < rows, and before the sequence the carried state (its values
-// rounded to bf16: exact for a state this library wrote) or zeros.
-__device__ __forceinline__ uint4 conv_src(const ConvArgs& cv, int64_t b, int64_t row0, int64_t pos0, int j, int ch) {
-  const int64_t pos = pos0 + j;
-  if (pos >= 0) return ld16(cv.xbc + (row0 + j) * cv.CH + ch);
-  if (cv.st_in != nullptr && pos >= -(cv.K - 1)) {
-    const float* s = cv.st_in + (b * cv.CH + ch) * (cv.K - 1) + (cv.K - 1 + pos);
-    const int k1 = cv.K - 1;
-    return make_uint4(pack_bf16x2(s[0], s[k1]), pack_bf16x2(s[2 * k1], s[3 * k1]), pack_bf16x2(s[4 * k1], s[5 * k1]),
-                      pack_bf16x2(s[6 * k1], s[7 * k1]));
-  }
-  return make_uint4(0, 0, 0, 0);
-}
+constexpr int kReadCumsum = 0, kFuseCumsum = 1, kWindowFinals = 2;
 template <int P, int NB, int Q, int MODE>
 __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
@@ -170,11 +110,10 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     float* __restrict__ dA_cs, float* __restrict__ dtc,
     uint16_t* __restrict__ states, int64_t L, int H, int G, int N, int64_t nc, int HB, DtOpts dto,
     const ChunkInfo* __restrict__ ctab, const uint8_t* __restrict__ seg, float* __restrict__ fin,
-    const uint16_t* __restrict__ hin, int64_t hnc, ConvArgs cv) {
+    const uint16_t* __restrict__ hin, int64_t hnc) {
   using C = StateCfg<P, NB, Q>;
   constexpr bool FUSED = MODE != kReadCumsum;
   constexpr bool WIN = MODE == kWindowFinals;
-  constexpr bool CONV = MODE == kConvCumsum;
   constexpr int KS = C::KS;
   constexpr int TAB_U4 = FUSED ? C::TAB_FLOATS / 4 : 0;
   __shared__ __align__(16) uint4 lds[C::LDS_FRAGS + TAB_U4];
@@ -219,15 +158,11 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   // ---- x of one head: raw rows into registers; scaled, transposed into LDS.
   // The loads of head hh+1 are issued when head hh starts, so one head of
   // loads is in flight per workgroup while its products run. ----
-  constexpr int XCV = CONV ? C::XPT : 1;  // convolution: input rows before each block, weights
   struct XSet {
     uint4 xr[C::XPT][8];
     float4 lr[C::XPT][2], dr[C::XPT][2];
     float lam;
-    uint4 xh[XCV][3];
-    ConvW cw[XCV];
   };
-  const int64_t pos0 = c * Q;  // (convolution, batched layout) the chunk's first position in its sequence
   auto fetch_x = [&](XSet& xs, int h) {
     if constexpr (!FUSED) {
       const float* lc = dA_cs + ((b * H + h) * nc + c) * Q;
@@ -246,22 +181,11 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     for (int k = 0; k < C::XPT; ++k) {
       const int bi = tid + k * kThreads;
       const int cb = bi % (P / 8), jb = (bi / (P / 8)) % (Q / 8);
-      if constexpr (CONV) {
-        // the raw rows and the three before them, and the channels' weights
-        const int ch = h * P + 8 * cb;
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr)
-          xs.xr[k][rr] = ld16(cv.xbc + (row0 + min(8 * jb + rr, rows - 1)) * cv.CH + ch);
-#pragma unroll
-        for (int q = 0; q < 3; ++q) xs.xh[k][q] = conv_src(cv, b, row0, pos0, min(8 * jb - 3 + q, rows - 1), ch);
-        conv_weights(cv, ch, xs.cw[k]);
-      } else {
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          // clamped row, always in bounds; rows past the end are zeroed later
-          const int j = 8 * jb + rr;
-          xs.xr[k][rr] = ld16(x + ((row0 + min(j, rows - 1)) * H + h) * P + 8 * cb);
-        }
+      for (int rr = 0; rr < 8; ++rr) {
+        // clamped row, always in bounds; rows past the end are zeroed later
+        const int j = 8 * jb + rr;
+        xs.xr[k][rr] = ld16(x + ((row0 + min(j, rows - 1)) * H + h) * P + 8 * cb);
       }
     }
   };
@@ -276,25 +200,6 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         xs.lr[k][1] = *reinterpret_cast<const float4*>(lt + 8 * jb + 4);
         xs.dr[k][0] = *reinterpret_cast<const float4*>(lt + Q + 8 * jb);
         xs.dr[k][1] = *reinterpret_cast<const float4*>(lt + Q + 8 * jb + 4);
-      }
-    }
-    if constexpr (CONV) {
-      // convolve the block's rows (from the last down, so each input row is
-      // overwritten only after its last use) and write the convolved x
-      const int h = h0 + hh;
-#pragma unroll
-      for (int k = 0; k < C::XPT; ++k) {
-        const int bi = tid + k * kThreads;
-        const int cb = bi % (P / 8), jb = (bi / (P / 8)) % (Q / 8);
-#pragma unroll
-        for (int rr = 7; rr >= 0; --rr) {
-          const uint4 a = rr >= 3 ? xs.xr[k][rr - 3] : xs.xh[k][rr];
-          const uint4 b2 = rr >= 2 ? xs.xr[k][rr - 2] : xs.xh[k][rr + 1];
-          const uint4 c2 = rr >= 1 ? xs.xr[k][rr - 1] : xs.xh[k][2];
-          xs.xr[k][rr] = conv_row8(xs.cw[k], cv.silu, a, b2, c2, xs.xr[k][rr]);
-          if (nb == 0 && bi < C::XBLK && 8 * jb + rr < rows)
-            *reinterpret_cast<uint4*>(cv.xo + ((row0 + 8 * jb + rr) * H + h) * P + 8 * cb) = xs.xr[k][rr];
-        }
       }
     }
 #pragma unroll
@@ -329,9 +234,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
   // wait covers one group only and the three latencies overlap. ----
   const int hlast = h0 + HB - 1;
   // B tile of the chunk straight into the LDS (rows past the end fall
-  // outside the buffer range and arrive as zeros); with the convolution,
-  // through registers (below)
-  if constexpr (!CONV) {
+  // outside the buffer range and arrive as zeros)
+  {
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint4*)lds);
     const v4i32_t brs =
         buffer_words(Bm + (row0 * G + g) * N + nb * NB, (uint32_t)(((rows - 1) * (int64_t)G * N + NB) * 2));
@@ -342,60 +246,6 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         const int pos = blk * 1024 + 16 * lane;
         const int j = pos / C::BRB, cp = (pos % C::BRB) / 16;
         dma16(brs, lds_base + blk * 1024, (uint32_t)(j * G * N * 2 + 16 * (cp ^ bsw<NB>(j))));
-      }
-    }
-  }
-  // the convolution's B (and C) slices: thread (column block bcb, row run
-  // brg) convolves RPT consecutive rows, RB at a time; B goes into the LDS in
-  // the layout of the direct loads above (zero rows past the end)
-  const bool conv_lead = CONV && h0 % (H / G) == 0;  // first head group of its B/C group
-  if constexpr (CONV) {
-    constexpr int BCB = NB / 8, TPC = kThreads / BCB;
-    constexpr int RPT = Q / TPC > 0 ? Q / TPC : 1, RB = RPT < 8 ? RPT : 8;
-    const int bcb = tid % BCB, brg = tid / BCB;
-    auto conv_slice = [&](int ch, uint16_t* out, bool to_lds) {
-      ConvW cw;
-      conv_weights(cv, ch, cw);
-#pragma unroll
-      for (int r0 = 0; r0 < RPT; r0 += RB) {
-        const int j0 = brg * RPT + r0;
-        if (j0 < Q) {
-          uint4 in[RB + 3];
-#pragma unroll
-          for (int q = 0; q < RB + 3; ++q) in[q] = conv_src(cv, b, row0, pos0, min(j0 - 3 + q, rows - 1), ch);
-#pragma unroll
-          for (int r = 0; r < RB; ++r) {
-            const int j = j0 + r;
-            const uint4 v = conv_row8(cw, cv.silu, in[r], in[r + 1], in[r + 2], in[r + 3]);
-            if (to_lds)
-              *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(lds) + j * C::BRB + 16 * (bcb ^ bsw<NB>(j))) =
-                  j < rows ? v : make_uint4(0, 0, 0, 0);
-            if (out != nullptr && j < rows) *reinterpret_cast<uint4*>(out + (row0 + j) * G * N) = v;
-          }
-        }
-      }
-    };
-    const int nch = nb * NB + 8 * bcb;  // n of the column block
-    conv_slice((int)(H * P) + g * (int)N + nch, conv_lead ? cv.bo + g * N + nch : nullptr, true);
-    if (conv_lead) conv_slice((int)(H * P + G * N) + g * (int)N + nch, cv.co + g * N + nch, false);
-    // the carried state after the sequence's last chunk: its last K-1 raw
-    // inputs of the channels this workgroup writes (x: first block of state
-    // columns; B and C: the lead head group), fp32 as the stand-alone kernel
-    if (cv.st_out != nullptr && c == nc - 1 && cv.K > 1) {
-      const int nx = nb == 0 ? HB * P : 0, nbc = conv_lead ? 2 * NB : 0;
-      const int k1 = cv.K - 1;
-      for (int i = tid; i < (nx + nbc) * k1; i += kThreads) {
-        const int k = i % k1, e = i / k1;
-        const int ch = e < nx ? h0 * P + e
-                              : (e - nx < NB ? (int)(H * P) + g * (int)N + nb * NB + (e - nx)
-                                             : (int)(H * P + G * N) + g * (int)N + nb * NB + (e - nx - NB));
-        const int64_t t = L - k1 + k;  // position in the sequence
-        float v;
-        if (t >= 0)
-          v = __uint_as_float((uint32_t)cv.xbc[(b * L + t) * cv.CH + ch] << 16);
-        else
-          v = cv.st_in != nullptr ? cv.st_in[(b * cv.CH + ch) * k1 + k1 + t] : 0.f;
-        cv.st_out[(b * cv.CH + ch) * k1 + k] = v;
       }
     }
   }
@@ -618,8 +468,7 @@ hipError_t launch_pnq(const Plan& p, const void* x, const void* B, const float* 
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), dt, A, cs, dtc,
       static_cast<uint16_t*>(st), p.L, (int)p.H, (int)p.G, (int)p.N, p.nc, hb, p.dto, p.ctab,
       MODE == kFuseCumsum ? p.seg_start : nullptr, MODE == kWindowFinals ? p.window_finals : nullptr,
-      MODE == kWindowFinals ? static_cast<const uint16_t*>(p.window_hin) : nullptr, p.window_nc,
-      MODE == kConvCumsum ? *p.conv : ConvArgs{});
+      MODE == kWindowFinals ? static_cast<const uint16_t*>(p.window_hin) : nullptr, p.window_nc);
   return hipGetLastError();
 }
 
@@ -676,7 +525,6 @@ hipError_t launch_cumsum_chunk_state_mfma(const Plan& p, const void* x, const vo
                                           const float* A, float* dA_cs, float* dtc, void* states,
                                           hipStream_t s) {
   if (p.window_finals != nullptr) return launch_any<kWindowFinals>(p, x, B, dt, A, nullptr, nullptr, nullptr, s);
-  if (p.conv != nullptr) return launch_any<kConvCumsum>(p, x, B, dt, A, dA_cs, dtc, states, s);
   return launch_any<kFuseCumsum>(p, x, B, dt, A, dA_cs, dtc, states, s);
 }
 

@@ -32,23 +32,6 @@ constexpr int32_t kWindowCrossing = 4;
 // The chunk count of a sequence is also kept per sequence (first slot, count)
 // so that state passing can run one chain per sequence.
 
-// The short causal convolution applied by the chunk-state kernel as it loads
-// x and B (and C, which it only writes out): xbc [batch, L, CH] bf16 with
-// CH = H*P + 2*G*N (x, then B, then C channels), weights [CH, K] fp32 (K in
-// 1..4), bias [CH] or null, the carried state [batch, CH, K-1] fp32 in and
-// out (either null), and the convolved x, B, C written in their layouts.
-struct ConvArgs {
-  const uint16_t* xbc = nullptr;
-  const float* w = nullptr;
-  const float* bias = nullptr;
-  const float* st_in = nullptr;
-  float* st_out = nullptr;
-  uint16_t* xo = nullptr;
-  uint16_t* bo = nullptr;
-  uint16_t* co = nullptr;
-  int K = 0, silu = 0, CH = 0;
-};
-
 // A validated problem plus the chosen chunk length.
 struct Plan {
   DtOpts dto;
@@ -66,10 +49,6 @@ struct Plan {
   float* window_finals = nullptr;
   const void* window_hin = nullptr;
   int64_t window_nc = 0;
-  // batched bf16 only: the chunk-state kernel convolves its inputs from the
-  // packed activations (x and B then read from conv->xo and conv->bo by the
-  // later steps), else nullptr
-  const ConvArgs* conv = nullptr;
   int64_t batch, L, H, P, N, G;
   int io;       // IoType of x, B, C, y and of the chunk states
   int Q;        // chunk length

@@ -415,17 +415,13 @@ def test_headdim_128_chunk_sizes_that_fit_are_accepted(kw):
     assert ssd.effective_chunk_size(d) == (kw.get("chunk_size") or 128)
 
 
-# ---- the short convolution, alone and inside the forward ------------------
-
-def _conv_ptrs():
-    # xbc weight bias st_in st_out | x B C (conv1d_split outputs)
-    return [ctypes.c_void_p(BASE + k * (1 << 32)) for k in range(8)]
-
+# ---- the short convolution --------------------------------------------------
 
 def test_conv1d_split_validates():
     L = lib()
     d = desc(batch=2, seqlen=300, nheads=4, headdim=32, dstate=16, ngroups=2)
-    p = _conv_ptrs()
+    # xbc weight bias st_in st_out | x B C
+    p = [ctypes.c_void_p(BASE + k * (1 << 32)) for k in range(8)]
     call = lambda q, K=4, dd=d: L.ssd_conv1d_split(ctypes.byref(dd), K, q[0], q[1], q[2], 1, q[3], q[4], q[5], q[6],
                                                    q[7], None)
     assert call(p, K=0) == UNSUP and call(p, K=5) == UNSUP
@@ -439,31 +435,3 @@ def test_conv1d_split_validates():
     q = list(p)
     q[4] = p[3]  # carried state out over in
     assert call(q) == ALIAS
-
-
-def _fwd_conv_args(d, q, K=4):
-    # q: xbc weight bias st_in st_out dt A D h0 x B C y hT ws
-    return (ctypes.byref(d), K, q[0], q[1], q[2], 1, q[3], q[4], q[5], q[6], q[7], q[8], q[9], q[10], q[11], q[12],
-            q[13], q[14], ctypes.c_size_t(1 << 31), None)
-
-
-def test_forward_conv_validates():
-    L = lib()
-    d = desc(batch=2, seqlen=300, nheads=4, headdim=32, dstate=16, ngroups=2)
-    p = [ctypes.c_void_p(BASE + k * (1 << 32)) for k in range(15)]
-    f = lambda q, K=4, dd=d: L.ssd_forward_conv(*_fwd_conv_args(dd, q, K))
-    assert f(p, dd=desc(batch=2, seqlen=300, nheads=4, headdim=32, dstate=16, ngroups=2, io_dtype="fp32")) == UNSUP
-    assert f(p, K=0) == UNSUP and f(p, K=5) == UNSUP
-    for i in (0, 1, 5, 6, 9, 10, 11, 12):  # xbc, weight, dt, A, x, B, C, y
-        q = list(p)
-        q[i] = None
-        assert f(q) == NULLP, i
-    q = list(p)
-    q[0] = ctypes.c_void_p(BASE + 8)
-    assert f(q) == ALIGN
-    for i, j in ((9, 0), (10, 6), (11, 12), (4, 3), (13, 1), (12, 9), (14, 10)):
-        q = list(p)
-        q[i] = p[j]  # output i over input or output j
-        assert f(q) == ALIAS, (i, j)
-    d_bad = desc(batch=2, seqlen=300, nheads=4, headdim=48, dstate=16, ngroups=2)
-    assert f(p, dd=d_bad) == UNSUP
