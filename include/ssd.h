@@ -52,9 +52,11 @@
  *
  * Supported: io dtype fp32 or bf16; P in {16, 32, 64, 128};
  * N in {16, 32, 64, 128, 256}; H % G == 0; chunk_size in {0 (default), 64,
- * 128, 256}, except, for bf16 with P = 128, chunk_size 256 with N >= 64 and
- * chunk_size 64 with N = 256 (SSD_ERR_UNSUPPORTED: the intra-chunk kernel's
- * register tiles do not fit there; the default, 128, always does). Base pointers of x, B, C, y, init_state, final_state must be
+ * 128, 256}, except, for bf16, chunk_size 256 with P = 128 and N >= 64,
+ * chunk_size 64 with P = 128 and N = 256, and chunk_size 256 with P = 16 and
+ * N = 256 (SSD_ERR_UNSUPPORTED: the intra-chunk kernel's register tiles do
+ * not fit there; the default, 128 for those headdim/dstate pairs, always
+ * does). Base pointers of x, B, C, y, init_state, final_state must be
  * 16-byte aligned, dt/A/D 4-byte aligned, the workspace 256-byte aligned.
  */
 #ifndef SSD_H_

@@ -64,8 +64,9 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 int default_chunk(const ssd_desc_t& d) {
   // 256 halves the chunk-state traffic of 128 (and is faster at every state
-  // size up to 256); with headdim 128 the intra-chunk kernel's register
-  // tiles only fit at 128.
+  // size up to 256); with headdim 128, and with headdim 16 at dstate 256,
+  // the intra-chunk kernel's register tiles only fit at 128.
+  if (d.headdim == 16 && d.dstate == 256) return 128;
   return d.headdim <= 64 ? 256 : 128;
 }
 
@@ -85,11 +86,13 @@ ssd_status_t make_plan(const ssd_desc_t* d, Plan* p) {
   int Q = d->chunk_size;
   if (Q == 0) Q = default_chunk(*d);
   if (Q != 64 && Q != 128 && Q != 256) return SSD_ERR_UNSUPPORTED;
-  // headdim 128 on the matrix cores: the intra-chunk kernel's register tiles
-  // do not fit at chunk length 256 (dstate >= 64) or 64 (dstate 256); those
-  // instantiations would spill to scratch, so the pairs are refused
-  if (d->io_dtype == SSD_DTYPE_BF16 && d->headdim == 128 &&
-      ((Q == 256 && d->dstate >= 64) || (Q == 64 && d->dstate == 256)))
+  // the matrix-core intra-chunk kernel's register tiles do not fit with
+  // headdim 128 at chunk length 256 (dstate >= 64) or 64 (dstate 256), nor
+  // with headdim 16 at dstate 256 and chunk length 256; those instantiations
+  // would spill to scratch, so the combinations are refused
+  if (d->io_dtype == SSD_DTYPE_BF16 &&
+      ((d->headdim == 128 && ((Q == 256 && d->dstate >= 64) || (Q == 64 && d->dstate == 256))) ||
+       (d->headdim == 16 && d->dstate == 256 && Q == 256)))
     return SSD_ERR_UNSUPPORTED;
   const int64_t nc = (d->seqlen + Q - 1) / Q;
   // element counts of the largest arrays must stay well inside 64-bit byte math

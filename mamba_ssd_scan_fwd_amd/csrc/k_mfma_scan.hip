@@ -146,18 +146,31 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   // chunk that belongs at byte 16 l of the block. Rows of x past the end of
   // the chunk fall outside the buffer range and arrive as zeros. The decay
   // inputs are read into registers and tabulated in the LDS afterwards.
-  uint32_t xgo[C::XBPW], hgo[C::HBPW];
-#pragma unroll
-  for (int k = 0; k < C::XBPW; ++k) {
-    const int pos = (wave * C::XBPW + k) * 1024 + 16 * lane;
+  // Source offsets of the blocks: lane l's chunk of x block k and of Hin
+  // block k. With N = 256 they are recomputed at each use from an opaque copy
+  // of the lane id instead of held across the head loop: held, they were
+  // spilled, and every reload waited for all the loads in flight.
+  constexpr bool REMAT = N >= 256 && P <= 64;
+  auto xgo_at = [&](int k) {
+    int l = lane;
+    if constexpr (REMAT) asm volatile("" : "+v"(l));
+    const int pos = (wave * C::XBPW + k) * 1024 + 16 * l;
     const int j = pos / C::XRB, cp = (pos % C::XRB) / 16;
-    xgo[k] = (uint32_t)(j * H * P * 2 + 16 * (cp ^ scan_xsw<P>(j)));
-  }
-#pragma unroll
-  for (int k = 0; k < C::HBPW; ++k) {
-    const int pos = (wave * C::HBPW + k) * 1024 + 16 * lane;  // past P*N*2: padding, reads zeros
+    return (uint32_t)(j * H * P * 2 + 16 * (cp ^ scan_xsw<P>(j)));
+  };
+  auto hgo_at = [&](int k) {
+    int l = lane;
+    if constexpr (REMAT) asm volatile("" : "+v"(l));
+    const int pos = (wave * C::HBPW + k) * 1024 + 16 * l;  // past P*N*2: padding, reads zeros
     const int p = pos / C::HRB, cp = (pos % C::HRB) / 16;
-    hgo[k] = (uint32_t)(p * C::HRB + 16 * (cp ^ scan_hsw<N>(p)));
+    return (uint32_t)(p * C::HRB + 16 * (cp ^ scan_hsw<N>(p)));
+  };
+  uint32_t xgo[REMAT ? 1 : C::XBPW], hgo[REMAT ? 1 : C::HBPW];
+  if constexpr (!REMAT) {
+#pragma unroll
+    for (int k = 0; k < C::XBPW; ++k) xgo[k] = xgo_at(k);
+#pragma unroll
+    for (int k = 0; k < C::HBPW; ++k) hgo[k] = hgo_at(k);
   }
   float lpre = 0.f, dpre = 0.f, tl1 = 0.f, tl2 = 0.f;
   // thread e < R*R tabulates exp(l_{16 r} - l_{16 t + 15}), r = e / R, t = e % R.
@@ -167,7 +180,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   auto fetch_x_block = [&](int h, int bufoff, int k) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + bufoff);
     const v4i32_t xrs = buffer_words(x + (row0 * H + h) * P, (uint32_t)(((rows - 1) * (int64_t)H + 1) * P * 2));
-    dma16(xrs, dst + C::OFF_X + (wave * C::XBPW + k) * 1024, xgo[k]);
+    dma16(xrs, dst + C::OFF_X + (wave * C::XBPW + k) * 1024, REMAT ? xgo_at(k) : xgo[k]);
   };
   // Hin blocks of this wavefront and the decay inputs
   auto fetch_rest = [&](int h, int bufoff) {
@@ -175,7 +188,7 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
     const v4i32_t hrs = buffer_words(states + ((b * H + h) * nc + c) * (int64_t)P * N, (uint32_t)(P * N * 2));
 #pragma unroll
     for (int k = 0; k < C::HBPW; ++k)
-      if (wave * C::HBPW + k < C::HBLK) dma16(hrs, dst + C::OFF_H + (wave * C::HBPW + k) * 1024, hgo[k]);
+      if (wave * C::HBPW + k < C::HBLK) dma16(hrs, dst + C::OFF_H + (wave * C::HBPW + k) * 1024, REMAT ? hgo_at(k) : hgo[k]);
     const float* lc = dA_cs + ((b * H + h) * nc + c) * Q;
     const float* dc = dtc + ((b * H + h) * nc + c) * Q;
     const int tq = min(tid, Q - 1), te = min(tid, R * R - 1);
@@ -554,9 +567,19 @@ int pick_heads_per_wg(const Plan& p, int resident) {
   return best;
 }
 
+// The shapes whose register tiles do not fit two wavefronts per SIMD without
+// spilling; the plan refuses them (bf16), so they are not instantiated.
+template <int P, int N, int Q>
+constexpr bool scan_tiles_fit() {
+  return !(P == 128 && ((Q == 256 && N >= 64) || (Q == 64 && N == 256))) && !(P == 16 && N == 256 && Q == 256);
+}
+
 template <int P, int N, int Q>
 hipError_t launch_pnq(const Plan& p, const void* x, const void* B, const void* Cm, const float* D,
                       const float* cs, const float* dtc, const void* st, void* y, hipStream_t s) {
+  if constexpr (!scan_tiles_fit<P, N, Q>()) {
+    return hipErrorInvalidValue;
+  } else {
   using Cfg = ScanCfg<P, N, Q>;
   // workgroups resident per compute unit: two wavefronts per SIMD (the
   // register budget), and the LDS
@@ -569,6 +592,7 @@ hipError_t launch_pnq(const Plan& p, const void* x, const void* B, const void* C
       cs, dtc, static_cast<const uint16_t*>(st), static_cast<uint16_t*>(y), p.L, (int)p.H, (int)p.G, p.nc, hb,
       p.ctab);
   return hipGetLastError();
+  }
 }
 
 template <int P, int N>

@@ -110,6 +110,7 @@ def test_effective_chunk_and_workspace_layout(Q):
         (dict(headdim=128, chunk_size=256), UNSUP),              # bf16 register tiles do not fit
         (dict(headdim=128, dstate=64, chunk_size=256), UNSUP),
         (dict(headdim=128, dstate=256, chunk_size=64), UNSUP),
+        (dict(headdim=16, dstate=256, chunk_size=256), UNSUP),
     ],
 )
 def test_bad_descriptors_are_rejected(kw, code):
@@ -302,6 +303,9 @@ def test_default_chunk_rule():
     assert ssd.effective_chunk_size(desc(dstate=256)) == 256
     assert ssd.effective_chunk_size(desc(headdim=32, dstate=16)) == 256
     assert ssd.effective_chunk_size(desc(headdim=128)) == 128
+    assert ssd.effective_chunk_size(desc(headdim=16, dstate=256)) == 128
+    assert ssd.effective_chunk_size(desc(headdim=16, dstate=256, io_dtype="fp32")) == 128
+    assert ssd.effective_chunk_size(desc(headdim=16, dstate=256, io_dtype="fp32", chunk_size=256)) == 256
 
 
 # ---- the one-pass entry point --------------------------------------------

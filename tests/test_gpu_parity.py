@@ -156,6 +156,7 @@ EDGE = [
     (300, 64, 32, 4, 1, "bf16", 0, True),
     (300, 64, 256, 4, 2, "bf16", 0, True),
     (300, 128, 256, 2, 1, "bf16", 128, True),
+    (300, 16, 256, 4, 1, "bf16", 0, True),   # headdim 16, dstate 256: default chunk 128
     # Hin smaller than one 1 KB load block; B tile with fewer load blocks
     # than wavefronts; one LDS buffer per head (P = 128 at Q = 256)
     (300, 16, 16, 4, 1, "bf16", 0, True),
