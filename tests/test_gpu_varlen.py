@@ -110,3 +110,43 @@ def test_one_sequence_equals_the_batched_split_path(L, Q, H):
     assert torch.equal(y1, y2)
     scale = h1.abs().max().item()
     assert (h2 - h1).abs().max().item() <= 2.0 ** -7 * scale
+
+
+@pytest.mark.parametrize("Q", [64, 256])
+def test_changing_one_sequence_leaves_the_others_bit_for_bit(Q):
+    """Sequence isolation in fixed chunks: every decay across a sequence start
+    is exactly 0, so the other sequences' y and final states must not change
+    by a single bit when one sequence's x, B and C change (including
+    sequences that share a chunk with it). (Its dt is left alone: dt enters
+    the chunk's dA cumsum, and a later sequence in the same chunk sees the
+    offset of its start rounded with it, so its decays may move by a
+    rounding.)"""
+    lib = ssd()
+    cfg = BASE.with_(nheads=4, ngroups=2)
+    lengths = [70, 3, 130, 1, 0, 200, 45]
+    T = sum(lengths)
+    inp = make_inputs(cfg.with_(batch=1, seqlen=T, init_state=False), seed=95)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    cu_d = torch.tensor(cu, device=DEV)
+    note(f"[gpu] varlen sequence isolation Q={Q}")
+
+    def run(d):
+        y, hT = lib.forward_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], cu_seqlens=cu_d, chunk_size=Q)
+        torch.cuda.synchronize()
+        return y.cpu(), hT.cpu()
+
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    y0, h0 = run(d)
+    for s in (1, 2, 5):  # a 3-token sequence inside a chunk, one spanning chunks, the one after an empty one
+        a, e = int(cu[s]), int(cu[s + 1])
+        g = torch.Generator().manual_seed(96 + s)
+        d2 = {k: (v.clone() if v is not None else None) for k, v in d.items()}
+        for k in ("x", "B", "C"):
+            d2[k][:, a:e] = torch.randn(d2[k][:, a:e].shape, generator=g).to(d2[k].dtype).to(DEV)
+        y1, h1 = run(d2)
+        keep = torch.ones(T, dtype=torch.bool)
+        keep[a:e] = False
+        assert torch.equal(y1[:, keep], y0[:, keep]), f"changing sequence {s} changed another sequence's y"
+        others = [q for q in range(len(lengths)) if q != s]
+        assert torch.equal(h1[others], h0[others]), f"changing sequence {s} changed another final state"
+        assert not torch.equal(y1[:, a:e], y0[:, a:e])
