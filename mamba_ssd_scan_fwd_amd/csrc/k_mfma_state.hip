@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
 #pragma unroll
     for (int k = 0; k < C::XPT; ++k) {
       const int bi = tid + k * kThreads;
-      if (bi < C::XBLK) {
+      if (C::XPT * kThreads == C::XBLK || bi < C::XBLK) {  // (no branch when the blocks fill the threads)
         const int cb = bi % (P / 8), jb = bi / (P / 8);
         const float l8[8] = {xs.lr[k][0].x, xs.lr[k][0].y, xs.lr[k][0].z, xs.lr[k][0].w,
                              xs.lr[k][1].x, xs.lr[k][1].y, xs.lr[k][1].z, xs.lr[k][1].w};
@@ -332,6 +332,9 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
     const int h = h0 + hh;
     uint4* cur = lds + (hh & 1) * C::X_FRAGS;
     fetch_x(mine, min(h + 1, hlast));
+    // keep the loads here, issued before the products (the scheduler would
+    // otherwise move them down next to their use and wait for them there)
+    __builtin_amdgcn_sched_barrier(0);
 
     // end windows that continue a sequence: the entering state's four bf16
     // of each tile, loaded now so the loads overlap the products
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
           }
         }
       }
-      if (hh + 1 < HB) stage_x(mine, lds + ((hh + 1) & 1) * C::X_FRAGS, hh + 1);  // the other buffer
+      stage_x(mine, lds + ((hh + 1) & 1) * C::X_FRAGS, hh + 1 < HB ? hh + 1 : hh);  // the other buffer
       __syncthreads();
       return;
     }
@@ -436,7 +439,11 @@ __global__ __launch_bounds__(kThreads) void chunk_state_mfma_kernel(
         }
       }
     }
-    if (hh + 1 < HB) stage_x(mine, lds + ((hh + 1) & 1) * C::X_FRAGS, hh + 1);  // the other buffer
+    // into the other buffer; also after the last head (its data again, never
+    // read): staged unconditionally, the loads of `mine` have a use on every
+    // path, which keeps them where they are issued, one head ahead, instead
+    // of being sunk into a branch next to their use
+    stage_x(mine, lds + ((hh + 1) & 1) * C::X_FRAGS, hh + 1 < HB ? hh + 1 : hh);
     __syncthreads();
   };
   for (int hh = 0; hh < HB; hh += 2) {
