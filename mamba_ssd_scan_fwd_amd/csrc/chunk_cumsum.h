@@ -13,11 +13,16 @@ namespace ssd {
 // dt as the entry points use it: optional per-head bias, softplus
 // log(1 + e^z) (z itself above 20, where the two agree in fp32), then an
 // optional clamp. Applied to positions inside the sequence only.
-__device__ __forceinline__ float dt_pre(float v, int h, const DtOpts& o) {
-  if (o.bias != nullptr) v += o.bias[h];
+// dt_pre_with takes the head's bias already loaded (used only when o.bias
+// is set), so that a caller can issue that load early, beside its others.
+__device__ __forceinline__ float dt_pre_with(float v, float bias, const DtOpts& o) {
+  if (o.bias != nullptr) v += bias;
   if (o.softplus) v = v > 20.f ? v : log1pf(expf(v));
   if (o.clamp) v = fminf(fmaxf(v, o.lo), o.hi);
   return v;
+}
+__device__ __forceinline__ float dt_pre(float v, int h, const DtOpts& o) {
+  return dt_pre_with(v, o.bias != nullptr ? o.bias[h] : 0.f, o);
 }
 
 // Lane `lane` owns the QPL = Q/64 consecutive positions lane*QPL .. +QPL-1 of

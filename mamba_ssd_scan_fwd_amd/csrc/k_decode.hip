@@ -43,42 +43,54 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
   const int sub = tid % TPR;                        // which four n
   const int64_t row0 = (int64_t)blockIdx.x * RPW * kRPT + tid / TPR;
 
-  float4 hs[kRPT];
-  int64_t rr[kRPT];
+  // Every load of the thread's rows is issued first, from valid addresses
+  // only (the optional D and dt bias read A's address when absent and are
+  // selected away), so that the thread waits once for all of them instead of
+  // once per dependent group.
+  float4 hs[kRPT], bv[kRPT], cv[kRPT];
+  float dtv[kRPT], av[kRPT], xv[kRPT], dv[kRPT], biv[kRPT];
+  int64_t rr[kRPT], rc[kRPT];
+  const float* dsrc = D != nullptr ? D : A;
+  const float* bsrc = dto.bias != nullptr ? dto.bias : A;
+  const int G = H / hpg;
 #pragma unroll
   for (int k = 0; k < kRPT; ++k) {
     rr[k] = row0 + (int64_t)k * RPW;
     // rows past the end re-read the last row (not stored)
     const int64_t r = rr[k] < rows ? rr[k] : rows - 1;
-    hs[k] = *reinterpret_cast<const float4*>(state + r * N + 4 * sub);
-  }
-#pragma unroll
-  for (int k = 0; k < kRPT; ++k) {
-    const int64_t r = rr[k] < rows ? rr[k] : rows - 1;
+    rc[k] = r;
     // row r = (b * H + h) * P + p; P is a power of two and b * H < 2^31
     const int bh = (int)(r >> pshift);
     const int b = bh / H, h = bh - b * H;
     const int g = h / hpg;
-    const int G = H / hpg;
-    const float d = dt_pre(dt[bh], h, dto);
-    const float alpha = __expf(d * A[h]);
-    const float xp = to_f32(x[r]);
-    const float4 bv = IO4<TIO>::load(Bm + ((int64_t)b * G + g) * N + 4 * sub);
-    const float4 cv = IO4<TIO>::load(Cm + ((int64_t)b * G + g) * N + 4 * sub);
+    hs[k] = *reinterpret_cast<const float4*>(state + r * N + 4 * sub);
+    dtv[k] = dt[bh];
+    av[k] = A[h];
+    xv[k] = to_f32(x[r]);
+    bv[k] = IO4<TIO>::load(Bm + ((int64_t)b * G + g) * N + 4 * sub);
+    cv[k] = IO4<TIO>::load(Cm + ((int64_t)b * G + g) * N + 4 * sub);
+    dv[k] = dsrc[h];
+    biv[k] = bsrc[h];
+  }
+#pragma unroll
+  for (int k = 0; k < kRPT; ++k) {
+    const float d = dt_pre_with(dtv[k], biv[k], dto);
+    const float alpha = __expf(d * av[k]);
+    const float xp = xv[k];
     const float u = d * xp;
     float4 hn;
-    hn.x = fmaf(alpha, hs[k].x, u * bv.x);
-    hn.y = fmaf(alpha, hs[k].y, u * bv.y);
-    hn.z = fmaf(alpha, hs[k].z, u * bv.z);
-    hn.w = fmaf(alpha, hs[k].w, u * bv.w);
-    float part = hn.x * cv.x + hn.y * cv.y + hn.z * cv.z + hn.w * cv.w;
+    hn.x = fmaf(alpha, hs[k].x, u * bv[k].x);
+    hn.y = fmaf(alpha, hs[k].y, u * bv[k].y);
+    hn.z = fmaf(alpha, hs[k].z, u * bv[k].z);
+    hn.w = fmaf(alpha, hs[k].w, u * bv[k].w);
+    float part = hn.x * cv[k].x + hn.y * cv[k].y + hn.z * cv[k].z + hn.w * cv[k].w;
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, TPR);
     if (rr[k] < rows) {
-      *reinterpret_cast<float4*>(state + r * N + 4 * sub) = hn;
+      *reinterpret_cast<float4*>(state + rc[k] * N + 4 * sub) = hn;
       if (sub == 0) {
-        const float dh = D != nullptr ? D[h] : 0.f;
-        y[r] = from_f32<TIO>(fmaf(dh, xp, part));
+        const float dh = D != nullptr ? dv[k] : 0.f;
+        y[rc[k]] = from_f32<TIO>(fmaf(dh, xp, part));
       }
     }
   }
