@@ -59,26 +59,28 @@ __global__ __launch_bounds__(kThreads) void conv1d_split_kernel(
   const int64_t b = blockIdx.z;
   const TIO* in = xbc + b * L * CH + ch;
 
+  // Every load below is issued from a valid address and its value selected
+  // afterwards (no load behind a branch: a branch join would wait for it),
+  // so the weights, bias, history and first tokens are in flight together.
   float4 wk[K];
 #pragma unroll
   for (int k = 0; k < K; ++k)
     wk[k] = make_float4(w[(ch + 0) * K + k], w[(ch + 1) * K + k], w[(ch + 2) * K + k], w[(ch + 3) * K + k]);
-  const float4 bv = bias != nullptr ? *reinterpret_cast<const float4*>(bias + ch) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* bp = bias != nullptr ? bias : w;  // w: any valid address
+  const float4 braw = make_float4(bp[ch], bp[ch + 1], bp[ch + 2], bp[ch + 3]);
+  const float4 bv = bias != nullptr ? braw : make_float4(0.f, 0.f, 0.f, 0.f);
 
   // history: the K-1 inputs before t0 (from the carried state before t = 0)
   float4 hist[K > 1 ? K - 1 : 1];
 #pragma unroll
   for (int k = 0; k < K - 1; ++k) {
     const int64_t t = t0 - (K - 1) + k;
-    if (t >= 0) {
-      hist[k] = V4<TIO>::load(in + t * CH);
-    } else if (st_in != nullptr) {
-      const int j = (int)(t + (K - 1));  // position inside the carried state
-      const float* s = st_in + (b * CH + ch) * (K - 1) + j;
-      hist[k] = make_float4(s[0], s[K - 1], s[2 * (K - 1)], s[3 * (K - 1)]);
-    } else {
-      hist[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    const float4 v = V4<TIO>::load(in + (t >= 0 ? t : 0) * CH);
+    int j = (int)(t + (K - 1));  // position inside the carried state (clamped: always a valid address)
+    j = j < 0 ? 0 : (j > K - 2 ? K - 2 : j);
+    const float* s = st_in != nullptr ? st_in + (b * CH + ch) * (K - 1) + j : w;
+    const float4 sv = make_float4(s[0], s[K - 1], s[2 * (K - 1)], s[3 * (K - 1)]);
+    hist[k] = t >= 0 ? v : (st_in != nullptr ? sv : make_float4(0.f, 0.f, 0.f, 0.f));
   }
 
   // output channel block: x, B or C (four channels never straddle them)
@@ -96,13 +98,24 @@ __global__ __launch_bounds__(kThreads) void conv1d_split_kernel(
   }
 
   const int64_t tend = t0 + kTT < L ? t0 + kTT : L;
+  // kU tokens' loads in flight at once (rows past the end re-read the last),
+  // the next kU issued before the current ones are used
+  float4 nxt[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int64_t t = t0 + u < tend ? t0 + u : tend - 1;
+    nxt[u] = V4<TIO>::load(in + t * CH);
+  }
   for (int64_t tb = t0; tb < tend; tb += kU) {
-    // kU tokens' loads in flight at once (rows past the end re-read the last)
     float4 cur[kU];
 #pragma unroll
+    for (int u = 0; u < kU; ++u) cur[u] = nxt[u];
+    // (issued on every pass, past the end too: a load behind a branch would
+    // be waited for where the branch joins)
+#pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int64_t t = tb + u < tend ? tb + u : tend - 1;
-      cur[u] = V4<TIO>::load(in + t * CH);
+      const int64_t t = tb + kU + u < tend ? tb + kU + u : tend - 1;
+      nxt[u] = V4<TIO>::load(in + t * CH);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
