@@ -97,46 +97,70 @@ __global__ __launch_bounds__(kThreads) void state_passing_kernel(
     cnt = st.y;
   }
 
-  float h[kVec];
-  if (active && h0 != nullptr) {
-    Vec8<float> v;
-    v.load(h0 + bh * PN + e0);
-    v.to(h);
-  } else {
+  if (cnt <= 0) {  // an empty sequence: its final state is its initial state
+    if (active && hT != nullptr) {
+      float z[kVec];
+      if (h0 != nullptr) {
+        Vec8<float> v;
+        v.load(h0 + bh * PN + e0);
+        v.to(z);
+      } else {
 #pragma unroll
-    for (int k = 0; k < kVec; ++k) h[k] = 0.f;
+        for (int k = 0; k < kVec; ++k) z[k] = 0.f;
+      }
+      Vec8<float>::store(hT + bh * PN + e0, z);
+    }
+    return;
   }
 
-  TS* s = states + (row * nc + c_beg) * (int64_t)PN + e0;
+  // Loads are issued from valid addresses only and not behind branches (a
+  // branch join waits for the loads issued inside it, and a wait for the
+  // newest load waits for all): an inactive thread reads element 0, a ring
+  // slot past the chain's end re-reads its last chunk (never used).
+  const int ec = active ? e0 : 0;
   const float* lam = dA_cs + (row * nc + c_beg) * Q + (Q - 1);
+  // lane l's log-decay of chunk cb + l for the block of 64 chunks from cb;
+  // the first block's is read before the ring's loads, so that waiting for
+  // it drains nothing (later blocks' waits drain the ring once per 64)
+  float lv = lam[(int64_t)(lane < cnt ? lane : cnt - 1) * Q];
+
+  float h[kVec];
+  {
+    Vec8<float> v;
+    v.load((h0 != nullptr ? h0 + bh * PN : dA_cs) + (h0 != nullptr ? ec : 0));
+    float hv[kVec];
+    v.to(hv);
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) h[k] = h0 != nullptr && active ? hv[k] : 0.f;
+  }
+
+  TS* s = states + (row * nc + c_beg) * (int64_t)PN + ec;
 
   Vec8<TS> ring[PF];
 #pragma unroll
-  for (int k = 0; k < PF; ++k)
-    if (active && k < cnt) ring[k].load(s + (int64_t)k * PN);
+  for (int k = 0; k < PF; ++k) ring[k].load(s + (int64_t)(k < cnt ? k : cnt - 1) * PN);
 
-  float dec = 0.f;
-  for (int64_t c0 = 0; c0 < cnt; c0 += PF) {
+  for (int64_t cb = 0; cb < cnt; cb += 64) {
+    const float dec = cb + lane < cnt ? __expf(lv) : 0.f;
+    const int64_t ce = cb + 64 < cnt ? cb + 64 : cnt;
+    for (int64_t c0 = cb; c0 < ce; c0 += PF) {
+      // the PF steps run whole (c0 is a multiple of PF, which divides 64);
+      // past the chain's end a step stores nothing and keeps h
 #pragma unroll
-    for (int k = 0; k < PF; ++k) {
-      const int64_t c = c0 + k;
-      if (c < cnt) {
-        if ((c & 63) == 0) {  // refresh: lane l holds exp(Lam_{c+l})
-          const int64_t cl = c + lane;
-          dec = cl < cnt ? __expf(lam[cl * Q]) : 0.f;
-        }
-        const float d = __int_as_float(
-            __builtin_amdgcn_readlane(__float_as_int(dec), (int)(c & 63)));
-        if (active) {
-          float sv[kVec];
-          ring[k].to(sv);
-          if (c + PF < cnt) ring[k].load(s + (c + PF) * PN);
-          Vec8<TS>::store(s + c * PN, h);
+      for (int k = 0; k < PF; ++k) {
+        const int64_t c = c0 + k;
+        const bool live = c < cnt;
+        const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dec), (int)(c & 63)));
+        float sv[kVec];
+        ring[k].to(sv);
+        ring[k].load(s + (c + PF < cnt ? c + PF : cnt - 1) * PN);
+        if (live && active) Vec8<TS>::store(s + c * PN, h);
 #pragma unroll
-          for (int e = 0; e < kVec; ++e) h[e] = fmaf(d, h[e], sv[e]);
-        }
+        for (int e = 0; e < kVec; ++e) h[e] = live ? fmaf(d, h[e], sv[e]) : h[e];
       }
     }
+    const int64_t cn = cb + 64 + lane;  // the next block's
+    lv = lam[(cn < cnt ? cn : cnt - 1) * Q];
   }
   if (active && hT != nullptr) Vec8<float>::store(hT + bh * PN + e0, h);
 }
