@@ -150,3 +150,53 @@ def test_changing_one_sequence_leaves_the_others_bit_for_bit(Q):
         others = [q for q in range(len(lengths)) if q != s]
         assert torch.equal(h1[others], h0[others]), f"changing sequence {s} changed another final state"
         assert not torch.equal(y1[:, a:e], y0[:, a:e])
+
+
+@pytest.mark.parametrize("init,T", [(False, 700), (False, 17000), (True, 700)])
+def test_varlen_replays_from_a_captured_graph(init, T):
+    """ssd_forward_varlen enqueues kernels only (the tables and the cleared
+    words come from kernels, not memsets), so a call can be captured into a
+    HIP graph with a preallocated workspace and replayed; every replay, with
+    eager work in between, gives the eager bits. Both cuts (fixed chunks
+    without initial states, with the segmented state passing at 17000
+    tokens; chunks per sequence with them)."""
+    lib = ssd()
+    cfg = BASE.with_(nheads=4, ngroups=2)
+    lengths = [T // 3, 5, T - T // 3 - 5 - 40, 0, 40]
+    inp = make_inputs(cfg.with_(batch=1, seqlen=T, init_state=False), seed=97)
+    d = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), device=DEV)
+    S = len(lengths)
+    h0 = (0.1 * torch.randn((S, cfg.nheads, cfg.headdim, cfg.dstate), generator=torch.Generator().manual_seed(98))
+          ).to(DEV) if init else None
+    desc = lib.make_desc(1, T, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, "bf16", 0)
+    ws = torch.empty(lib.workspace_bytes_varlen(desc, S), dtype=torch.uint8, device=DEV)
+    y = torch.empty_like(d["x"])
+    hT = torch.empty((S, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device=DEV)
+
+    def call():
+        lib.forward_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], cu_seqlens=cu, init_states=h0, y=y,
+                           final_states=hT, workspace=ws)
+
+    note(f"[gpu] varlen graph capture and replay init={init} T={T}")
+    call()
+    torch.cuda.synchronize()
+    y_ref, h_ref = y.clone(), hT.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for r in range(3):
+        y.fill_(float("nan"))
+        hT.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref) and torch.equal(hT, h_ref), f"replay {r} differs from the eager result"
+        path, status = lib.workspace_status_varlen(desc, S, ws)
+        assert status == 0
