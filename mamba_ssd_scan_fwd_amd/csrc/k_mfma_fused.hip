@@ -62,7 +62,11 @@ struct FusedCfg {
   static constexpr int NTP = P / 16;          // p tiles
   static constexpr int NTN = N / 16;          // n tiles
   static constexpr int NK = N / 32;           // 32-deep steps over n
-  static constexpr int NGT = R - 1;           // off-diagonal G^T tiles per wavefront
+  // row groups as in the chunk-output kernel: with eight wavefronts the four
+  // served first at their SIMDs take one tile more (2w + 1, R - 1 - 2w),
+  // the other four one less (2v, R - 2 - 2v), where the registers allow
+  static constexpr bool BAL = WAVES == 8 && N <= 128 && P <= 64;
+  static constexpr int NGT = BAL ? R : R - 1;  // off-diagonal G^T slots per wavefront
   static constexpr int XRB = 2 * P, HRB = 2 * N, HCPR = N / 8;
   static constexpr int XBLK = Q * P * 2 / 1024, XBPW = XBLK / WAVES;
   static constexpr int BBLK = Q * N * 2 / 1024, BBPW = BBLK / WAVES;
@@ -127,12 +131,18 @@ __global__ __launch_bounds__(2 * Q) __attribute__((amdgpu_waves_per_eu(2))) void
   const bool last = c + 1 == nc;
 
   int rk[RG], ik[RG];
-  rk[0] = wave;
-  rk[1] = R - 1 - wave;
+  if constexpr (C::BAL) {
+    const int v = wave & 3;
+    rk[0] = wave < 4 ? 2 * v + 1 : 2 * v;
+    rk[1] = wave < 4 ? R - 1 - 2 * v : R - 2 - 2 * v;
+  } else {
+    rk[0] = wave;
+    rk[1] = R - 1 - wave;
+  }
 #pragma unroll
   for (int k = 0; k < RG; ++k) ik[k] = 16 * rk[k] + r16;
   auto gslot = [&](int k, int t) {
-    const int sidx = k == 0 ? t : R - 2 - t;
+    const int sidx = k == 0 ? t : C::NGT - 1 - t;
     return sidx < 0 ? 0 : (sidx > C::NGT - 1 ? C::NGT - 1 : sidx);
   };
 
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(2 * Q) __attribute__((amdgpu_waves_per_eu(2))) void
       t = e;
     } else {
       k = 1;
-      t = R - 2 - e;
+      t = C::NGT - 1 - e;
     }
     srow[e] = 16 * t + r16;
     sk[e] = k;
@@ -369,17 +379,17 @@ __global__ __launch_bounds__(2 * Q) __attribute__((amdgpu_waves_per_eu(2))) void
     }
 
     // ---- diagonal tiles (mask j > i before the exponential) and the skip
-    // term D_h x_i as a product with D_h times the identity (two bf16 parts) ----
+    // term D_h x_i in the same products: the x operand holds the tile's rows
+    // in both halves of the 32-deep step, the weight operand the masked
+    // weights in one half and the bf16 part of D_h times the identity in the
+    // other; the remainder of D_h is added to the diagonal weight before that
+    // is rounded ----
     const float dh = D != nullptr ? D[h] : 0.f;
     const uint32_t dhi_bits = pack_bf16x2(dh, 0.f) & 0xffffu;
-    const uint32_t dlo_bits = pack_bf16x2(dh - bf16_lo(dhi_bits), 0.f) & 0xffffu;
+    const float dlo = dh - bf16_lo(dhi_bits);
     const int dq = r16 - 4 * g4;
-    const bool don = dq >= 0 && dq < 4;
-    auto ident = [&](uint32_t bits, bool upper) {
-      const uint32_t wv = don ? bits << (16 * (dq & 1)) : 0u;
-      const uint32_t w0 = (dq >> 1) == 0 ? wv : 0u, w1 = (dq >> 1) == 1 ? wv : 0u;
-      return as_bf16x8(upper ? make_uint4(0, 0, w0, w1) : make_uint4(w0, w1, 0, 0));
-    };
+    const uint32_t dwv = dq >= 0 && dq < 4 ? dhi_bits << (16 * (dq & 1)) : 0u;
+    const uint32_t did0 = (dq >> 1) == 0 ? dwv : 0u, did1 = (dq >> 1) == 1 ? dwv : 0u;
 #pragma unroll
     for (int k = 0; k < RG; ++k) {
       const int t = rk[k], i = ik[k];
@@ -396,21 +406,18 @@ __global__ __launch_bounds__(2 * Q) __attribute__((amdgpu_waves_per_eu(2))) void
       for (int q = 0; q < 4; ++q) {
         const int jq = j0 + q;
         const float e = __expf(jq <= i ? li - ljv[q] : -INFINITY);
-        w[q] = gv[q] * e * djv[q];
+        w[q] = gv[q] * e * djv[q] + (jq == i ? dlo : 0.f);
       }
-      const uint32_t w01 = pack_bf16x2(w[0], w[1]), w23 = pack_bf16x2(w[2], w[3]);
-      const bool upper = t & 1;
-      const bf16x8_t wop = as_bf16x8(upper ? make_uint4(0, 0, w01, w23) : make_uint4(w01, w23, 0, 0));
-      const bf16x8_t dop_hi = ident(dhi_bits, upper), dop_lo = ident(dlo_bits, upper);
+      const bf16x8_t wop = as_bf16x8(make_uint4(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), did0, did1));
+      const unsigned char* xa = buf + (t >> 1) * 32 * C::XRB + (t & 1) * 16 * C::XRB;
       bf16x8_t a[NTP];
 #pragma unroll
-      for (int pt = 0; pt < NTP; ++pt) a[pt] = as_bf16x8(xfrag(t >> 1, pt));
+      for (int pt = 0; pt < NTP; ++pt) {
+        const uint2 v = lds_tr8(xa + xoff[pt]);
+        a[pt] = as_bf16x8(make_uint4(v.x, v.y, v.x, v.y));
+      }
 #pragma unroll
       for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(a[pt], wop, acc[k][pt]);
-#pragma unroll
-      for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(a[pt], dop_hi, acc[k][pt]);
-#pragma unroll
-      for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(a[pt], dop_lo, acc[k][pt]);
     }
 
     // ---- the state chain: Hin = H_{c-1} (the initial state for c = 0), then,

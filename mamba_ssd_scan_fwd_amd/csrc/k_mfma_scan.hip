@@ -22,9 +22,11 @@
 //    bf16 in registers; only the decay mask is per head. The C fragments,
 //    which also feed the chunk-output product of every head, stay in
 //    registers too.
-//  * The R = Q/16 row groups of 16 rows are dealt out in pairs: wavefront w
-//    owns row groups w and R-1-w, w + 1 and R - w causal tiles, R + 1 for
-//    every wavefront.
+//  * The R = Q/16 row groups of 16 rows are dealt out in pairs, a short and
+//    a long one: wavefront w owns row groups w and R-1-w, w + 1 and R - w
+//    causal tiles, R + 1 for every wavefront; with eight wavefronts, the
+//    four served first at their SIMDs take one tile more and the other four
+//    one tile less (ScanCfg::BAL).
 //  * The decay exp(l_i - l_j) is never formed from exp(l_i) * exp(-l_j)
 //    (that overflows). Off-diagonal tiles use a factorisation through the
 //    tile boundaries, exp(l_i - l_r0) * exp(l_r0 - l_te) * exp(l_te - l_j),
@@ -43,9 +45,10 @@
 //    XOR of the 16-byte chunk positions keeps both reads free of bank
 //    conflicts. The decay tables are tabulated per head from values read
 //    into registers.
-//  * The skip term D_h x_i is one more product on the diagonal tiles' x
-//    operand, against D_h times the identity (D_h split into two bf16 parts,
-//    so the term is exact to 16 bits of D_h in the fp32 accumulator).
+//  * The skip term D_h x_i shares the diagonal tiles' products: a diagonal
+//    tile fills half of a 32-deep step, and the other half carries the bf16
+//    part of D_h times the identity against the same x rows; the remainder
+//    of D_h is added to the diagonal weight before that is rounded.
 #include "mfma_common.h"
 
 namespace ssd {
@@ -60,7 +63,15 @@ struct ScanCfg {
   static constexpr int THREADS = WAVES * 64;  // = 2 Q
   static constexpr int NTP = P / 16;          // p tiles
   static constexpr int NK = (N + 31) / 32;    // 32-deep steps over n
-  static constexpr int NGT = R - 1;           // off-diagonal G^T tiles per wavefront
+  // Eight wavefronts (Q = 256) run two per SIMD, wavefront w beside w + 4,
+  // and the older one (w < 4) is served first and used to wait at the
+  // per-head barrier while its younger neighbour ran alone. The row groups
+  // are therefore dealt out unevenly there: the first four wavefronts take
+  // the odd row groups (2w + 1, R - 1 - 2w, R + 2 tiles), the last four the
+  // even ones (2v, R - 2 - 2v, R tiles), where the one more G^T slot fits
+  // the registers. Otherwise: (w, R - 1 - w), R + 1.
+  static constexpr bool BAL = WAVES == 8 && N <= 128 && P <= 64;
+  static constexpr int NGT = BAL ? R : R - 1;  // off-diagonal G^T slots per wavefront
   // x: Q rows of P bf16, Hin: P rows of N bf16, each in its natural row
   // order with the 16-byte chunks of a row permuted (scan_xsw, scan_hsw); both are
   // filled in 1 KB blocks by loads that write the LDS directly
@@ -127,17 +138,24 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
   chunk_span(ctab, b, c, L, Q, row0, rows);
   if (rows <= 0) return;  // unused slot of a packed-sequence table (uniform)
 
-  // row groups of this wavefront: w and R-1-w
+  // row groups of this wavefront, rk[0] < rk[1]
   int rk[RG], ik[RG];
-  rk[0] = wave;
-  rk[1] = R - 1 - wave;
+  if constexpr (C::BAL) {
+    const int v = wave & 3;
+    rk[0] = wave < 4 ? 2 * v + 1 : 2 * v;
+    rk[1] = wave < 4 ? R - 1 - 2 * v : R - 2 - 2 * v;
+  } else {
+    rk[0] = wave;
+    rk[1] = R - 1 - wave;
+  }
 #pragma unroll
   for (int k = 0; k < RG; ++k) ik[k] = 16 * rk[k] + r16;
   // G^T slot of off-diagonal tile t of row group k, static for static k and
-  // t: row group 0 fills slots 0.. upwards, row group 1 fills R-2.. downwards
-  // (its tile t at slot R-2-t), and the two runs meet without overlap.
+  // t: row group 0 fills slots 0.. upwards, row group 1 fills NGT-1..
+  // downwards (its tile t at slot NGT-1-t), and as rk[0] + rk[1] <= NGT the
+  // two runs meet without overlap.
   auto gslot = [&](int k, int t) {
-    const int sidx = k == 0 ? t : R - 2 - t;
+    const int sidx = k == 0 ? t : C::NGT - 1 - t;
     return sidx < 0 ? 0 : (sidx > C::NGT - 1 ? C::NGT - 1 : sidx);
   };
 
@@ -219,7 +237,6 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
     }
     if (tid < R * R) sT[tid] = tt < tr ? __expf(tl1 - tl2) : 0.f;
   };
-  if constexpr (C::EARLY) fetch_head(h0, 0);
 
   // ---- C fragments of the row groups (B operand: column i, 8 consecutive n),
   // kept in registers: they also feed the chunk-output product of every head.
@@ -255,25 +272,42 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
     } else if (e < rk[0]) {
       k = 0;
       t = e;
-    } else {
+    } else {  // (slots between the two runs, if any, repeat a needed tile)
       k = 1;
-      t = R - 2 - e;
+      t = C::NGT - 1 - e;
     }
     srow[e] = 16 * t + r16;
     sk[e] = k;
   }
+  // B is staged one slice of 128 n at a time; each slice's loads are issued
+  // before the previous slice's products, and the first head's x and Hin
+  // loads after the first slice's, so that the G^T set-up waits for B only.
+  constexpr int CH = Q * C::NSW / 8;  // 16-byte chunks of a slice
+  constexpr int CPT = (CH + C::THREADS - 1) / C::THREADS;
+  uint4 bst[CPT];
+  auto load_b = [&](int sl) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int ci = min(tid + q * C::THREADS, CH - 1);
+      const int j = ci / (C::NSW / 8), n0 = 8 * (ci % (C::NSW / 8));
+      bst[q] = ld16_keep(Bm + ((row0 + min(j, rows - 1)) * G + g) * N + sl * 128 + n0, j < rows);
+    }
+  };
+  load_b(0);
 #pragma unroll
   for (int sl = 0; sl < C::NSL; ++sl) {
     if (sl > 0) __syncthreads();
-    constexpr int CH = Q * C::NSW / 8;  // 16-byte chunks of the slice
 #pragma unroll
-    for (int q = 0; q < (CH + C::THREADS - 1) / C::THREADS; ++q) {
+    for (int q = 0; q < CPT; ++q) {
       const int ci = tid + q * C::THREADS;
-      if (ci < CH) {
+      if (CH % C::THREADS == 0 || ci < CH) {
         const int j = ci / (C::NSW / 8), n0 = 8 * (ci % (C::NSW / 8));
-        st16(sB + j * C::BPITCH + n0,
-             ld16_keep(Bm + ((row0 + min(j, rows - 1)) * G + g) * N + sl * 128 + n0, j < rows));
+        st16(sB + j * C::BPITCH + n0, bst[q]);
       }
+    }
+    if (sl + 1 < C::NSL) load_b(sl + 1);
+    if constexpr (C::EARLY) {
+      if (sl == 0) fetch_head(h0, 0);
     }
     __syncthreads();
 #pragma unroll
@@ -449,21 +483,19 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
         if (k >= steps) fetch_x_block(h + 1, nbo, k);
     }
 
-    // The skip term D_h x_i rides on the diagonal tiles' x operand: an extra
-    // product with D_h times the identity, D_h split into two bf16 parts
-    // (hi + lo carries 16 bits of D_h; bf16 x times either part is exact in
-    // the fp32 accumulator). Lane (i, g4) holds the one identity entry
+    // The skip term D_h x_i rides on the diagonal tiles' products. A diagonal
+    // tile uses one 16-row half of the 32-deep step, so its x operand holds
+    // the tile's rows twice (one transposing read per p tile) and the weight
+    // operand's other half holds D_h times the identity. D_h is split into
+    // two parts: the bf16 part goes into that identity (bf16 x times it is
+    // exact in the fp32 accumulator), the remainder (below 2^-8 |D_h|) onto
+    // the diagonal weight before that is rounded, so it adds no error beyond
+    // that weight's own rounding. Lane (i, g4) holds the identity entry
     // j == i when 4 g4 <= i < 4 g4 + 4.
     const float dh = D != nullptr ? D[h] : 0.f;
     const uint32_t dhi_bits = pack_bf16x2(dh, 0.f) & 0xffffu;
-    const uint32_t dlo_bits = pack_bf16x2(dh - bf16_lo(dhi_bits), 0.f) & 0xffffu;
+    const float dlo = dh - bf16_lo(dhi_bits);
     const int dq = r16 - 4 * g4;
-    const bool don = dq >= 0 && dq < 4;
-    auto ident = [&](uint32_t bits, bool upper) {
-      const uint32_t wv = don ? bits << (16 * (dq & 1)) : 0u;
-      const uint32_t w0 = (dq >> 1) == 0 ? wv : 0u, w1 = (dq >> 1) == 1 ? wv : 0u;
-      return as_bf16x8(upper ? make_uint4(0, 0, w0, w1) : make_uint4(w0, w1, 0, 0));
-    };
 
     // diagonal tiles: mask (j > i) before the exponential
 #pragma unroll
@@ -482,22 +514,19 @@ __global__ __launch_bounds__(kScanThreads<Q>) __attribute__((amdgpu_waves_per_eu
       for (int q = 0; q < 4; ++q) {
         const int jq = j0 + q;
         const float e = __expf(jq <= i ? li - ljv[q] : -INFINITY);
-        w[q] = gv[q] * e * djv[q];
+        w[q] = gv[q] * e * djv[q] + (jq == i ? dlo : 0.f);
       }
-      const uint32_t w01 = pack_bf16x2(w[0], w[1]), w23 = pack_bf16x2(w[2], w[3]);
-      const bool upper = t & 1;  // which half of the 32-deep pair holds tile t
-      const bf16x8_t wop = as_bf16x8(upper ? make_uint4(0, 0, w01, w23) : make_uint4(w01, w23, 0, 0));
-      const bf16x8_t dop_hi = ident(dhi_bits, upper), dop_lo = ident(dlo_bits, upper);
-      bf16x8_t a[NTP];
+      const uint32_t dwv = dq >= 0 && dq < 4 ? dhi_bits << (16 * (dq & 1)) : 0u;
+      const bf16x8_t wop = as_bf16x8(make_uint4(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]),
+                                                (dq >> 1) == 0 ? dwv : 0u, (dq >> 1) == 1 ? dwv : 0u));
+      // rows of tile t: the lower or upper half of its 32-row step
+      const unsigned char* xa = buf + (t >> 1) * 32 * C::XRB + (t & 1) * 16 * C::XRB;
+      uint2 v[NTP];
 #pragma unroll
-      for (int pt = 0; pt < NTP; ++pt) a[pt] = as_bf16x8(xfrag(t >> 1, pt));
-      // three rounds over the p tiles, so consecutive products are independent
+      for (int pt = 0; pt < NTP; ++pt) v[pt] = lds_tr8(xa + xoff[pt]);
 #pragma unroll
-      for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(a[pt], wop, acc[k][pt]);
-#pragma unroll
-      for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(a[pt], dop_hi, acc[k][pt]);
-#pragma unroll
-      for (int pt = 0; pt < NTP; ++pt) acc[k][pt] = mfma_16x16x32(a[pt], dop_lo, acc[k][pt]);
+      for (int pt = 0; pt < NTP; ++pt)
+        acc[k][pt] = mfma_16x16x32(as_bf16x8(make_uint4(v[pt].x, v[pt].y, v[pt].x, v[pt].y)), wop, acc[k][pt]);
     }
 
     // this wavefront's loads of the next head have landed (waited for before
