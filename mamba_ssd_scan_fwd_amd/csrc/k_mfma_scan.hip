@@ -98,7 +98,7 @@ struct ScanCfg {
   static constexpr int NBUF = DB ? 2 : 1;
   // the B staging area of the G^T set-up lies over buffer 1 when buffer 0
   // and it fit together: then the first head's loads into buffer 0 are
-  // issued before the set-up
+  // issued during the set-up, right after the first B slice's loads
   static constexpr bool EARLY = DB && BUF + BST_BYTES <= 160 * 1024;
   static constexpr int OFF_SB = EARLY ? BUF : 0;
   static constexpr int TOTAL = NBUF * BUF > OFF_SB + BST_BYTES ? NBUF * BUF : OFF_SB + BST_BYTES;
