@@ -180,6 +180,44 @@ def test_edge_shapes(L, P, N, H, G, io, Q, init):
     full_check(inp, TOL[io], f"edge L={L} P={P} N={N} H={H} G={G} {io} Q={Q}", chunk_size=Q)
 
 
+def _bf16_refused(P, N, Q):
+    """The bf16 shapes the plan refuses (their register tiles would spill)."""
+    return (P == 128 and ((Q == 256 and N >= 64) or (Q == 64 and N == 256))) or (P == 16 and N == 256 and Q == 256)
+
+
+def _random_split_shapes(n=24, seed=4242):
+    """Seeded shapes over the supported set: every head dimension, state size
+    and chunk length the plan accepts (0: the shape's default), grouped heads,
+    ragged lengths from one token to several chunks, with and without an
+    initial state; small enough for the fp64 recurrence on every chain."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        P = int(rng.choice([16, 32, 64, 128]))
+        N = int(rng.choice([16, 32, 64, 128, 256]))
+        Q = int(rng.choice([0, 64, 128, 256]))
+        io = "bf16" if rng.random() < 0.75 else "fp32"
+        if io == "bf16" and Q != 0 and _bf16_refused(P, N, Q):
+            continue
+        G = int(rng.choice([1, 2]))
+        H = G * int(rng.choice([1, 2, 4]))
+        L = int(rng.integers(1, 900))
+        out.append((L, P, N, H, G, io, Q, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("L,P,N,H,G,io,Q,init", _random_split_shapes())
+def test_random_shapes_in_full(L, P, N, H, G, io, Q, init):
+    """Every output of seeded random shapes through ssd_forward_split (the
+    path of every bf16 kernel instantiation these shapes reach, including the
+    uneven row-group deal of the eight-wavefront chunk scan) against the fp64
+    recurrence."""
+    cfg = BASE.with_(seqlen=L, headdim=P, dstate=N, nheads=H, ngroups=G, io_dtype=io, init_state=init)
+    inp = make_inputs(cfg, seed=3 * L + P + N + H + Q)
+    full_check(inp, TOL[io], f"random L={L} P={P} N={N} H={H} G={G} {io} Q={Q} init={init}", chunk_size=Q,
+               split=True)
+
+
 @pytest.mark.parametrize("Q", [64, 128, 256])
 @pytest.mark.parametrize("io", ["bf16", "fp32"])
 def test_every_chunk_length_gives_the_same_result(Q, io):
